@@ -1,0 +1,155 @@
+"""CPU oracle for the tiled GEMM C = A * B^T -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+under ``tiled_gemm_amd/`` and never imports it.
+
+Contents
+--------
+* ``gemm_bt`` / ``gemm_bt_entries`` -- the fp64 triple loop in ``oracle.c``
+  (plain i-j-k, sequential k, sigma = s_a * s_b for fp8), built with gcc.
+* ``round_bf16`` -- the oracle's own round-to-nearest-even to bf16.
+* ``bf16_value`` / ``e4m3fn_value`` -- element decoders from the format
+  definitions.
+* ``layout`` -- brute-force layout algebra (``crd2idx``/``idx2crd``) and the
+  B pre-shuffle permutation written as a reshape/transpose.
+
+Every function's pins are in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+E4M3FN = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.oracle_bf16_value.restype = dbl
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3fn_value.restype = dbl
+    lib.oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_gemm_bt.restype = None
+    lib.oracle_gemm_bt.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, dbl, vp, vp]
+    lib.oracle_gemm_bt_entries.restype = None
+    lib.oracle_gemm_bt_entries.argtypes = [i64, ctypes.c_int, vp, vp, dbl, i64, vp, vp, vp, vp]
+    lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16.argtypes = [dbl]
+    lib.oracle_round_bf16_array.restype = None
+    lib.oracle_round_bf16_array.argtypes = [i64, vp, vp]
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses (``OMP_NUM_THREADS`` or all cores)."""
+    return int(_load().oracle_threads())
+
+
+def _kind(dtype: str) -> int:
+    if dtype == "bf16":
+        return BF16
+    if dtype == "e4m3":
+        return E4M3FN
+    raise ValueError("oracle: unknown element type %r" % (dtype,))
+
+
+def _operand(x: np.ndarray, dtype: str) -> np.ndarray:
+    want = np.uint16 if dtype == "bf16" else np.uint8
+    x = np.ascontiguousarray(x)
+    if x.dtype != want:
+        raise TypeError("oracle: %s operand must hold raw %s bits" % (dtype, want.__name__))
+    return x
+
+
+def sigma_of(scale_a: float = 1.0, scale_b: float = 1.0) -> float:
+    """sigma = s_a * s_b formed in fp64 from the two fp32 scales."""
+    return float(np.float64(np.float32(scale_a)) * np.float64(np.float32(scale_b)))
+
+
+def gemm_bt(A: np.ndarray, B: np.ndarray, dtype: str = "bf16", sigma: float = 1.0,
+            want_s: bool = True):
+    """Full C_ref (M x N, fp64) and S, for A (M x K) and B (N x K) raw bits."""
+    A = _operand(A, dtype)
+    B = _operand(B, dtype)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError("oracle: K mismatch")
+    C = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64) if want_s else None
+    _load().oracle_gemm_bt(M, N, K, _kind(dtype), A.ctypes.data, B.ctypes.data, float(sigma),
+                           C.ctypes.data, S.ctypes.data if want_s else None)
+    return C, S
+
+
+def gemm_bt_entries(A: np.ndarray, B: np.ndarray, rows, cols, dtype: str = "bf16",
+                    sigma: float = 1.0):
+    """C_ref and S at the (rows[t], cols[t]) entries only."""
+    A = _operand(A, dtype)
+    B = _operand(B, dtype)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("oracle: rows/cols shape mismatch")
+    K = A.shape[1]
+    if B.shape[1] != K:
+        raise ValueError("oracle: K mismatch")
+    if rows.size and (rows.min() < 0 or rows.max() >= A.shape[0]
+                      or cols.min() < 0 or cols.max() >= B.shape[0]):
+        raise IndexError("oracle: entry out of range")
+    C = np.empty(rows.shape, np.float64)
+    S = np.empty(rows.shape, np.float64)
+    _load().oracle_gemm_bt_entries(K, _kind(dtype), A.ctypes.data, B.ctypes.data, float(sigma),
+                                   rows.size, rows.ctypes.data, cols.ctypes.data,
+                                   C.ctypes.data, S.ctypes.data)
+    return C, S
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round fp64 values to bf16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_bf16_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out
+
+
+def bf16_value(bits: int) -> float:
+    return float(_load().oracle_bf16_value(int(bits)))
+
+
+def e4m3fn_value(bits: int) -> float:
+    return float(_load().oracle_e4m3fn_value(int(bits)))
+
+
+from . import layout  # noqa: E402,F401  (brute-force layout algebra)

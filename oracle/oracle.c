@@ -1,0 +1,163 @@
+/*
+ * CPU oracle for the tiled GEMM  C = A * B^T  (TEST INFRASTRUCTURE ONLY).
+ *
+ * Only tests/, the smoke check and the benchmark's CPU-baseline leg may load
+ * this file's library.  The product path never calls it, and it shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * What it computes (FlyDSL "Kernel authoring guide", section 11 "Complete
+ * example: Preshuffle GEMM": a GEMM with fp32 accumulation whose output is
+ * scaled by per-operand scales and converted to bf16; FlyDSL "Kernel Authoring"
+ * skill, section 3 "Internal Types", for the scale order (value * scale_a) *
+ * scale_b):
+ *
+ *     C_ref[i][j] = sigma * sum_{k=0}^{K-1} a(i,k) * b(j,k)
+ *
+ * with A stored M x K row-major and B stored N x K row-major (both
+ * K-contiguous, so b(j,k) = B[j][k]), one fp64 accumulator per output and k
+ * taken in increasing order, sigma = 1 for bf16 and s_a * s_b (formed in fp64)
+ * for fp8.  It also returns S[i][j] = |sigma| * sum_k |a(i,k) * b(j,k)|, the
+ * magnitude sum used by the element-wise tolerance.
+ *
+ * Element decoders are written from the format definitions:
+ *   bf16      : the upper 16 bits of an IEEE binary32 (1 sign, 8 exponent,
+ *               7 fraction bits).
+ *   e4m3fn    : OCP 8-bit float, 1 sign, 4 exponent bits (bias 7), 3 fraction
+ *               bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is
+ *               NaN; no infinities; largest finite value 448.
+ *
+ * The output rounding to bf16 is round-to-nearest, ties-to-even, done in
+ * fp64 with nearbyint() under the default FE_TONEAREST mode.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math, so every fp64 sum
+ * stays in program order).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_E4M3FN = 1 };
+
+double oracle_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double oracle_e4m3fn_value(uint8_t bits)
+{
+    int sign = (bits >> 7) & 1;
+    int expo = (bits >> 3) & 0xF;
+    int frac = bits & 0x7;
+    double mag;
+    if (expo == 0xF && frac == 0x7)
+        return NAN;
+    if (expo == 0)
+        mag = ldexp((double)frac, -9);              /* subnormal: m * 2^(1-7-3) */
+    else
+        mag = ldexp(1.0 + frac / 8.0, expo - 7);    /* normal: 1.m * 2^(e-7)    */
+    return sign ? -mag : mag;
+}
+
+static double element(int kind, const void *base, int64_t idx)
+{
+    if (kind == ORACLE_BF16)
+        return oracle_bf16_value(((const uint16_t *)base)[idx]);
+    return oracle_e4m3fn_value(((const uint8_t *)base)[idx]);
+}
+
+/* One output element: the definition written out. */
+static void dot_entry(int64_t K, int kind, const void *A, const void *B,
+                      int64_t i, int64_t j, double sigma, double *c, double *s)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = element(kind, A, i * K + k) * element(kind, B, j * K + k);
+        acc += p;
+        mag += fabs(p);
+    }
+    *c = sigma * acc;
+    *s = fabs(sigma) * mag;
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full product.  C and S are M x N row-major fp64 (S may be NULL). */
+void oracle_gemm_bt(int64_t M, int64_t N, int64_t K, int kind,
+                    const void *A, const void *B, double sigma,
+                    double *C, double *S)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double c, s;
+            dot_entry(K, kind, A, B, i, j, sigma, &c, &s);
+            C[i * N + j] = c;
+            if (S)
+                S[i * N + j] = s;
+        }
+    }
+}
+
+/* Selected entries (rows[t], cols[t]) for t < count, for checks at sizes
+ * where the full product would take too long. */
+void oracle_gemm_bt_entries(int64_t K, int kind, const void *A, const void *B,
+                            double sigma, int64_t count, const int64_t *rows,
+                            const int64_t *cols, double *C, double *S)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < count; ++t) {
+        double c, s;
+        dot_entry(K, kind, A, B, rows[t], cols[t], sigma, &c, &s);
+        C[t] = c;
+        if (S)
+            S[t] = s;
+    }
+}
+
+/* Round-to-nearest-even of a finite double to bf16, returned as bits.
+ * bf16 keeps 8 significant bits; below 2^-126 the spacing is fixed at
+ * 2^-133 (subnormals).  Overflow past the largest finite bf16 gives inf. */
+uint16_t oracle_round_bf16(double x)
+{
+    double r;
+    float f;
+    uint32_t u;
+    if (isnan(x))
+        return 0x7FC0;
+    if (x == 0.0)
+        return signbit(x) ? 0x8000 : 0x0000;
+    if (fabs(x) < ldexp(1.0, -126)) {
+        r = ldexp(nearbyint(ldexp(x, 133)), -133);
+    } else {
+        int e;
+        double m = frexp(x, &e);                     /* x = m * 2^e, 0.5 <= |m| < 1 */
+        r = ldexp(nearbyint(ldexp(m, 8)), e - 8);    /* 8 significant bits */
+    }
+    f = (float)r;                                    /* exact: r has <= 8 bits */
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_round_bf16_array(int64_t n, const double *x, uint16_t *out)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < n; ++t)
+        out[t] = oracle_round_bf16(x[t]);
+}

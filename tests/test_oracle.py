@@ -1,0 +1,236 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each pin is chosen so that a plausible mistake (a dropped term, a sign, a
+swapped index, a transposed operand, a wrong decoder bit) fails at least one:
+identity and permutation matrices, closed-form rank-1 products, all-ones,
+exact rational brute force on tiny non-square shapes, the format definitions
+of bf16 / e4m3fn checked against torch's decoders, round-to-nearest-even
+ties, and the layout worked examples printed on the FlyDSL pages.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import layout as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(x):
+    return workloads.to_bf16_bits(np.asarray(x, np.float32))
+
+
+def e4m3(x):
+    t = torch.tensor(np.asarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decoder_matches_torch_on_every_code(oracle_mod):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle_mod.bf16_value(c) for c in codes[::97]])
+    w = want[::97]
+    nan = np.isnan(w)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], w[~nan])
+    for bits, val in [(0x3F80, 1.0), (0xC000, -2.0), (0x4049, 3.140625), (0x0001, 2.0 ** -133),
+                      (0x7F7F, 3.3895313892515355e38), (0x8000, -0.0)]:
+        assert oracle_mod.bf16_value(bits) == val
+
+
+def test_e4m3fn_decoder_matches_torch_and_format(oracle_mod):
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([oracle_mod.e4m3fn_value(int(c)) for c in codes])
+    nan = np.isnan(want)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # format definition: largest finite 448, smallest subnormal 2^-9, 1.0 = 0 0111 000
+    assert oracle_mod.e4m3fn_value(0x7E) == 448.0
+    assert oracle_mod.e4m3fn_value(0x01) == 2.0 ** -9
+    assert oracle_mod.e4m3fn_value(0x08) == 2.0 ** -6
+    assert oracle_mod.e4m3fn_value(0x38) == 1.0
+    assert oracle_mod.e4m3fn_value(0xB8) == -1.0
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_round_bf16_golden_ties(oracle_mod):
+    with open(os.path.join(GOLDEN, "bf16_rounding.json")) as f:
+        cases = json.load(f)["cases"]
+    xs = np.array([c["x"] for c in cases])
+    got = oracle_mod.round_bf16(xs)
+    for c, g in zip(cases, got):
+        assert int(g) == int(c["bits"], 16), c
+        assert oracle_mod.bf16_value(int(g)) == c["value"]
+
+
+def test_round_bf16_matches_torch_on_fp32_values(oracle_mod):
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 1000,
+                        rng.standard_normal(2000).astype(np.float32) * 1e-30,
+                        np.float32([1e-39, -3e-40, 65504.5, 3.38e38])]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle_mod.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- the GEMM
+
+def test_identity(oracle_mod):
+    rng = np.random.default_rng(1)
+    K = 24
+    B = bf16(rng.integers(-8, 9, size=(10, K)))
+    I = bf16(np.eye(K))
+    C, S = oracle_mod.gemm_bt(I, B)          # A = I  =>  C = B^T
+    Bv = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(C, Bv.T)
+    assert np.array_equal(S, np.abs(Bv.T))
+    A = bf16(rng.integers(-8, 9, size=(7, K)))
+    C2, _ = oracle_mod.gemm_bt(A, I)         # B = I  =>  C = A
+    Av = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(C2, Av)
+
+
+def test_permutation(oracle_mod):
+    rng = np.random.default_rng(2)
+    K, N = 9, 5
+    perm = rng.permutation(K)
+    P = np.zeros((K, K), np.float32)
+    P[np.arange(K), perm] = 1.0              # row i selects k = perm[i]
+    Bf = rng.integers(-5, 6, size=(N, K)).astype(np.float32)
+    C, _ = oracle_mod.gemm_bt(bf16(P), bf16(Bf))
+    assert np.array_equal(C, Bf[:, perm].T.astype(np.float64))
+
+
+def test_rank1_closed_form(oracle_mod):
+    u = np.array([1, -2, 3], np.float32)
+    v = np.array([2, 1, -1, 4, 0], np.float32)
+    x = np.array([1, 2, -3, 1, 1, -1, 2], np.float32)
+    y = np.array([-1, 1, 1, 2, -2, 3, 1], np.float32)
+    A = np.outer(u, x)
+    B = np.outer(v, y)
+    C, S = oracle_mod.gemm_bt(bf16(A), bf16(B))
+    xy = float(np.dot(x.astype(np.float64), y))
+    assert np.array_equal(C, np.outer(u, v).astype(np.float64) * xy)
+    assert np.array_equal(S, np.abs(np.outer(u, v)).astype(np.float64) * float(np.abs(x * y).sum()))
+
+
+def test_all_ones_and_alternating(oracle_mod):
+    K = 33
+    ones = bf16(np.ones((4, K)))
+    C, S = oracle_mod.gemm_bt(ones, bf16(np.ones((6, K))))
+    assert np.all(C == K) and np.all(S == K)
+    alt = bf16(np.tile((-1.0) ** np.arange(K), (4, 1)))
+    C, S = oracle_mod.gemm_bt(alt, bf16(np.ones((3, K))))
+    assert np.all(C == 1.0) and np.all(S == K)   # K odd: one uncancelled +1
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 4, 4), (3, 5, 7), (5, 2, 6)])
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_brute_force_rational(oracle_mod, M, N, K, dtype):
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    a = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+    b = (rng.standard_normal((N, K)) * 3).astype(np.float32)
+    if dtype == "bf16":
+        A, B = bf16(a), bf16(b)
+        table = torch.from_numpy(np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.int16)) \
+            .view(torch.bfloat16).double().numpy()
+        dec = lambda bits: Fraction(float(table[int(bits)]))
+        sa, sb = 1.0, 1.0
+    else:
+        A, B = e4m3(a), e4m3(b)
+        table = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+        dec = lambda bits: Fraction(float(table[int(bits)]))
+        sa, sb = 0.375, 1.5
+    sigma = oracle_mod.sigma_of(sa, sb)
+    C, S = oracle_mod.gemm_bt(A, B, dtype=dtype, sigma=sigma)
+    for i in range(M):
+        for j in range(N):
+            exact = sum(dec(A[i, k]) * dec(B[j, k]) for k in range(K)) * Fraction(sa) * Fraction(sb)
+            mag = sum(abs(dec(A[i, k]) * dec(B[j, k])) for k in range(K)) * Fraction(sa) * Fraction(sb)
+            assert C[i, j] == float(exact), (i, j)   # small sums are exact in fp64
+            assert S[i, j] == float(mag), (i, j)
+
+
+def test_entries_equal_full(oracle_mod):
+    inp = workloads.make_inputs(workloads.WORKLOADS["bf16_4096"], M=40, N=24, K=64, seed=5)
+    C, S = oracle_mod.gemm_bt(inp.A, inp.B)
+    rows = np.array([0, 39, 17, 5, 39])
+    cols = np.array([23, 0, 11, 5, 23])
+    c, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols)
+    assert np.array_equal(c, C[rows, cols]) and np.array_equal(s, S[rows, cols])
+
+
+def test_entries_reject_out_of_range(oracle_mod):
+    inp = workloads.int_inputs(4, 4, 64, "bf16", 1)
+    with pytest.raises(IndexError):
+        oracle_mod.gemm_bt_entries(inp.A, inp.B, [4], [0])
+
+
+# ---------------------------------------------------------------- layouts
+
+def test_layout_golden_examples():
+    with open(os.path.join(GOLDEN, "layout_examples.json")) as f:
+        g = json.load(f)
+    for c in g["crd2idx"]:
+        assert L.crd2idx(tuple(c["coord"]), tuple(c["shape"]), tuple(c["stride"])) == c["index"]
+    for c in g["idx2crd"]:
+        assert L.idx2crd(c["index"], tuple(c["shape"]), tuple(c["stride"])) == tuple(c["coord"])
+
+
+def test_layout_brute_force_table():
+    # compact column-major: the table is 0..size-1 in order
+    assert np.array_equal(L.brute_force_table((8, 16), (1, 8)), np.arange(128))
+    # row-major (4,6):(6,1) visited colexicographically
+    t = L.brute_force_table((4, 6), (6, 1))
+    assert list(t[:5]) == [0, 6, 12, 18, 1]
+    # nested shapes flatten
+    assert L.crd2idx(((1, 2), 3), ((2, 4), 5), ((1, 2), 8)) == 1 + 4 + 24
+    # integer coordinates split colexicographically
+    assert L.crd2idx(43, (8, 16), (1, 8)) == 43
+    assert L.crd2idx(5, (2, 3), (3, 1)) == 1 * 3 + 2 * 1
+
+
+def test_preshuffle_two_formulations_agree():
+    rng = np.random.default_rng(3)
+    N, K = 48, 96                                  # bf16: 192 bytes per row
+    B = rng.integers(0, 65535, size=(N, K), dtype=np.uint16)
+    shuf = L.preshuffle_b_bytes(B)
+    raw = B.view(np.uint8).reshape(N, -1)
+    kbytes = raw.shape[1]
+    assert sorted(shuf.tolist()) == sorted(raw.reshape(-1).tolist())
+    for n in range(N):
+        for kb in range(kbytes):
+            assert shuf[L.preshuffle_src_offset(n, kb, N, kbytes)] == raw[n, kb]
+    # a hand-computed element: n=17, byte 70 of a 128-byte row
+    assert L.preshuffle_src_offset(17, 70, 32, 128) == ((((1 * 2 + 1) * 4 + 0) * 16 + 1) * 16 + 6)
+
+
+def test_preshuffle_block_is_one_wave_operand():
+    """Each 1 KiB block holds, for lane l = 16*q + r, the 16 bytes of row
+    16*nb + r at k-bytes 64*kb + 16*q: one 16-byte load per lane."""
+    N, K = 32, 64                                  # bf16 -> 128 bytes per row
+    B = (np.arange(N * K, dtype=np.uint32) % 65521).astype(np.uint16).reshape(N, K)
+    shuf = L.preshuffle_b_bytes(B).reshape(N // 16, 2, 64, 16)
+    raw = B.view(np.uint8).reshape(N, -1)
+    for nb in range(N // 16):
+        for kb in range(2):
+            for lane in range(64):
+                q, r = divmod(lane, 16)
+                assert np.array_equal(shuf[nb, kb, lane], raw[16 * nb + r, 64 * kb + 16 * q:64 * kb + 16 * q + 16])
+
+
+def test_preshuffle_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        L.preshuffle_b_bytes(np.zeros((24, 64), np.uint16))
+    with pytest.raises(ValueError):
+        L.preshuffle_b_bytes(np.zeros((32, 40), np.uint8))
