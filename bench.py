@@ -1,0 +1,211 @@
+"""Benchmark of the tiled GEMM on one MI355X.
+
+A step is one gemm_run of C = A * B^T on the headline workload: bf16
+8192 x 8192 x 8192 with B pre-shuffled into MFMA operand order (the
+pre-shuffle is done once, ahead of the timed steps, and reported separately),
+fp32 accumulation, bf16 output.  Inputs are seeded synthetic data resident in
+HBM before timing starts.
+
+Prints one JSON line with TFLOP/s, the roofline of the GEMM kernel measured
+with HIP events on the launch stream, and the CPU oracle timed on a bounded
+sample of the same workload.  The other workloads (bf16 4096^3, skinny
+32 x 8192 x 8192, fp8 8192^3) are measured too and reported under "also".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}     # MI355X dense peaks
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "bf16_8192_preshuffled"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1):
+    """Time `steps` gemm_run launches (after `warmup`) with HIP events on the
+    launch stream.  With rotate > 1, that many independent input/output sets
+    are cycled so the operands are not served from the last-level cache."""
+    code = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
+            ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}[(w.dtype, w.out)]
+    plan = tg.Plan(w.M, w.N, w.K, code, tg.LAYOUTS[w.layout])
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def dev(bits):
+        bits = np.ascontiguousarray(bits)
+        return torch.from_numpy(bits.view(np.int16) if bits.dtype == np.uint16 else bits).cuda()
+
+    A0, B0 = dev(inp.A), dev(inp.B)
+    sets = []
+    shuf_ms = None
+    for r in range(rotate):
+        A = A0 if r == 0 else A0.clone()
+        B = B0 if r == 0 else B0.clone()
+        if w.layout == "bt_preshuffled":
+            Bs = torch.empty(tg.gemm_preshuffled_b_bytes(plan.handle), dtype=torch.uint8, device="cuda")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            plan.preshuffle_b(B.data_ptr(), Bs.data_ptr(), s)      # warm
+            e0.record(stream)
+            plan.preshuffle_b(B.data_ptr(), Bs.data_ptr(), s)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            shuf_ms = e0.elapsed_time(e1)
+            B = Bs
+        C = torch.empty(w.M * w.N * w.out_bytes, dtype=torch.uint8, device="cuda")
+        sets.append((A, B, C))
+    scale = torch.tensor([inp.scale_a, inp.scale_b], dtype=torch.float32, device="cuda")
+    sp = scale.data_ptr() if w.dtype == "e4m3" else None
+    for i in range(warmup):
+        A, B, C = sets[i % rotate]
+        plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        A, B, C = sets[i % rotate]
+        plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    info = plan.info()
+    plan.close()
+    del sets
+    torch.cuda.empty_cache()
+    return ms, wall, info, shuf_ms
+
+
+def cpu_baseline(w, inp, target_s=12.0):
+    """The oracle on a bounded sample of the same workload: whole rows of C,
+    as many as fit ~target_s seconds (calibrated on a small first sample)."""
+    import oracle
+    threads = oracle.threads()
+    rng = np.random.default_rng(w.seed)
+
+    def run(nrows):
+        rows = np.repeat(rng.choice(w.M, size=nrows, replace=False), w.N)
+        cols = np.tile(np.arange(w.N), nrows)
+        sigma = oracle.sigma_of(inp.scale_a, inp.scale_b)
+        t0 = time.perf_counter()
+        oracle.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype, sigma=sigma)
+        return time.perf_counter() - t0
+
+    probe_rows = max(1, threads // 2)
+    t = run(probe_rows)
+    nrows = int(max(1, min(w.M, probe_rows * target_s / max(t, 1e-3))))
+    t = run(nrows)
+    flops = 2.0 * nrows * w.N * w.K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full rows of C (%d x %d outputs, K=%d) of %s in %.1f s" % (
+                nrows, nrows, w.N, w.K, w.name, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--only", default=None, help="time only this workload (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus %d requested); "
+              "the sharded design is described in DESIGN.md" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_gemm_amd as tg
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    tg.load()
+    names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
+        "bf16_4096", "bf16_skinny_32x8192x8192", "e4m3_8192"])
+    results = {}
+    inputs = {}
+    for name in names:
+        w = W.WORKLOADS[name]
+        log("bench: generating", name)
+        inp = W.make_inputs(w)
+        rotate = 3 if name == "bf16_skinny_32x8192x8192" else 1
+        steps = args.steps if name == (args.only or HEADLINE) else max(10, args.steps // 2)
+        ms, wall, info, shuf_ms = time_gemm(torch, tg, w, inp, steps, args.warmup, rotate)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = w.min_bytes / (ms * 1e-3) / 1e9
+        results[name] = dict(ms=ms, wall=wall, steps=steps, tflops=tflops, gbs=gbs, info=info,
+                             shuf_ms=shuf_ms, rotate=rotate)
+        log("bench: %-26s %.4f ms  %.1f TFLOP/s  %.0f GB/s  tile %dx%d grid %d" % (
+            name, ms, tflops, gbs, info["tile_m"], info["tile_n"], info["grid"]))
+        if name == HEADLINE:
+            inputs[name] = inp
+
+    head = args.only or HEADLINE
+    w = W.WORKLOADS[head]
+    r = results[head]
+    bound = "hbm" if head == "bf16_skinny_32x8192x8192" else "mfma"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_TFLOPS[w.dtype], 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(r["gbs"] / PEAK_HBM_GBS, 4), "traffic": None}
+    line = {
+        "metric": "GEMM TFLOP/s (bf16 8192^3, B pre-shuffled, fp32 accumulate, bf16 out)",
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": r["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp8_e4m3",
+        "data": "synthetic (seeded %s)" % w.name,
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "layout": w.layout,
+                   "out": w.out, "tile": "%dx%d" % (r["info"]["tile_m"], r["info"]["tile_n"]),
+                   "grid": r["info"]["grid"], "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if r["shuf_ms"] is not None:
+        line["preshuffle"] = {"ms": round(r["shuf_ms"], 4),
+                              "GB/s": round(2 * w.N * w.K * w.elem_bytes / (r["shuf_ms"] * 1e-3) / 1e9, 1)}
+    also = {}
+    for name, rr in results.items():
+        if name == head:
+            continue
+        ww = W.WORKLOADS[name]
+        also[name] = {"ms": round(rr["ms"], 5), "TFLOP/s": round(rr["tflops"], 2),
+                      "frac_mfma_peak": round(rr["tflops"] / PEAK_TFLOPS[ww.dtype], 4),
+                      "GB/s": round(rr["gbs"], 1), "frac_hbm_peak": round(rr["gbs"] / PEAK_HBM_GBS, 4),
+                      "tile": "%dx%d" % (rr["info"]["tile_m"], rr["info"]["tile_n"]),
+                      "input_sets_rotated": rr["rotate"]}
+    if also:
+        line["also"] = also
+    if not args.no_cpu_baseline and head in inputs:
+        log("bench: timing the CPU oracle on a sample")
+        line["cpu_baseline"] = cpu_baseline(w, inputs[head])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

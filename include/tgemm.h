@@ -1,0 +1,185 @@
+/*
+ * tgemm -- tiled GEMM  C = A * B^T  for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one FlyDSL's preshuffle GEMM computes (FlyDSL "Kernel
+ * authoring guide", section 11 "Complete example: Preshuffle GEMM"; FlyDSL
+ * "Kernel Authoring" skill, section 6 "GEMM Pattern (Preshuffle)"):
+ *
+ *     C[m][n] = cvt( (sum_k A[m][k] * B[n][k]) * s_a * s_b )
+ *
+ * products of the input elements summed in fp32, the scale applied in fp32
+ * as (acc * s_a) * s_b (the Kernel Authoring skill's section 3 shows that
+ * order), then converted to the output type with round-to-nearest-even.
+ *
+ * Storage (all row-major, leading dimensions implicit):
+ *   A  M x K    elements of the input type            (lda = K)
+ *   B  N x K    elements of the input type            (ldb = K)
+ *              or, for GEMM_LAYOUT_BT_PRESHUFFLED, the N*K-element image
+ *              written by gemm_preshuffle_b (see there)
+ *   C  M x N    elements of the output type           (ldc = N)
+ *
+ * Every pointer passed to gemm_preshuffle_b / gemm_run is a DEVICE pointer
+ * owned by the caller.  The library allocates no device memory, never
+ * synchronises, and launches asynchronously on the given stream; a plan holds
+ * only host metadata and may be destroyed as soon as gemm_run returns.
+ * Calls on one plan from several streams or threads are safe.  C must not
+ * overlap A or B.
+ *
+ * Errors: functions returning int give GEMM_OK (0) or a negative
+ * gemm_status; functions returning a pointer give NULL.  The reason is kept
+ * per thread and read with gemm_last_error().  Only errors detectable on the
+ * host are reported (argument checks, launch failures via hipGetLastError);
+ * a fault inside a kernel surfaces at the caller's next synchronisation.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,   /* NULL or misaligned pointer, bad enum, negative size */
+    GEMM_ERR_UNSUPPORTED = -2,   /* shape outside the supported set, wrong GPU       */
+    GEMM_ERR_HIP = -3            /* a HIP runtime call or kernel launch failed        */
+} gemm_status;
+
+typedef enum {
+    GEMM_BF16_OUT_F32 = 0,       /* A, B bf16; C fp32 (no rounding of the fp32 sum)   */
+    GEMM_BF16_OUT_BF16 = 1,      /* A, B bf16; C bf16                                 */
+    GEMM_E4M3_OUT_BF16 = 2       /* A, B OCP fp8 e4m3fn (max 448); C bf16             */
+} gemm_dtype;
+
+typedef enum {
+    GEMM_LAYOUT_BT = 0,               /* B is N x K row-major                        */
+    GEMM_LAYOUT_BT_PRESHUFFLED = 1    /* B is the image written by gemm_preshuffle_b */
+} gemm_layout;
+
+typedef struct gemm_plan gemm_plan;   /* opaque, immutable after creation */
+
+/*
+ * gemm_plan_create -- validate a problem and pick its kernel and tiling.
+ *   M, N, K  sizes in elements; M may be 0 (gemm_run then does nothing),
+ *            K may be 0 (C is then all zeros).
+ *   dtype    gemm_dtype; layout gemm_layout.
+ * Requirements (else NULL with GEMM_ERR_UNSUPPORTED / GEMM_ERR_INVALID_ARG):
+ *   0 <= M, N, K <= 2^30;  N % 16 == 0;
+ *   K * elem_bytes % 64 == 0 -- the 64-byte K step of the pages' GEMM (Kernel
+ *   Authoring skill, section 10 "Troubleshooting", tile_k rule).
+ * Host only: no device work, no allocation on the device.  Returns a plan the
+ * caller frees with gemm_plan_destroy.
+ */
+gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout);
+
+/* gemm_plan_destroy -- free a plan (NULL is ignored). */
+void gemm_plan_destroy(gemm_plan *plan);
+
+/*
+ * gemm_preshuffled_b_bytes -- bytes of the pre-shuffled B image:
+ * N * K * elem_bytes (a pure permutation of B).  0 for a NULL plan.
+ */
+size_t gemm_preshuffled_b_bytes(const gemm_plan *plan);
+
+/*
+ * gemm_preshuffle_b -- write B (N x K row-major) in MFMA operand order.
+ * The image is the 5-mode byte array (N/16, Kb/64, 4, 16, 16) taken in
+ * row-major order, with Kb = K * elem_bytes: n-block, 64-byte k-block,
+ * 16-byte k-quarter q, row r within the n-block, byte.  Each 1 KiB block is
+ * therefore one wave's B operand for a 64-byte K step: lane 16*q + r loads
+ * the 16 bytes of row 16*nb + r at k-bytes 64*kb + 16*q.  (Kernel Authoring
+ * skill, section 6 "GEMM Pattern (Preshuffle)" step 1; K counted in bytes and
+ * kpack = 16 bytes is this library's reading of that tuple.)
+ *   B       device pointer, 16-byte aligned, N*K elements.
+ *   B_shuf  device pointer, 16-byte aligned, gemm_preshuffled_b_bytes(plan)
+ *           bytes, must not overlap B.
+ *   stream  HIP stream (0 = default stream).
+ * Any plan of the same (N, K, dtype) may be used; the image does not depend
+ * on M or on the plan's layout.  Asynchronous; returns GEMM_OK or an error.
+ */
+int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStream_t stream);
+
+/*
+ * gemm_run -- C = cvt((A * B^T) * s_a * s_b) on `stream`.
+ *   A      device pointer, 16-byte aligned, M x K input elements.
+ *   B      device pointer, 16-byte aligned: N x K (GEMM_LAYOUT_BT) or the
+ *          pre-shuffled image (GEMM_LAYOUT_BT_PRESHUFFLED).
+ *   C      device pointer, 16-byte aligned, M x N output elements; overwritten.
+ *   scale  device pointer to two floats {s_a, s_b}, or NULL for 1, 1.  Read
+ *          on the device, so fp8 scales never force a host synchronisation.
+ * Asynchronous; allocates nothing.  Returns GEMM_OK or an error code.
+ */
+int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C,
+             const float *scale, hipStream_t stream);
+
+/* gemm_last_error -- message for the calling thread's last failure ("" if none). */
+const char *gemm_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Planner introspection (host only).  A layout is (shape, stride) of up to
+ * GEMM_MAX_RANK modes; a coordinate maps to sum(c_i * stride_i) (Kernel
+ * Authoring skill, section 2 "Layout System", "Coordinate Mapping").
+ * ------------------------------------------------------------------------ */
+#define GEMM_MAX_RANK 8
+
+typedef struct {
+    int64_t M, N, K;
+    int32_t dtype, layout;
+    int32_t elem_bytes, out_bytes;
+    int32_t kernel;          /* 0 tiled, 1 skinny                                     */
+    int32_t tile_m, tile_n;  /* output tile of one workgroup                          */
+    int32_t tile_k_bytes;    /* K bytes consumed per main-loop step (multiple of 64)  */
+    int32_t threads;         /* threads per workgroup                                 */
+    int32_t lds_stages;      /* LDS buffers in the software pipeline                  */
+    int32_t lds_bytes;       /* static LDS per workgroup (<= 160 KiB on gfx950)       */
+    int32_t grid;            /* workgroups per gemm_run launch                        */
+    int32_t tiles_m, tiles_n;
+    int32_t group_m;         /* tile rows per raster group within one XCD             */
+    int32_t split_k;         /* K slices reduced inside a workgroup (skinny kernel)   */
+} gemm_plan_info;
+
+/* gemm_plan_query -- copy the plan's decisions into *info. */
+int gemm_plan_query(const gemm_plan *plan, gemm_plan_info *info);
+
+typedef enum {
+    GEMM_VIEW_A = 0,          /* A bytes:       (M, Kb):(Kb, 1)                              */
+    GEMM_VIEW_B = 1,          /* B bytes:       (N, Kb):(Kb, 1)                              */
+    GEMM_VIEW_B_SHUF = 2,     /* pre-shuffled:  (N/16, Kb/64, 4, 16, 16):(16Kb, 1024, 256, 16, 1) */
+    GEMM_VIEW_B_SRC = 3,      /* B bytes seen through the same 5 coordinates:
+                                 (N/16, Kb/64, 4, 16, 16):(16Kb, 64, 16, Kb, 1)           */
+    GEMM_VIEW_C = 4,          /* C bytes:       (M, N):(N*out_bytes, out_bytes)              */
+    GEMM_VIEW_LDS_A = 5,      /* one LDS stage of A, before the XOR swizzle:
+                                 (tile_m, tile_k_bytes/16, 16):(tile_k_bytes, 16, 1)     */
+    GEMM_VIEW_TILE = 6        /* C tile grid:   (tiles_m, tiles_n):(tile_m*N*ob, tile_n*ob) */
+} gemm_view;
+
+/* gemm_plan_layout -- the byte layout of one view; rank and GEMM_MAX_RANK-long arrays out. */
+int gemm_plan_layout(const gemm_plan *plan, int view, int32_t *rank, int64_t *shape, int64_t *stride);
+
+/* gemm_layout_crd2idx -- sum(crd_i * stride_i); -1 and GEMM_ERR_INVALID_ARG
+ * in gemm_last_error when a coordinate lies outside its mode. */
+int64_t gemm_layout_crd2idx(int32_t rank, const int64_t *shape, const int64_t *stride, const int64_t *crd);
+
+/* gemm_layout_idx2crd -- c_i = (idx / stride_i) % shape_i (the inverse of
+ * crd2idx on an injective layout whose modes do not overlap). */
+int gemm_layout_idx2crd(int32_t rank, const int64_t *shape, const int64_t *stride, int64_t idx, int64_t *crd);
+
+/* gemm_lds_swizzle -- physical 16-byte chunk of logical chunk `chunk` of row
+ * `row` in an LDS tile of `chunks_per_row` chunks (the XOR-16 swizzle the
+ * pages name in section 6 of the Kernel Authoring skill; the function is this
+ * library's choice).  -1 on bad arguments. */
+int32_t gemm_lds_swizzle(int32_t row, int32_t chunk, int32_t chunks_per_row);
+
+/* gemm_tile_of_workgroup -- the (tile_m index, tile_n index) the plan's
+ * XCD-aware raster assigns to workgroup `wg` (0 <= wg < grid). */
+int gemm_tile_of_workgroup(const gemm_plan *plan, int32_t wg, int32_t *tm, int32_t *tn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: device upload, one GEMM through the C
+ABI, decoding of C, and the element-wise acceptance bound.
+
+Acceptance (per element):  |C - C_ref| <= 4e-6 * S + rho * |C_ref|, with
+S = |sigma| * sum_k |a_ik * b_jk| from the oracle, rho = 2^-8 for bf16 inputs
+and 2^-3 for fp8 inputs; NaN or Inf anywhere fails.  Integer-valued inputs
+whose partial sums are exact in fp32 must match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import tiled_gemm_amd as tg
+
+RHO = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -3}
+ABS_COEF = 4e-6
+
+DTYPE_CODE = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
+              ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    bits = np.ascontiguousarray(bits)
+    if bits.dtype == np.uint16:
+        return torch.from_numpy(bits.view(np.int16)).cuda()
+    return torch.from_numpy(bits).cuda()
+
+
+def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
+             scale=(1.0, 1.0), use_scale=True, stream=None, plan=None, return_plan_info=False):
+    """One C = A * B^T through gemm_plan_create / [gemm_preshuffle_b] / gemm_run.
+    Returns the raw bits of C as a numpy array (M x N)."""
+    code = DTYPE_CODE[(dtype, out)]
+    lay = tg.LAYOUTS[layout]
+    own = plan is None
+    if own:
+        plan = tg.Plan(M, N, K, code, lay)
+    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    ob = 4 if out == "f32" else 2
+    A = to_dev(A_bits) if A_bits.size else torch.empty(16, dtype=torch.uint8, device="cuda")
+    B = to_dev(B_bits) if B_bits.size else torch.empty(16, dtype=torch.uint8, device="cuda")
+    Bx = B
+    if layout == "bt_preshuffled" and B_bits.size:
+        Bx = torch.empty(tg.gemm_preshuffled_b_bytes(plan.handle), dtype=torch.uint8, device="cuda")
+        plan.preshuffle_b(B.data_ptr(), Bx.data_ptr(), s)
+    C = torch.full((max(1, M * N * ob),), 0x5A, dtype=torch.uint8, device="cuda")
+    sc = torch.tensor(scale, dtype=torch.float32, device="cuda")
+    plan.run(A.data_ptr(), Bx.data_ptr(), C.data_ptr(), sc.data_ptr() if use_scale else None, s)
+    torch.cuda.synchronize()
+    raw = C.cpu().numpy()[:M * N * ob]
+    info = plan.info()
+    if own:
+        plan.close()
+    bits = raw.view(np.uint32 if out == "f32" else np.uint16).reshape(M, N)
+    return (bits, info) if return_plan_info else bits
+
+
+def decode(bits: np.ndarray) -> np.ndarray:
+    """C bits -> float64 (fp32 or bf16 storage)."""
+    if bits.dtype == np.uint32:
+        return bits.view(np.float32).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_within_bound(C: np.ndarray, C_ref: np.ndarray, S: np.ndarray, dtype: str, what: str = ""):
+    assert np.all(np.isfinite(C)), "%s: non-finite output" % what
+    err = np.abs(C - C_ref)
+    bound = ABS_COEF * S + RHO[dtype] * np.abs(C_ref)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = ", ".join("(%s) got %r want %r bound %r" % (tuple(i), C[tuple(i)], C_ref[tuple(i)],
+                                                             bound[tuple(i)]) for i in idx)
+        raise AssertionError("%s: %d of %d elements outside the bound; %s" % (what, int(bad.sum()), bad.size, detail))
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+
+
+def sample_entries(M: int, N: int, n_random: int, seed: int):
+    """Rows 0 and M-1 in full, columns 0 and N-1 in full, and random entries."""
+    rng = np.random.default_rng(seed)
+    rows = [np.zeros(N, np.int64), np.full(N, M - 1, np.int64), np.arange(M), np.arange(M),
+            rng.integers(0, M, n_random)]
+    cols = [np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1, np.int64),
+            rng.integers(0, N, n_random)]
+    return np.concatenate(rows), np.concatenate(cols)

@@ -1,0 +1,185 @@
+"""Host-side tests of the C ABI: no GPU work is launched here.
+
+* the library loads and exports every function ``include/tgemm.h`` declares;
+* the planner's crd2idx / idx2crd agree with the brute-force oracle and the
+  pages' worked examples;
+* the pre-shuffle layouts the planner hands to the kernel reproduce the
+  oracle's pre-shuffle permutation byte for byte;
+* the LDS swizzle is a bijection with the bank properties it claims;
+* the XCD-aware raster is a bijection onto the tile grid;
+* argument validation rejects what it documents, before any device call.
+"""
+import itertools
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tiled_gemm_amd as tg
+from oracle import layout as OL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tg.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tg.EXPORTS)
+
+
+def test_crd2idx_matches_brute_force(lib):
+    rng = np.random.default_rng(11)
+    layouts = [((8, 16), (1, 8)), ((4, 64), (64, 1)), ((3, 5, 7), (35, 7, 1)),
+               ((2, 3, 4, 5), (1, 2, 6, 24)), ((4, 4, 2), (9, 1, 40))]
+    for _ in range(6):
+        r = int(rng.integers(1, 6))
+        shape = tuple(int(x) for x in rng.integers(1, 5, size=r))
+        stride = tuple(int(x) for x in rng.integers(0, 50, size=r))
+        layouts.append((shape, stride))
+    for shape, stride in layouts:
+        table = OL.brute_force_table(shape, stride)
+        for n, crd in enumerate(OL.all_coords(shape)):
+            assert tg.gemm_layout_crd2idx(shape, stride, crd) == table[n]
+
+
+def test_golden_examples_through_the_planner(lib):
+    with open(os.path.join(GOLDEN, "layout_examples.json")) as f:
+        g = json.load(f)
+    for c in g["crd2idx"]:
+        assert tg.gemm_layout_crd2idx(c["shape"], c["stride"], c["coord"]) == c["index"]
+    for c in g["idx2crd"]:
+        assert tg.gemm_layout_idx2crd(c["shape"], c["stride"], c["index"]) == tuple(c["coord"])
+
+
+def test_crd2idx_rejects_out_of_range(lib):
+    with pytest.raises(tg.GemmError):
+        tg.gemm_layout_crd2idx((8, 16), (1, 8), (8, 0))
+
+
+@pytest.mark.parametrize("dtype,N,K", [(tg.GEMM_BF16_OUT_BF16, 32, 64), (tg.GEMM_BF16_OUT_BF16, 48, 96),
+                                       (tg.GEMM_E4M3_OUT_BF16, 32, 192), (tg.GEMM_E4M3_OUT_BF16, 16, 64)])
+def test_preshuffle_layouts_reproduce_oracle_permutation(lib, dtype, N, K):
+    p = tg.Plan(64, N, K, dtype, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+    dst_shape, dst_stride = tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B_SHUF)
+    src_shape, src_stride = tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B_SRC)
+    assert dst_shape == src_shape
+    eb = 1 if dtype == tg.GEMM_E4M3_OUT_BF16 else 2
+    kbytes = K * eb
+    assert dst_shape == (N // 16, kbytes // 64, 4, 16, 16)
+    rng = np.random.default_rng(N + K)
+    B = rng.integers(0, 256, size=(N, kbytes), dtype=np.uint8)
+    out = np.full(N * kbytes, 0xEE, np.uint8)
+    flat = B.reshape(-1)
+    seen = set()
+    # every 16-byte chunk as the kernel moves it: coordinate -> (src, dst)
+    for crd in itertools.product(*[range(s) for s in dst_shape[:4]]):
+        c5 = crd + (0,)
+        s = tg.gemm_layout_crd2idx(src_shape, src_stride, c5)
+        d = tg.gemm_layout_crd2idx(dst_shape, dst_stride, c5)
+        out[d:d + 16] = flat[s:s + 16]
+        seen.add(d)
+    assert len(seen) == N * kbytes // 16
+    assert tg.gemm_preshuffled_b_bytes(p.handle) == N * kbytes
+    want = OL.preshuffle_b_bytes(B.view(np.uint16) if eb == 2 else B)
+    assert np.array_equal(out, want)
+    p.close()
+
+
+def test_lds_swizzle_bijection_and_banks(lib):
+    for row in range(64):
+        phys = [tg.gemm_lds_swizzle(row, c) for c in range(8)]
+        assert sorted(phys) == list(range(8))
+    for base in range(0, 64, 16):
+        for c in range(8):
+            # 8 consecutive rows aligned to 8: all 8 slots (128-byte bank width)
+            for b8 in (base, base + 8):
+                assert sorted(tg.gemm_lds_swizzle(r, c) for r in range(b8, b8 + 8)) == list(range(8))
+            # 16 rows of 128 bytes = 8 lines of 256 bytes: even rows and odd rows each
+            # cover all 8 slots (256-byte bank width)
+            for par in (0, 1):
+                assert sorted(tg.gemm_lds_swizzle(r, c) for r in range(base + par, base + 16, 2)) == list(range(8))
+    with pytest.raises(tg.GemmError):
+        tg.gemm_lds_swizzle(0, 8)
+
+
+@pytest.mark.parametrize("M,N,K,dtype,layout", [
+    (8192, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED),
+    (4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT),
+    (300, 272, 96, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT),
+    (1000, 4096, 512, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT),
+    (5000, 3000 // 16 * 16, 64, tg.GEMM_BF16_OUT_F32, tg.GEMM_LAYOUT_BT)])
+def test_raster_is_a_bijection(lib, M, N, K, dtype, layout):
+    p = tg.Plan(M, N, K, dtype, layout)
+    info = p.info()
+    tiles = [tg.gemm_tile_of_workgroup(p.handle, wg) for wg in range(info["grid"])]
+    assert len(set(tiles)) == info["grid"] == info["tiles_m"] * info["tiles_n"]
+    assert all(0 <= a < info["tiles_m"] and 0 <= b < info["tiles_n"] for a, b in tiles)
+    # workgroups sharing an XCD (wg % 8) get a contiguous run of the grouped raster
+    if info["grid"] >= 64:
+        xcd0 = [tiles[w] for w in range(0, info["grid"], 8)][:16]
+        rows = {t[0] for t in xcd0}
+        assert len(rows) <= max(info["group_m"], 2)
+    p.close()
+
+
+def test_plan_choices(lib):
+    def info(*a):
+        with tg.Plan(*a) as p:
+            return p.info()
+    c = info(256, 256, 256, tg.GEMM_BF16_OUT_F32, tg.GEMM_LAYOUT_BT)
+    assert c["kernel"] == 0 and c["out_bytes"] == 4
+    c = info(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
+    assert (c["tile_m"], c["tile_n"], c["grid"]) == (256, 256, 256)
+    c = info(8192, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+    assert c["lds_bytes"] <= 160 * 1024 and c["grid"] == 1024
+    c = info(32, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
+    assert c["kernel"] == 1 and c["grid"] == 256
+    c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
+    assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((16, 16, 64, 7, 0), tg.GEMM_ERR_INVALID_ARG),              # unknown dtype
+    ((16, 16, 64, 1, 5), tg.GEMM_ERR_INVALID_ARG),              # unknown layout
+    ((-1, 16, 64, 1, 0), tg.GEMM_ERR_INVALID_ARG),              # negative
+    ((16, 24, 64, 1, 0), tg.GEMM_ERR_UNSUPPORTED),              # N % 16
+    ((16, 16, 40, 1, 0), tg.GEMM_ERR_UNSUPPORTED),              # bf16 K*2 % 64
+    ((16, 16, 96, 2, 0), tg.GEMM_ERR_UNSUPPORTED),              # fp8 K % 64
+    ((16, 16, 1 << 23, 1, 0), tg.GEMM_ERR_UNSUPPORTED),         # row bytes 2^24
+    ((1 << 31, 16, 64, 1, 0), tg.GEMM_ERR_UNSUPPORTED),         # above 2^30
+])
+def test_plan_create_rejects(lib, args, code):
+    h = lib.gemm_plan_create(*args)
+    assert not h
+    assert tg.gemm_last_error() != ""
+
+
+def test_run_argument_errors_before_device(lib):
+    with tg.Plan(64, 64, 64, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert lib.gemm_run(p.handle, None, 0x1000, 0x2000, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_run(p.handle, 0x1008, 0x1000000, 0x2000000, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert "aligned" in tg.gemm_last_error()
+        # C overlapping A
+        assert lib.gemm_run(p.handle, 0x100000, 0x200000, 0x100000, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_b(p.handle, None, 0x1000, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_b(p.handle, 0x1000, 0x1000, None) == tg.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_run(None, 0x1000, 0x2000, 0x3000, None, None) == tg.GEMM_ERR_INVALID_ARG
+    # M == 0 is a successful no-op that touches no device
+    with tg.Plan(0, 64, 64, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert lib.gemm_run(p.handle, None, None, None, None, None) == tg.GEMM_OK

@@ -1,0 +1,219 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact where the arithmetic is exact (integer-valued inputs whose partial
+sums fit fp32), within the stated bound otherwise.  Shapes span several
+tiles with ragged M, N and K tails; the full-size workloads run in the
+launch configuration the benchmark times and are checked on sampled entries.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import tiled_gemm_amd as tg
+import workloads as W
+from gpu_util import assert_within_bound, decode, run_gemm, sample_entries
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [  # (dtype, out, layout, tile) -- tile None = the planner's own choice
+    ("bf16", "f32", "bt", "128x128"), ("bf16", "f32", "bt", "256x256"),
+    ("bf16", "bf16", "bt", "128x128"), ("bf16", "bf16", "bt", "256x256"),
+    ("bf16", "bf16", "bt_preshuffled", "128x128"), ("bf16", "bf16", "bt_preshuffled", "256x256"),
+    ("bf16", "f32", "bt_preshuffled", "256x256"),
+    ("e4m3", "bf16", "bt", "128x128"), ("e4m3", "bf16", "bt", "256x256"),
+    ("e4m3", "bf16", "bt_preshuffled", "128x128"), ("e4m3", "bf16", "bt_preshuffled", "256x256"),
+]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+@pytest.fixture
+def tile_env(monkeypatch):
+    def set_tile(t):
+        if t:
+            monkeypatch.setenv("TGEMM_TILE", t)
+        else:
+            monkeypatch.delenv("TGEMM_TILE", raising=False)
+    return set_tile
+
+
+def exact_check(oracle_mod, inp, M, N, K, dtype, out, layout, scale=(1.0, 1.0)):
+    C_bits = run_gemm(inp.A, inp.B, M, N, K, dtype, out, layout, scale=scale)
+    sigma = oracle_mod.sigma_of(*scale)
+    C_ref, _ = oracle_mod.gemm_bt(inp.A, inp.B, dtype=dtype, sigma=sigma, want_s=False)
+    if out == "f32":
+        want = C_ref.astype(np.float32)
+        assert np.array_equal(want.astype(np.float64), C_ref), "reference not exact in fp32"
+        got = C_bits.view(np.float32)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, "first mismatches %s: got %s want %s" % (
+            bad[:3].tolist(), got[tuple(bad[0])], want[tuple(bad[0])])
+    else:
+        want = oracle_mod.round_bf16(C_ref)
+        bad = np.argwhere(C_bits != want)
+        assert bad.size == 0, "first mismatches %s: got %s want %s (ref %r)" % (
+            bad[:3].tolist(), hex(C_bits[tuple(bad[0])]), hex(want[tuple(bad[0])]), C_ref[tuple(bad[0])])
+
+
+# ------------------------------------------------------------------ config 1
+
+def test_bf16_int_256_bit_exact(oracle_mod):
+    w = W.WORKLOADS["bf16_int_256"]
+    say("case bf16_int_256", w)
+    inp = W.make_inputs(w)
+    exact_check(oracle_mod, inp, w.M, w.N, w.K, "bf16", "f32", "bt")
+
+
+# ------------------------------------------------------------------ integer-exact, every path
+
+@pytest.mark.parametrize("dtype,out,layout,tile", PATHS)
+@pytest.mark.parametrize("shape", ["small", "ragged"])
+def test_integer_exact_every_path(oracle_mod, tile_env, dtype, out, layout, tile, shape):
+    # "ragged": M and N not multiples of the tile, and K*elem_bytes an odd
+    # multiple of 64 so the last 128-byte K step is half full.
+    if shape == "small":
+        M, N, K = 300, 272, 192
+    else:
+        M, N, K = 513, 528, (1056 if dtype == "bf16" else 1088)
+    tile_env(tile)
+    say("case int-exact", dtype, out, layout, tile, M, N, K)
+    inp = W.int_inputs(M, N, K, dtype, seed=M * 7 + N + K)
+    scale = (0.5, 0.25) if dtype == "e4m3" else (1.0, 1.0)
+    exact_check(oracle_mod, inp, M, N, K, dtype, out, layout, scale)
+
+
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("e4m3", "bf16")])
+@pytest.mark.parametrize("M", [1, 17, 32, 33, 64])
+def test_integer_exact_skinny(oracle_mod, tile_env, dtype, out, M):
+    tile_env(None)
+    N, K = 544, 1024 + 64 * (dtype == "bf16")      # bf16: 2176 bytes -> ragged last 128-byte step
+    say("case skinny int-exact", dtype, out, M, N, K)
+    inp = W.int_inputs(M, N, K, dtype, seed=M + 99)
+    with tg.Plan(M, N, K, gpu_dtype(dtype, out), tg.GEMM_LAYOUT_BT) as p:
+        assert p.info()["kernel"] == 1
+    scale = (2.0, 0.125) if dtype == "e4m3" else (1.0, 1.0)
+    exact_check(oracle_mod, inp, M, N, K, dtype, out, "bt", scale)
+
+
+def gpu_dtype(dtype, out):
+    return {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
+            ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}[(dtype, out)]
+
+
+# ------------------------------------------------------------------ random values, full oracle
+
+@pytest.mark.parametrize("dtype,out,layout,tile", PATHS + [("bf16", "bf16", "bt", None), ("e4m3", "bf16", "bt", None)])
+def test_random_within_bound(oracle_mod, tile_env, dtype, out, layout, tile):
+    M, N, K = 520, 784, 1472
+    tile_env(tile)
+    say("case random", dtype, out, layout, tile, M, N, K)
+    w = W.WORKLOADS["e4m3_8192" if dtype == "e4m3" else "bf16_4096"]
+    inp = W.make_inputs(w, M=M, N=N, K=K, seed=4242)
+    C_bits = run_gemm(inp.A, inp.B, M, N, K, dtype, out, layout, scale=(inp.scale_a, inp.scale_b))
+    sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+    C_ref, S = oracle_mod.gemm_bt(inp.A, inp.B, dtype=dtype, sigma=sigma)
+    r = assert_within_bound(decode(C_bits), C_ref, S, dtype, "random %s %s %s" % (dtype, layout, tile))
+    say("  worst err/bound", r)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+
+@pytest.mark.parametrize("name", ["bf16_4096", "bf16_8192_preshuffled", "bf16_skinny_32x8192x8192", "e4m3_8192"])
+def test_full_size_sampled(oracle_mod, tile_env, name):
+    tile_env(None)
+    w = W.WORKLOADS[name]
+    say("case full-size", name)
+    inp = W.make_inputs(w)
+    C_bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout,
+                            scale=(inp.scale_a, inp.scale_b), return_plan_info=True)
+    say("  plan", info)
+    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+    c_ref, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype, sigma=sigma)
+    r = assert_within_bound(decode(C_bits[rows, cols]), c_ref, s, w.dtype, name)
+    say("  worst err/bound", r)
+    # property at any size: no NaN/Inf anywhere in C
+    assert np.all(np.isfinite(decode(C_bits)))
+
+
+# ------------------------------------------------------------------ preshuffle kernel
+
+@pytest.mark.parametrize("dtype,N,K", [("bf16", 48, 96), ("bf16", 256, 1056), ("e4m3", 64, 320), ("bf16", 8192, 8192)])
+def test_preshuffle_byte_exact(dtype, N, K):
+    from oracle import layout as OL
+    say("case preshuffle", dtype, N, K)
+    rng = np.random.default_rng(N + K)
+    code = tg.GEMM_E4M3_OUT_BF16 if dtype == "e4m3" else tg.GEMM_BF16_OUT_BF16
+    if dtype == "bf16":
+        B = rng.integers(0, 65536, size=(N, K), dtype=np.uint32).astype(np.uint16)
+    else:
+        B = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    want = OL.preshuffle_b_bytes(B)
+    with tg.Plan(64, N, K, code, tg.GEMM_LAYOUT_BT_PRESHUFFLED) as p:
+        dB = torch.from_numpy(B.view(np.uint8).reshape(-1).copy()).cuda()
+        out = torch.zeros(tg.gemm_preshuffled_b_bytes(p.handle), dtype=torch.uint8, device="cuda")
+        p.preshuffle_b(dB.data_ptr(), out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_k_zero_gives_zeros(tile_env):
+    tile_env(None)
+    say("case K=0")
+    A = np.zeros((0,), np.uint16)
+    C = run_gemm(A.reshape(64, 0), np.zeros((0,), np.uint16).reshape(32, 0), 64, 32, 0, "bf16", "bf16", "bt")
+    assert np.all(C == 0)
+
+
+def test_m_zero_is_noop():
+    say("case M=0")
+    with tg.Plan(0, 64, 64, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        C = torch.full((16,), 7, dtype=torch.uint8, device="cuda")
+        p.run(0, 0, C.data_ptr(), None, 0)
+        torch.cuda.synchronize()
+        assert torch.all(C == 7)
+
+
+def test_repeat_runs_bitwise_stable(tile_env):
+    tile_env(None)
+    M = N = K = 2048
+    say("case repeat", M, N, K)
+    w = W.WORKLOADS["bf16_4096"]
+    inp = W.make_inputs(w, M=M, N=N, K=K, seed=3)
+    with tg.Plan(M, N, K, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        A, B = torch.from_numpy(inp.A.view(np.int16)).cuda(), torch.from_numpy(inp.B.view(np.int16)).cuda()
+        C0 = torch.empty(M * N, dtype=torch.int16, device="cuda")
+        C1 = torch.empty_like(C0)
+        s = torch.cuda.current_stream().cuda_stream
+        p.run(A.data_ptr(), B.data_ptr(), C0.data_ptr(), None, s)
+        for _ in range(20):
+            p.run(A.data_ptr(), B.data_ptr(), C1.data_ptr(), None, s)
+            torch.cuda.synchronize()
+            assert torch.equal(C0, C1)
+
+
+def test_side_stream_and_scale_pointer(oracle_mod, tile_env):
+    tile_env(None)
+    say("case side stream")
+    M, N, K = 384, 512, 640
+    inp = W.int_inputs(M, N, K, "e4m3", seed=17)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        C_bits = run_gemm(inp.A, inp.B, M, N, K, "e4m3", "bf16", "bt", scale=(4.0, 0.5), stream=st)
+    C_ref, _ = oracle_mod.gemm_bt(inp.A, inp.B, dtype="e4m3", sigma=2.0, want_s=False)
+    assert np.array_equal(C_bits, oracle_mod.round_bf16(C_ref))

@@ -1,0 +1,467 @@
+// C ABI of the tiled GEMM library (declared in include/tgemm.h): the host
+// planner (shape validation, static tile table, layouts, raster) and the
+// launchers.  Host code only; the kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "../../include/tgemm.h"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+using tg::Layout;
+
+struct gemm_plan {
+    gemm_plan_info info;
+    int64_t kbytes;
+    int32_t k_tiles, tail_bytes;
+    const tg::TiledVariant *tiled;     // kernel == 0
+    const tg::SkinnyVariant *skinny;   // kernel == 1
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void ok() { g_last_error.clear(); }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxRowBytes = int64_t(1) << 24;    // 256 rows must fit a 32-bit buffer range
+constexpr int kLdsLimit = 160 * 1024;                   // gfx950 LDS per workgroup
+
+int elem_bytes_of(int dtype) { return dtype == GEMM_E4M3_OUT_BF16 ? 1 : 2; }
+int out_bytes_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? 4 : 2; }
+int elem_of(int dtype) { return dtype == GEMM_E4M3_OUT_BF16 ? tg::kFp8 : tg::kBf16; }
+int out_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? tg::kOutF32 : tg::kOutBf16; }
+
+// Static tile table: the first entry whose predicate holds.  An optional
+// TGEMM_TILE=<bm>x<bn> in the environment forces a tiled variant (sweeps).
+const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
+{
+    int n = 0;
+    const tg::TiledVariant *v = tg::tiled_variants(&n);
+    const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
+    const int elem = elem_of(I.dtype), out = out_of(I.dtype);
+    int want_bm = 0, want_bn = 0;
+    if (const char *e = getenv("TGEMM_TILE"))
+        if (sscanf(e, "%dx%d", &want_bm, &want_bn) != 2)
+            want_bm = want_bn = 0;
+    if (!want_bm) {
+        const int64_t big = ((I.M + 255) / 256) * ((I.N + 255) / 256);
+        want_bm = want_bn = big >= 128 ? 256 : 128;
+    }
+    for (int i = 0; i < n; ++i)
+        if (v[i].bm == want_bm && v[i].bn == want_bn && v[i].elem == elem && v[i].out == out &&
+            v[i].preshuffled == pre)
+            return &v[i];
+    return nullptr;
+}
+
+const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
+{
+    if (I.layout != GEMM_LAYOUT_BT || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE"))
+        return nullptr;
+    const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
+    int n = 0;
+    const tg::SkinnyVariant *v = tg::skinny_variants(&n);
+    for (int i = 0; i < n; ++i)
+        if (v[i].mblocks == mb && v[i].elem == elem_of(I.dtype) && v[i].out == out_of(I.dtype))
+            return &v[i];
+    return nullptr;
+}
+
+Layout make(std::initializer_list<int64_t> shape, std::initializer_list<int64_t> stride)
+{
+    Layout L{};
+    L.rank = (int32_t)shape.size();
+    int i = 0;
+    for (int64_t s : shape)
+        L.shape[i++] = s;
+    i = 0;
+    for (int64_t d : stride)
+        L.stride[i++] = d;
+    return L;
+}
+
+Layout view_of(const gemm_plan &p, int view, bool *okv)
+{
+    const gemm_plan_info &I = p.info;
+    const int64_t Kb = p.kbytes;
+    *okv = true;
+    switch (view) {
+    case GEMM_VIEW_A:
+        return make({I.M, Kb}, {Kb, 1});
+    case GEMM_VIEW_B:
+        return make({I.N, Kb}, {Kb, 1});
+    case GEMM_VIEW_B_SHUF:
+        return make({I.N / 16, Kb / 64, 4, 16, 16}, {16 * Kb, 1024, 256, 16, 1});
+    case GEMM_VIEW_B_SRC:
+        return make({I.N / 16, Kb / 64, 4, 16, 16}, {16 * Kb, 64, 16, Kb, 1});
+    case GEMM_VIEW_C:
+        return make({I.M, I.N}, {I.N * I.out_bytes, I.out_bytes});
+    case GEMM_VIEW_LDS_A:
+        return make({I.tile_m, tg::kChunksPerRow, tg::kChunkBytes}, {tg::kTileKBytes, tg::kChunkBytes, 1});
+    case GEMM_VIEW_TILE:
+        return make({I.tiles_m, I.tiles_n},
+                    {(int64_t)I.tile_m * I.N * I.out_bytes, (int64_t)I.tile_n * I.out_bytes});
+    default:
+        *okv = false;
+        return Layout{};
+    }
+}
+
+// gfx950 check, once per device.
+int check_device()
+{
+    static std::mutex mu;
+    static int verdict[64];   // 0 unknown, 1 ok, -1 not gfx950
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(GEMM_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64)
+        return fail(GEMM_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> g(mu);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(GEMM_ERR_HIP, "hipGetDeviceProperties failed");
+        verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    if (verdict[dev] != 1)
+        return fail(GEMM_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    return GEMM_OK;
+}
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_last_error(void) { return g_last_error.c_str(); }
+
+gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout)
+{
+    if (dtype < GEMM_BF16_OUT_F32 || dtype > GEMM_E4M3_OUT_BF16) {
+        fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+        return nullptr;
+    }
+    if (layout != GEMM_LAYOUT_BT && layout != GEMM_LAYOUT_BT_PRESHUFFLED) {
+        fail(GEMM_ERR_INVALID_ARG, "unknown layout %d", layout);
+        return nullptr;
+    }
+    if (M < 0 || N < 0 || K < 0) {
+        fail(GEMM_ERR_INVALID_ARG, "negative size (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
+             (long long)K);
+        return nullptr;
+    }
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) {
+        fail(GEMM_ERR_UNSUPPORTED, "size above 2^30");
+        return nullptr;
+    }
+    const int eb = elem_bytes_of(dtype), ob = out_bytes_of(dtype);
+    const int64_t kbytes = K * eb;
+    if (N % 16 != 0) {
+        fail(GEMM_ERR_UNSUPPORTED, "N=%lld must be a multiple of 16", (long long)N);
+        return nullptr;
+    }
+    if (kbytes % 64 != 0) {
+        fail(GEMM_ERR_UNSUPPORTED, "K*elem_bytes=%lld must be a multiple of 64 (64-byte K step)",
+             (long long)kbytes);
+        return nullptr;
+    }
+    if (kbytes >= kMaxRowBytes) {
+        fail(GEMM_ERR_UNSUPPORTED, "K*elem_bytes=%lld must be below 2^24", (long long)kbytes);
+        return nullptr;
+    }
+    if (N * ob * 256 >= (int64_t(1) << 32)) {
+        fail(GEMM_ERR_UNSUPPORTED, "N=%lld too large for 32-bit C tile offsets", (long long)N);
+        return nullptr;
+    }
+    if (M * kbytes >= (int64_t(1) << 32) && M <= 64) {
+        fail(GEMM_ERR_UNSUPPORTED, "skinny A above 4 GiB");
+        return nullptr;
+    }
+
+    gemm_plan *p = new (std::nothrow) gemm_plan();
+    if (!p) {
+        fail(GEMM_ERR_INVALID_ARG, "out of host memory");
+        return nullptr;
+    }
+    gemm_plan_info &I = p->info;
+    I.M = M;
+    I.N = N;
+    I.K = K;
+    I.dtype = dtype;
+    I.layout = layout;
+    I.elem_bytes = eb;
+    I.out_bytes = ob;
+    p->kbytes = kbytes;
+    p->k_tiles = (int32_t)((kbytes + tg::kTileKBytes - 1) / tg::kTileKBytes);
+    p->tail_bytes = kbytes % tg::kTileKBytes ? (int32_t)(kbytes % tg::kTileKBytes) : tg::kTileKBytes;
+    I.tile_k_bytes = tg::kTileKBytes;
+    I.split_k = 1;
+
+    if ((p->skinny = pick_skinny(I)) != nullptr) {
+        I.kernel = 1;
+        I.tile_m = p->skinny->mblocks * 16;
+        I.tile_n = tg::kSkinnyTileN;
+        I.threads = tg::kSkinnyThreads;
+        I.lds_stages = 0;
+        I.lds_bytes = p->skinny->lds_bytes;
+        I.tiles_m = 1;
+        I.tiles_n = (int32_t)(N / tg::kSkinnyTileN + (N % tg::kSkinnyTileN ? 1 : 0));
+        I.group_m = 1;
+        I.split_k = tg::kSkinnyThreads / 64;
+        I.grid = I.tiles_n;
+    } else if ((p->tiled = pick_tiled(I)) != nullptr) {
+        I.kernel = 0;
+        I.tile_m = p->tiled->bm;
+        I.tile_n = p->tiled->bn;
+        I.threads = tg::kTiledThreads;
+        I.lds_stages = 2;
+        I.lds_bytes = p->tiled->lds_bytes;
+        I.tiles_m = (int32_t)((M + I.tile_m - 1) / I.tile_m);
+        I.tiles_n = (int32_t)((N + I.tile_n - 1) / I.tile_n);
+        I.group_m = I.tile_m >= 256 ? 4 : 8;
+        if (I.group_m > I.tiles_m)
+            I.group_m = I.tiles_m > 0 ? I.tiles_m : 1;
+        const int64_t grid = (int64_t)I.tiles_m * I.tiles_n;
+        if (grid >= (int64_t(1) << 31)) {
+            delete p;
+            fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
+            return nullptr;
+        }
+        I.grid = (int32_t)grid;
+    } else {
+        delete p;
+        fail(GEMM_ERR_UNSUPPORTED, "no kernel variant for this dtype/layout/tile");
+        return nullptr;
+    }
+    if (I.lds_bytes > kLdsLimit) {
+        delete p;
+        fail(GEMM_ERR_UNSUPPORTED, "tile needs %d bytes of LDS (> 160 KiB)", I.lds_bytes);
+        return nullptr;
+    }
+    ok();
+    return p;
+}
+
+void gemm_plan_destroy(gemm_plan *plan) { delete plan; }
+
+size_t gemm_preshuffled_b_bytes(const gemm_plan *plan)
+{
+    if (!plan)
+        return 0;
+    return (size_t)plan->info.N * (size_t)plan->kbytes;
+}
+
+int gemm_plan_query(const gemm_plan *plan, gemm_plan_info *info)
+{
+    if (!plan || !info)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL plan or info");
+    *info = plan->info;
+    ok();
+    return GEMM_OK;
+}
+
+int gemm_plan_layout(const gemm_plan *plan, int view, int32_t *rank, int64_t *shape, int64_t *stride)
+{
+    if (!plan || !rank || !shape || !stride)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL argument");
+    bool okv = false;
+    const Layout L = view_of(*plan, view, &okv);
+    if (!okv)
+        return fail(GEMM_ERR_INVALID_ARG, "unknown view %d", view);
+    *rank = L.rank;
+    for (int i = 0; i < GEMM_MAX_RANK; ++i) {
+        shape[i] = i < L.rank ? L.shape[i] : 0;
+        stride[i] = i < L.rank ? L.stride[i] : 0;
+    }
+    ok();
+    return GEMM_OK;
+}
+
+int64_t gemm_layout_crd2idx(int32_t rank, const int64_t *shape, const int64_t *stride, const int64_t *crd)
+{
+    if (rank < 0 || rank > GEMM_MAX_RANK || (rank && (!shape || !stride || !crd))) {
+        fail(GEMM_ERR_INVALID_ARG, "bad layout arguments");
+        return -1;
+    }
+    Layout L{};
+    L.rank = rank;
+    for (int i = 0; i < rank; ++i) {
+        if (crd[i] < 0 || crd[i] >= shape[i]) {
+            fail(GEMM_ERR_INVALID_ARG, "coordinate %d = %lld outside [0, %lld)", i, (long long)crd[i],
+                 (long long)shape[i]);
+            return -1;
+        }
+        L.shape[i] = shape[i];
+        L.stride[i] = stride[i];
+    }
+    ok();
+    return tg::crd2idx(L, crd);
+}
+
+int gemm_layout_idx2crd(int32_t rank, const int64_t *shape, const int64_t *stride, int64_t idx, int64_t *crd)
+{
+    if (rank < 0 || rank > GEMM_MAX_RANK || (rank && (!shape || !stride || !crd)) || idx < 0)
+        return fail(GEMM_ERR_INVALID_ARG, "bad layout arguments");
+    Layout L{};
+    L.rank = rank;
+    for (int i = 0; i < rank; ++i) {
+        if (shape[i] <= 0 || stride[i] < 0)
+            return fail(GEMM_ERR_INVALID_ARG, "mode %d: shape must be > 0, stride >= 0", i);
+        L.shape[i] = shape[i];
+        L.stride[i] = stride[i];
+    }
+    tg::idx2crd(L, idx, crd);
+    ok();
+    return GEMM_OK;
+}
+
+int32_t gemm_lds_swizzle(int32_t row, int32_t chunk, int32_t chunks_per_row)
+{
+    if (row < 0 || chunk < 0 || chunks_per_row != tg::kChunksPerRow || chunk >= chunks_per_row) {
+        fail(GEMM_ERR_INVALID_ARG, "swizzle defined for rows of %d chunks", tg::kChunksPerRow);
+        return -1;
+    }
+    ok();
+    return tg::swz_chunk(row, chunk);
+}
+
+int gemm_tile_of_workgroup(const gemm_plan *plan, int32_t wg, int32_t *tm, int32_t *tn)
+{
+    if (!plan || !tm || !tn || wg < 0 || wg >= plan->info.grid)
+        return fail(GEMM_ERR_INVALID_ARG, "bad workgroup query");
+    const gemm_plan_info &I = plan->info;
+    if (I.kernel == 1) {
+        *tm = 0;
+        *tn = wg;
+    } else {
+        int a = 0, b = 0;
+        tg::tile_of_wg(wg, I.grid, I.tiles_m, I.tiles_n, I.group_m, &a, &b);
+        *tm = a;
+        *tn = b;
+    }
+    ok();
+    return GEMM_OK;
+}
+
+int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
+    const size_t bytes = gemm_preshuffled_b_bytes(plan);
+    if (bytes == 0) {
+        ok();
+        return GEMM_OK;
+    }
+    if (!B || !B_shuf)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL B or B_shuf");
+    if (misaligned(B) || misaligned(B_shuf))
+        return fail(GEMM_ERR_INVALID_ARG, "B and B_shuf must be 16-byte aligned");
+    if (overlap(B, bytes, B_shuf, bytes))
+        return fail(GEMM_ERR_INVALID_ARG, "B_shuf overlaps B");
+    if (int rc = check_device())
+        return rc;
+    bool okv = false;
+    tg::PreshuffleArgs a{};
+    a.B = B;
+    a.Bs = B_shuf;
+    a.src = view_of(*plan, GEMM_VIEW_B_SRC, &okv);
+    a.dst = view_of(*plan, GEMM_VIEW_B_SHUF, &okv);
+    a.nblocks = (int32_t)(plan->info.N / 16);
+    a.kblocks = (int32_t)(plan->kbytes / 64);
+    const hipError_t e = tg::launch_preshuffle(a, stream);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "preshuffle launch: %s", hipGetErrorString(e));
+    ok();
+    return GEMM_OK;
+}
+
+int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const float *scale,
+             hipStream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
+    const gemm_plan_info &I = plan->info;
+    if (I.M == 0 || I.N == 0) {
+        ok();
+        return GEMM_OK;
+    }
+    if (!A && I.K)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL A");
+    if (!B && I.K)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL B");
+    if (!C)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL C");
+    if ((A && misaligned(A)) || (B && misaligned(B)) || misaligned(C))
+        return fail(GEMM_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
+    if (scale && ((uintptr_t)scale & 3u))
+        return fail(GEMM_ERR_INVALID_ARG, "scale must be 4-byte aligned");
+    const size_t cbytes = (size_t)I.M * I.N * I.out_bytes;
+    if (overlap(C, cbytes, A, (size_t)I.M * plan->kbytes) || overlap(C, cbytes, B, (size_t)I.N * plan->kbytes))
+        return fail(GEMM_ERR_INVALID_ARG, "C overlaps A or B");
+    if (int rc = check_device())
+        return rc;
+    hipError_t e;
+    if (I.kernel == 1) {
+        tg::SkinnyArgs a{};
+        a.A = A;
+        a.B = B;
+        a.C = C;
+        a.scale = scale;
+        a.M = (int32_t)I.M;
+        a.N = (int32_t)I.N;
+        a.kbytes = (int32_t)plan->kbytes;
+        a.k_tiles = plan->k_tiles;
+        a.tail_bytes = plan->tail_bytes;
+        e = plan->skinny->launch(a, I.grid, stream);
+    } else {
+        tg::TiledArgs a{};
+        a.A = A;
+        a.B = B;
+        a.C = C;
+        a.scale = scale;
+        a.M = (int32_t)I.M;
+        a.N = (int32_t)I.N;
+        a.kbytes = (int32_t)plan->kbytes;
+        a.k_tiles = plan->k_tiles;
+        a.tail_bytes = plan->tail_bytes;
+        a.grid = I.grid;
+        a.tiles_m = I.tiles_m;
+        a.tiles_n = I.tiles_n;
+        a.group_m = I.group_m;
+        e = plan->tiled->launch(a, stream);
+    }
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    ok();
+    return GEMM_OK;
+}
+
+}  // extern "C"

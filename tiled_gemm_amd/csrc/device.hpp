@@ -1,0 +1,97 @@
+// Device-side building blocks for gfx950 (CDNA4): buffer resources, the MFMA
+// atoms, and the fp32 -> bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace tg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Offset that lies past every buffer's record count: a load from it returns
+// zero and a store to it is dropped (buffer range checking).
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
+// lgkmcnt [11:8]); a field at its maximum means "do not wait on it".
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Raw buffer resource over [base, base + bytes).  Word 3 = 0x00020000 is the
+// gfx9-family default (32-bit data format, no swizzle, no stride).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, u32x4 v, uint32_t voff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+
+__device__ inline void buf_store8(__amdgpu_buffer_rsrc_t r, u32x2 v, uint32_t voff)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
+
+// 16 bytes per lane straight from global memory into LDS.  The destination
+// of lane l is lds_wave_base + 16 * l: a wave writes 1 KiB contiguously, so
+// any swizzle is applied on the global side (the lane picks its source).
+__device__ inline void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds_wave_base,
+                                         uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+__device__ inline u32x4 lds_load16(const void *p) { return *(const u32x4 *)p; }
+
+// ---------------------------------------------------------------------------
+// MFMA atoms.  Both compute a 16 x 16 fp32 tile D += X * Y^T over a K slice
+// of 64 bytes (bf16) or 128 bytes (fp8).  Lane l supplies row l % 16 of X and
+// of Y and the K slots (l / 16) of the slice; the result lane l holds
+// D[4 * (l / 16) + v][l % 16], v = 0..3.  X and Y use the same lane/K
+// assignment, so any consistent placement of the K elements into the slots
+// gives the same dot products.
+// ---------------------------------------------------------------------------
+__device__ inline f32x4 mfma_bf16(u32x4 x, u32x4 y, f32x4 acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                   __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
+}
+
+// fp8 e4m3 (format code 0 for both operands), unit E8M0 block scales (127).
+__device__ inline f32x4 mfma_fp8(u32x4 x_lo, u32x4 x_hi, u32x4 y_lo, u32x4 y_hi, f32x4 acc)
+{
+    i32x8 x, y;
+    x.s0 = x_lo.x; x.s1 = x_lo.y; x.s2 = x_lo.z; x.s3 = x_lo.w;
+    x.s4 = x_hi.x; x.s5 = x_hi.y; x.s6 = x_hi.z; x.s7 = x_hi.w;
+    y.s0 = y_lo.x; y.s1 = y_lo.y; y.s2 = y_lo.z; y.s3 = y_lo.w;
+    y.s4 = y_hi.x; y.s5 = y_hi.y; y.s6 = y_hi.z; y.s7 = y_hi.w;
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc, 0, 0, 0, 127, 0, 127);
+}
+
+// Two fp32 -> two bf16 (round to nearest even), packed low-first.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi)
+{
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ inline int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace tg

@@ -1,0 +1,71 @@
+// Kernel argument blocks and launcher entry points shared by the HIP kernel
+// translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace tg {
+
+enum Elem { kBf16 = 0, kFp8 = 1 };
+enum Out { kOutF32 = 0, kOutBf16 = 1 };
+
+struct TiledArgs {
+    const void *A;
+    const void *B;
+    void *C;
+    const float *scale;     // device {s_a, s_b} or nullptr
+    int32_t M, N;
+    int32_t kbytes;         // bytes of one row of A and of B (K * elem_bytes)
+    int32_t k_tiles;        // ceil(kbytes / 128)
+    int32_t tail_bytes;     // valid bytes of the last K tile: 64 or 128
+    int32_t grid, tiles_m, tiles_n, group_m;
+};
+
+struct SkinnyArgs {
+    const void *A;
+    const void *B;
+    void *C;
+    const float *scale;
+    int32_t M, N;
+    int32_t kbytes;
+    int32_t k_tiles;
+    int32_t tail_bytes;
+};
+
+struct PreshuffleArgs {
+    const void *B;
+    void *Bs;
+    Layout src;             // B bytes through the 5 pre-shuffle coordinates
+    Layout dst;             // the pre-shuffled image
+    int32_t nblocks;        // N / 16
+    int32_t kblocks;        // kbytes / 64
+};
+
+// Tiled-kernel variants compiled into the library.
+struct TiledVariant {
+    int bm, bn, wgm, wgn;   // output tile and wave grid (wgm x wgn waves)
+    int elem, out;
+    bool preshuffled;
+    int lds_bytes;
+    hipError_t (*launch)(const TiledArgs &, hipStream_t);
+};
+
+struct SkinnyVariant {
+    int mblocks;            // 16-row blocks of M covered (M <= 16 * mblocks)
+    int elem, out;
+    int lds_bytes;
+    hipError_t (*launch)(const SkinnyArgs &, int grid, hipStream_t);
+};
+
+constexpr int kSkinnyThreads = 512;
+constexpr int kSkinnyTileN = 32;
+constexpr int kTiledThreads = 256;
+
+const TiledVariant *tiled_variants(int *count);
+const SkinnyVariant *skinny_variants(int *count);
+hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
+
+}  // namespace tg

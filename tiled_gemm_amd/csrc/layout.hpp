@@ -1,0 +1,107 @@
+// Layout algebra shared by the host planner and the device code.
+//
+// A layout is a (shape, stride) pair; a coordinate maps to sum(c_i * stride_i)
+// (FlyDSL "Kernel Authoring" skill, section 2 "Layout System", "Coordinate
+// Mapping").  idx2crd is the stride-aware inverse (idx / stride_i) % shape_i,
+// which is how the same page splits a thread index into (wave, lane) through
+// the layout (4,64):(64,1).
+//
+// Also here: the XOR swizzle of 16-byte chunks inside an LDS tile (section 6
+// "GEMM Pattern (Preshuffle)" names an XOR16 swizzle for bank-conflict
+// avoidance without defining it; this is our definition) and the XCD-aware
+// workgroup -> output-tile raster.  Both are used by the kernels and exposed
+// to the host so that tests can check them exhaustively on the CPU.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TG_HD __host__ __device__
+#else
+#define TG_HD
+#endif
+
+namespace tg {
+
+constexpr int kMaxRank = 8;
+
+struct Layout {
+    int32_t rank;
+    int64_t shape[kMaxRank];
+    int64_t stride[kMaxRank];
+};
+
+TG_HD inline int64_t crd2idx(const Layout &L, const int64_t *crd)
+{
+    int64_t idx = 0;
+    for (int i = 0; i < L.rank; ++i)
+        idx += crd[i] * L.stride[i];
+    return idx;
+}
+
+TG_HD inline void idx2crd(const Layout &L, int64_t idx, int64_t *crd)
+{
+    for (int i = 0; i < L.rank; ++i)
+        crd[i] = L.stride[i] == 0 ? 0 : (idx / L.stride[i]) % L.shape[i];
+}
+
+TG_HD inline int64_t size(const Layout &L)
+{
+    int64_t n = 1;
+    for (int i = 0; i < L.rank; ++i)
+        n *= L.shape[i];
+    return n;
+}
+
+// Largest index + 1 (for non-negative strides).
+TG_HD inline int64_t cosize(const Layout &L)
+{
+    int64_t hi = 0;
+    for (int i = 0; i < L.rank; ++i)
+        hi += (L.shape[i] - 1) * L.stride[i];
+    return hi + 1;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile swizzle.  A tile row holds 8 chunks of 16 bytes (128 bytes).
+// Logical chunk c of row r lives at physical chunk c ^ f(r) with
+// f(r) = (r ^ (r >> 3)) & 7.  f is a bijection on the 8 chunk slots for every
+// row; on 8 consecutive rows (aligned to 8) it takes 8 distinct values, and on
+// the even (or odd) rows of 16 consecutive rows (aligned to 16) it also takes
+// 8 distinct values, so a 16-byte-per-lane read of one logical chunk by 16
+// lanes on 16 consecutive rows touches every bank group once whether the LDS
+// serves 128 or 256 bytes per clock.
+// ---------------------------------------------------------------------------
+constexpr int kChunkBytes = 16;
+constexpr int kTileKBytes = 128;                   // K bytes per main-loop step
+constexpr int kChunksPerRow = kTileKBytes / kChunkBytes;
+
+TG_HD constexpr int swz_row(int r) { return (r ^ (r >> 3)) & (kChunksPerRow - 1); }
+TG_HD constexpr int swz_chunk(int r, int c) { return c ^ swz_row(r); }
+
+// ---------------------------------------------------------------------------
+// Workgroup raster.  The dispatcher hands workgroup w to XCD w % 8, so the
+// ids are first renumbered so that each XCD owns a contiguous range; that
+// range is then walked in groups of `group_m` tile rows (column-major inside a
+// group) so the tiles live on one XCD at a time share A rows and B columns in
+// that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
+TG_HD inline void tile_of_wg(int wg, int grid, int tiles_m, int tiles_n, int group_m, int *tm, int *tn)
+{
+    const int xcd = wg % kXcds;
+    const int slot = wg / kXcds;
+    const int per = grid / kXcds;
+    const int rem = grid % kXcds;
+    const int v = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    const int width = group_m * tiles_n;
+    const int g = v / width;
+    const int first = g * group_m;
+    const int gs = (tiles_m - first) < group_m ? (tiles_m - first) : group_m;
+    const int r = v - g * width;
+    *tm = first + r % gs;
+    *tn = r / gs;
+}
+
+}  // namespace tg

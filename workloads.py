@@ -9,7 +9,8 @@ Recipe (every array is raw element bits in row-major order):
 * One ``numpy.random.Generator(PCG64(seed))`` per workload; A is drawn first,
   then B.  Samples are float32.
 * "integers uniform in [-4, 4]": inclusive integers, ``rng.integers(-4, 5)``.
-* "N(mu, sd)": ``rng.standard_normal`` times sd; "U(-1, 1)": ``rng.uniform``.
+* "N(mu, sd)": ``rng.standard_normal`` (float32) times sd plus mu;
+  "U(lo, hi)": ``rng.random`` (float32, [0, 1)) scaled to [lo, hi).
 * bf16: float32 sample rounded to bf16 (nearest-even) by torch's CPU cast.
 * e4m3 (OCP e4m3fn): per-tensor scale s = float32(amax(|X|) / 448), then
   q = e4m3fn(clamp(X / s, -448, 448)) by torch's CPU cast; the scale pair is
@@ -85,7 +86,8 @@ def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
         return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(dist[2])
                 + np.float32(dist[1])).astype(np.float32)
     if kind == "uniform":
-        return rng.uniform(dist[1], dist[2], size=shape).astype(np.float32)
+        u = rng.random(size=shape, dtype=np.float32)          # [0, 1)
+        return (u * np.float32(dist[2] - dist[1]) + np.float32(dist[1])).astype(np.float32)
     raise ValueError("unknown distribution %r" % (kind,))
 
 
