@@ -101,19 +101,31 @@ def test_preshuffle_layouts_reproduce_oracle_permutation(lib, dtype, N, K):
     p.close()
 
 
+def _bank_group(row, phys_chunk):
+    """16-byte bank group (of 16) of a chunk in a tile with 128-byte rows, for
+    an LDS of 64 four-byte banks (256-byte bank line)."""
+    return ((row * 128 + phys_chunk * 16) % 256) // 16
+
+
 def test_lds_swizzle_bijection_and_banks(lib):
     for row in range(64):
         phys = [tg.gemm_lds_swizzle(row, c) for c in range(8)]
         assert sorted(phys) == list(range(8))
-    for base in range(0, 64, 16):
-        for c in range(8):
-            # 8 consecutive rows aligned to 8: all 8 slots (128-byte bank width)
-            for b8 in (base, base + 8):
-                assert sorted(tg.gemm_lds_swizzle(r, c) for r in range(b8, b8 + 8)) == list(range(8))
-            # 16 rows of 128 bytes = 8 lines of 256 bytes: even rows and odd rows each
-            # cover all 8 slots (256-byte bank width)
-            for par in (0, 1):
-                assert sorted(tg.gemm_lds_swizzle(r, c) for r in range(base + par, base + 16, 2)) == list(range(8))
+    # MFMA operand read: lane l reads row base + l % 16, chunk cbase + l // 16.
+    # A read phase joins a rows-0-7 octet with a rows-8-15 octet (any chunk of
+    # the same half); every such pair must touch 16 distinct bank groups.
+    for base in range(0, 256, 16):
+        for cbase in (0, 4):
+            groups = {}
+            for q in range(4):
+                for half in (0, 1):
+                    rows = range(base + 8 * half, base + 8 * half + 8)
+                    groups[(q, half)] = [_bank_group(r, tg.gemm_lds_swizzle(r, cbase + q)) for r in rows]
+                    assert len(set(groups[(q, half)])) == 8
+            for qa in range(4):
+                for qb in range(4):
+                    both = groups[(qa, 0)] + groups[(qb, 1)]
+                    assert len(set(both)) == 16, (base, cbase, qa, qb)
     with pytest.raises(tg.GemmError):
         tg.gemm_lds_swizzle(0, 8)
 

@@ -65,18 +65,24 @@ TG_HD inline int64_t cosize(const Layout &L)
 // ---------------------------------------------------------------------------
 // LDS tile swizzle.  A tile row holds 8 chunks of 16 bytes (128 bytes).
 // Logical chunk c of row r lives at physical chunk c ^ f(r) with
-// f(r) = (r ^ (r >> 3)) & 7.  f is a bijection on the 8 chunk slots for every
-// row; on 8 consecutive rows (aligned to 8) it takes 8 distinct values, and on
-// the even (or odd) rows of 16 consecutive rows (aligned to 16) it also takes
-// 8 distinct values, so a 16-byte-per-lane read of one logical chunk by 16
-// lanes on 16 consecutive rows touches every bank group once whether the LDS
-// serves 128 or 256 bytes per clock.
+// f(r) = (r >> 1) & 7.
+//
+// gfx950's LDS has 64 four-byte banks (256 bytes per clock); a 16-byte read
+// of a wave is served in four phases of 16 lanes, each phase joining one
+// octet of lanes that read rows 0-7 of a 16-row block with one octet that
+// reads rows 8-15 (measured with the LDS bank-conflict counter).  In an MFMA
+// operand read, lane l reads row l % 16 of a 16-row block and a chunk from
+// either {0..3} or {4..7}.  A row pair (2j, 2j+1) forms one 256-byte bank
+// line, and f gives rows 0-7 the values 0-3 and rows 8-15 the values 4-7, so
+// a rows-0-7 octet and a rows-8-15 octet always land in disjoint halves of
+// the 16 bank groups, and inside an octet the 8 lanes hit 8 distinct groups.
+// f is a bijection on the 8 chunk slots of every row and has period 16.
 // ---------------------------------------------------------------------------
 constexpr int kChunkBytes = 16;
 constexpr int kTileKBytes = 128;                   // K bytes per main-loop step
 constexpr int kChunksPerRow = kTileKBytes / kChunkBytes;
 
-TG_HD constexpr int swz_row(int r) { return (r ^ (r >> 3)) & (kChunksPerRow - 1); }
+TG_HD constexpr int swz_row(int r) { return (r >> 1) & (kChunksPerRow - 1); }
 TG_HD constexpr int swz_chunk(int r, int c) { return c ^ swz_row(r); }
 
 // ---------------------------------------------------------------------------
