@@ -67,6 +67,21 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
         const int64_t big = ((I.M + 255) / 256) * ((I.N + 255) / 256);
         want_bm = want_bn = big >= 128 ? 256 : 128;
     }
+    // Pre-shuffled B at 256 x 256: the dedicated pipelined kernel, unless
+    // TGEMM_BPRE=0 asks for the generic one.
+    const char *bp = getenv("TGEMM_BPRE");
+    if (pre && want_bm == 256 && want_bn == 256 && !(bp && bp[0] == '0')) {
+        int nb = 0;
+        const tg::TiledVariant *b = tg::bpre_variants(&nb);
+        if (const char *e = getenv("TGEMM_BPRE_VARIANT")) {
+            const int k = atoi(e);
+            if (k >= 0 && k < nb && b[k].elem == elem && b[k].out == out)
+                return &b[k];
+        }
+        for (int i = 0; i < nb; ++i)
+            if (b[i].elem == elem && b[i].out == out)
+                return &b[i];
+    }
     for (int i = 0; i < n; ++i)
         if (v[i].bm == want_bm && v[i].bn == want_bn && v[i].elem == elem && v[i].out == out &&
             v[i].preshuffled == pre)
@@ -241,9 +256,10 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         I.kernel = 0;
         I.tile_m = p->tiled->bm;
         I.tile_n = p->tiled->bn;
-        I.threads = tg::kTiledThreads;
-        I.lds_stages = 2;
+        I.threads = 64 * p->tiled->wgm * p->tiled->wgn;
         I.lds_bytes = p->tiled->lds_bytes;
+        I.lds_stages = I.lds_bytes / (I.tile_m * tg::kTileKBytes +
+                                      (p->tiled->preshuffled ? 0 : I.tile_n * tg::kTileKBytes));
         I.tiles_m = (int32_t)((M + I.tile_m - 1) / I.tile_m);
         I.tiles_n = (int32_t)((N + I.tile_n - 1) / I.tile_n);
         I.group_m = I.tile_m >= 256 ? 4 : 8;

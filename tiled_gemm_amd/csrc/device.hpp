@@ -73,6 +73,17 @@ __device__ inline f32x4 mfma_bf16(u32x4 x, u32x4 y, f32x4 acc)
 }
 
 // fp8 e4m3 (format code 0 for both operands), unit E8M0 block scales (127).
+__device__ inline f32x4 mfma_fp8x8(i32x8 x, i32x8 y, f32x4 acc)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc, 0, 0, 0, 127, 0, 127);
+}
+
+// Two 16-byte halves as one 32-byte fp8 operand.
+__device__ inline i32x8 join32(u32x4 lo, u32x4 hi)
+{
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ inline f32x4 mfma_fp8(u32x4 x_lo, u32x4 x_hi, u32x4 y_lo, u32x4 y_hi, f32x4 acc)
 {
     i32x8 x, y;

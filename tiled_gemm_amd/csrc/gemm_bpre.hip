@@ -1,0 +1,292 @@
+// Pre-shuffled-B GEMM C = A * B^T, the kernel behind GEMM_LAYOUT_BT_PRESHUFFLED
+// for large M (FlyDSL "Kernel Authoring" skill, section 6 "GEMM Pattern
+// (Preshuffle)": B pre-shuffled into MFMA operand order, A staged through
+// XOR-swizzled LDS, 64-byte K micro-steps, LDS ping-pong; section 3 "Runtime
+// Loops with Loop-Carried Values" for the prefetch-next / compute-current
+// loop).
+//
+// Workgroup: WAVES waves (two per SIMD at 8), 256 x 256 output tile, waves
+// side by side along N (each wave owns all 256 rows and 256 / WAVES columns,
+// so no B byte is loaded twice).  Main-loop step: 128 bytes of K.
+//
+//   A   global -> LDS by 16-byte buffer loads that write LDS directly, into a
+//       ring of NS stages (NS - 2 tiles in flight beyond the one being read).
+//   B   global -> VGPRs, one 16-byte load per lane per 1 KiB operand block,
+//       issued at the start of the step before its use, in two register sets
+//       renamed by unrolling the loop.
+//   LDS -> VGPR: the A fragments of a step form one ordered stream; each
+//       fragment is requested PD groups before its MFMAs, and the first PD
+//       fragments of step k+1 are requested during the last PD groups of
+//       step k.
+//   Sync: one barrier per step, placed PD groups before the step's end.  At
+//       that point the wave waits (exact vmcnt) for A tile k+1, meets the
+//       other waves, then issues A tile k+NS-1 into the stage every wave
+//       finished reading in step k-1.  Every load is issued unconditionally
+//       (tiles past the end read out of range and return zeros), so the
+//       number of loads in flight behind any given load is fixed and the
+//       vmcnt immediates are exact.
+//   Epilogue as in the generic tiled kernel: (acc * s_a) * s_b, RNE to bf16,
+//   buffer stores (rows past M and columns past N dropped).
+#include "device.hpp"
+#include "kernels.hpp"
+
+#include <type_traits>
+
+namespace tg {
+
+namespace {
+
+constexpr int BP_BM = 256;
+constexpr int BP_BN = 256;
+constexpr int BP_STAGE = BP_BM * kTileKBytes;                       // 32 KiB of A per stage
+
+template <int WGM, int WGN, int NS>
+struct BpCfg {
+    static constexpr int WAVES = WGM * WGN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WTM = BP_BM / WGM;                        // rows per wave
+    static constexpr int WTN = BP_BN / WGN;                        // columns per wave
+    static constexpr int FM = WTM / 16;                            // 16-row blocks per wave
+    static constexpr int FN = WTN / 16;                            // 16-column blocks per wave
+    static constexpr int AR = BP_STAGE / (THREADS * kChunkBytes);  // DMA rounds per stage
+    static constexpr int BR = FN * 2;                              // B loads per lane per step
+    static constexpr int LDS = NS * BP_STAGE;
+    static_assert(NS >= 4, "the barrier schedule needs two stages beyond read/ready");
+    static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+};
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+}  // namespace
+
+// ELEM: kBf16 (2 x 16x16x32 per step) or kFp8 (1 x 16x16x128 per step).
+// PD: fragment prefetch distance in groups.
+template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const TiledArgs p)
+{
+    using Cfg = BpCfg<WGM, WGN, NS>;
+    constexpr int WAVES = Cfg::WAVES;
+    constexpr int BP_FM = Cfg::FM, BP_FN = Cfg::FN, BP_AR = Cfg::AR, BP_BR = Cfg::BR;
+    constexpr int BP_WTM = Cfg::WTM, BP_WTN = Cfg::WTN;
+    // Fragment stream of one step: bf16 -> 2 sub-steps x 16 row blocks, one
+    // 16-byte read each; fp8 -> 16 row blocks, two reads (chunks q, q+4).
+    constexpr int NG = ELEM == kBf16 ? 2 * BP_FM : BP_FM;   // groups (4 MFMAs each)
+    static_assert(PD >= 1 && PD < NG / 2, "prefetch distance");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
+
+    const int w = wave_id();
+    const int l = lane_id();
+    const int q = l >> 4, r16 = l & 15;
+    const int wm = w / WGN, wn = w % WGN;
+
+    int tm, tn;
+    tile_of_wg(blockIdx.x, p.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const int m0 = tm * BP_BM, n0 = tn * BP_BN;
+    const int rows_a = min(p.M - m0, BP_BM);
+    const int rows_b = min(p.N - n0, BP_BN);
+    const uint32_t kb = (uint32_t)p.kbytes;
+    const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
+    const int nk = p.k_tiles;
+    const uint32_t tail = (uint32_t)p.tail_bytes;
+
+    // ---- A: global -> LDS source offsets, as in the generic kernel.
+    uint32_t voffA[BP_AR];
+    uint32_t tailA = 0;
+#pragma unroll
+    for (int r = 0; r < BP_AR; ++r) {
+        const int pc = (r * WAVES + w) * 64 + l;
+        const int row = pc >> 3;
+        const int c = swz_chunk(row, pc & 7);
+        voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
+        tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+    }
+    auto issue_a = [&](int kt) {
+        const bool beyond = kt >= nk;
+        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+        uint8_t *sA = lds + (kt % NS) * BP_STAGE;
+        const uint32_t soff = (uint32_t)kt * kTileKBytes;
+#pragma unroll
+        for (int r = 0; r < BP_AR; ++r) {
+            const uint32_t vo = beyond || (part && !((tailA >> r) & 1u)) ? kOobOffset : voffA[r];
+            buf_load16_to_lds(rA, sA + (r * WAVES + w) * 1024, vo, soff);
+        }
+    };
+
+    // ---- B: n-block (w * FN + j) of the workgroup, k-blocks 2kt and 2kt+1.
+    uint32_t voffB[BP_FN];
+#pragma unroll
+    for (int j = 0; j < BP_FN; ++j)
+        voffB[j] = (uint32_t)(wn * BP_FN + j) * 16u * kb + (uint32_t)l * 16u;
+    u32x4 bq[2][BP_FN][2];
+    auto issue_b = [&](int kt, auto set_c) {
+        constexpr int S = decltype(set_c)::value;
+        const bool beyond = kt >= nk;
+        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+        const uint32_t soff = (uint32_t)kt * 2048u;
+#pragma unroll
+        for (int j = 0; j < BP_FN; ++j) {
+            bq[S][j][0] = buf_load16(rB, beyond ? kOobOffset : voffB[j], soff);
+            bq[S][j][1] = buf_load16(rB, beyond || part ? kOobOffset : voffB[j] + 1024u, soff);
+        }
+    };
+
+    f32x4 acc[BP_FM][BP_FN];
+#pragma unroll
+    for (int i = 0; i < BP_FM; ++i)
+#pragma unroll
+        for (int j = 0; j < BP_FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- fragment stream.  Group g of a step reads A row block g % FM at
+    // chunk (g / FM) * 4 + q (bf16) or chunks q and q + 4 (fp8).
+    using FragT = typename std::conditional<ELEM == kFp8, i32x8, u32x4>::type;
+    FragT fa[NG];
+    auto frag_addr = [&](int stage, int g, int half) -> const uint8_t * {
+        const int i = g % BP_FM;
+        const int c = ELEM == kBf16 ? (g / BP_FM) * 4 + q : half * 4 + q;
+        const int row = wm * BP_WTM + i * 16 + r16;
+        return lds + stage * BP_STAGE + row * kTileKBytes + swz_chunk(row, c) * kChunkBytes;
+    };
+    auto load_frag = [&](int stage, int g) {
+        const u32x4 lo = lds_load16(frag_addr(stage, g, 0));
+        if constexpr (ELEM == kFp8)
+            fa[g] = join32(lo, lds_load16(frag_addr(stage, g, 1)));
+        else
+            fa[g] = lo;
+    };
+    auto mma_group = [&](int g, auto set_c) {
+        constexpr int S = decltype(set_c)::value;
+        const int i = g % BP_FM;
+#pragma unroll
+        for (int j = 0; j < BP_FN; ++j) {
+            if constexpr (ELEM == kBf16)
+                acc[i][j] = mfma_bf16(bq[S][j][g / BP_FM], fa[g], acc[i][j]);
+            else
+                acc[i][j] = mfma_fp8x8(join32(bq[S][j][0], bq[S][j][1]), fa[g], acc[i][j]);
+        }
+    };
+
+    // Load issue order (one entry per step k):
+    //   start(k):   B(k+1)                      BP_BR loads
+    //   barrier(k): A tile k+NS-1 (DMA)         BP_AR loads
+    // At start(k), B(k) needs the loads issued after it done except the
+    // A(k+NS-2) DMA: vmcnt(AR).  At barrier(k), A tile k+1 (issued at
+    // barrier(k+2-NS)) has (NS-2) B issues and (NS-3) A issues behind it.
+    constexpr int kVmStart = BP_AR;
+    constexpr int kVmBarrier = (NS - 2) * BP_BR + (NS - 3) * BP_AR;
+    static_assert(kVmBarrier < 64, "vmcnt is 6 bits");
+    auto wait_vm = [&](auto n_c) {
+        constexpr int n = decltype(n_c)::value;
+        __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | (n & 0xF) | ((n >> 4) << 14));
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One step.  Set CUR holds B(kt); set 1-CUR receives B(kt+1).
+    auto step = [&](int kt, auto cur_c) {
+        constexpr int CUR = decltype(cur_c)::value;
+        const int st = kt % NS;
+        wait_vm(ic<kVmStart>{});
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(kt + 1, ic<1 - CUR>{});
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g == NG - PD) {
+                wait_vm(ic<kVmBarrier>{});
+                barrier();
+                issue_a(kt + NS - 1);
+            }
+            // prefetch: group g + PD of this step, or group g + PD - NG of the next
+            if (g + PD < NG)
+                load_frag(st, g + PD);
+            else
+                load_frag((kt + 1) % NS, g + PD - NG);
+            mma_group(g, ic<CUR>{});
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- prologue: the loads of virtual steps 1-NS .. -1 (B(k+1) only for
+    // k+1 >= 0, so the first barriers wait for everything), then the first
+    // fragments.
+    for (int v = 1 - NS; v < 0; ++v) {
+        if (v == -1)
+            issue_b(0, ic<0>{});
+        issue_a(v + NS - 1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+#pragma unroll
+    for (int g = 0; g < PD; ++g)
+        load_frag(0, g);
+    // Steps run in pairs; when nk is odd the last one is a phantom step whose
+    // operands are all out of range, i.e. zeros, and adds exact zeros.
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, ic<0>{});
+        step(kt + 1, ic<1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // ---- epilogue
+    float sa = 1.f, sb = 1.f;
+    if (p.scale != nullptr) {
+        sa = p.scale[0];
+        sb = p.scale[1];
+    }
+    constexpr int OB = OUT == kOutF32 ? 4 : 2;
+    const uint32_t ldc = (uint32_t)p.N * OB;
+    const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+#pragma unroll
+    for (int i = 0; i < BP_FM; ++i) {
+        const int row = wm * BP_WTM + i * 16 + r16;
+#pragma unroll
+        for (int j = 0; j < BP_FN; ++j) {
+            const int col = n0 + wn * BP_WTN + j * 16 + 4 * q;
+            const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
+            f32x4 v = acc[i][j];
+            v = (v * sa) * sb;
+            if constexpr (OUT == kOutF32)
+                buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
+            else
+                buf_store8(rC, u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)}, voff);
+        }
+    }
+}
+
+template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD>
+static hipError_t launch_bpre(const TiledArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_bpre_kernel<ELEM, OUT, WGM, WGN, NS, PD>), dim3(a.grid), dim3(64 * WGM * WGN), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+#define TG_BPRE(ELEM, OUT, WGM, WGN, NS, PD)                                                    \
+    TiledVariant{BP_BM, BP_BN, WGM, WGN, ELEM, OUT, true, BpCfg<WGM, WGN, NS>::LDS,              \
+                 &launch_bpre<ELEM, OUT, WGM, WGN, NS, PD>}
+
+// The first variant of each (elem, out) is the planner's choice; the rest
+// are alternatives selectable by index with TGEMM_BPRE_VARIANT (sweeps).
+static const TiledVariant kBpre[] = {
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 4),
+    TG_BPRE(kBf16, kOutF32, 1, 8, 4, 4),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 2),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 6),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 5, 4),
+    TG_BPRE(kBf16, kOutBf16, 2, 4, 4, 4),
+    TG_BPRE(kBf16, kOutBf16, 2, 4, 5, 4),
+    TG_BPRE(kBf16, kOutBf16, 1, 4, 4, 4),
+};
+
+const TiledVariant *bpre_variants(int *count)
+{
+    *count = (int)(sizeof(kBpre) / sizeof(kBpre[0]));
+    return kBpre;
+}
+
+}  // namespace tg
