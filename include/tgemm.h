@@ -70,7 +70,9 @@ typedef struct gemm_plan gemm_plan;   /* opaque, immutable after creation */
  * Requirements (else NULL with GEMM_ERR_UNSUPPORTED / GEMM_ERR_INVALID_ARG):
  *   0 <= M, N, K <= 2^30;  N % 16 == 0;
  *   K * elem_bytes % 64 == 0 -- the 64-byte K step of the pages' GEMM (Kernel
- *   Authoring skill, section 10 "Troubleshooting", tile_k rule).
+ *   Authoring skill, section 10 "Troubleshooting", tile_k rule);
+ *   K * elem_bytes < 2^23 and N * out_bytes * 256 < 2^31 (a 256-row tile of
+ *   any operand stays inside one 2^31-byte buffer range).
  * Host only: no device work, no allocation on the device.  Returns a plan the
  * caller frees with gemm_plan_destroy.
  */

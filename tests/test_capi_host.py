@@ -173,7 +173,7 @@ def test_plan_choices(lib):
     ((16, 24, 64, 1, 0), tg.GEMM_ERR_UNSUPPORTED),              # N % 16
     ((16, 16, 40, 1, 0), tg.GEMM_ERR_UNSUPPORTED),              # bf16 K*2 % 64
     ((16, 16, 96, 2, 0), tg.GEMM_ERR_UNSUPPORTED),              # fp8 K % 64
-    ((16, 16, 1 << 23, 1, 0), tg.GEMM_ERR_UNSUPPORTED),         # row bytes 2^24
+    ((16, 16, 1 << 22, 1, 0), tg.GEMM_ERR_UNSUPPORTED),         # row bytes 2^23
     ((1 << 31, 16, 64, 1, 0), tg.GEMM_ERR_UNSUPPORTED),         # above 2^30
 ])
 def test_plan_create_rejects(lib, args, code):

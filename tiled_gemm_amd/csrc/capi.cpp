@@ -11,7 +11,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/tgemm.h"
+#include "tgemm.h"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -43,7 +43,7 @@ int fail(int code, const char *fmt, ...)
 void ok() { g_last_error.clear(); }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
-constexpr int64_t kMaxRowBytes = int64_t(1) << 24;    // 256 rows must fit a 32-bit buffer range
+constexpr int64_t kMaxRowBytes = int64_t(1) << 23;    // 256 rows stay below 2^31 bytes of buffer range
 constexpr int kLdsLimit = 160 * 1024;                   // gfx950 LDS per workgroup
 
 int elem_bytes_of(int dtype) { return dtype == GEMM_E4M3_OUT_BF16 ? 1 : 2; }
@@ -209,10 +209,10 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         return nullptr;
     }
     if (kbytes >= kMaxRowBytes) {
-        fail(GEMM_ERR_UNSUPPORTED, "K*elem_bytes=%lld must be below 2^24", (long long)kbytes);
+        fail(GEMM_ERR_UNSUPPORTED, "K*elem_bytes=%lld must be below 2^23", (long long)kbytes);
         return nullptr;
     }
-    if (N * ob * 256 >= (int64_t(1) << 32)) {
+    if (N * ob * 256 >= (int64_t(1) << 31)) {
         fail(GEMM_ERR_UNSUPPORTED, "N=%lld too large for 32-bit C tile offsets", (long long)N);
         return nullptr;
     }

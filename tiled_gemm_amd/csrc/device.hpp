@@ -17,8 +17,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Offset that lies past every buffer's record count: a load from it returns
-// zero and a store to it is dropped (buffer range checking).
+// Offset that lies past every buffer's record count (the planner keeps
+// record counts below 2^31): a load from it returns zero and a store to it is
+// dropped (buffer range checking).
 constexpr uint32_t kOobOffset = 0x80000000u;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
@@ -35,6 +36,20 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+// Compiler-only memory fence: keeps the loads issued before it ahead of the
+// memory operations after it (no instruction, no wait), so a software
+// pipeline's loads stay where it issues them instead of sinking towards
+// their first use.
+__device__ inline void issue_fence() { asm volatile("" ::: "memory"); }
+
+// Branch-free choice of a buffer offset: `off` when `keep`, else an offset
+// past the record count (which the planner keeps below 2^31).
+__device__ inline uint32_t keep_or_oob(bool keep, uint32_t off)
+{
+    const uint32_t m = 0u - (uint32_t)keep;           // all ones when kept
+    return (off & m) | (kOobOffset & ~m);
 }
 
 __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, u32x4 v, uint32_t voff)

@@ -62,7 +62,9 @@ using ic = std::integral_constant<int, N>;
 
 // ELEM: kBf16 (2 x 16x16x32 per step) or kFp8 (1 x 16x16x128 per step).
 // PD: fragment prefetch distance in groups.
-template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD>
+// ADMA: A goes global -> LDS by the load's own LDS write (true) or through
+// VGPRs: loaded at barrier(k), written with ds_write_b128 at barrier(k+1).
+template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD, bool ADMA>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const TiledArgs p)
 {
     using Cfg = BpCfg<WGM, WGN, NS>;
@@ -102,6 +104,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
         voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
         tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
     }
+    u32x4 stA[BP_AR];                           // staging (ADMA == false)
+    int stA_tile = 0;
     auto issue_a = [&](int kt) {
         const bool beyond = kt >= nk;
         const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
@@ -109,9 +113,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
         const uint32_t soff = (uint32_t)kt * kTileKBytes;
 #pragma unroll
         for (int r = 0; r < BP_AR; ++r) {
-            const uint32_t vo = beyond || (part && !((tailA >> r) & 1u)) ? kOobOffset : voffA[r];
-            buf_load16_to_lds(rA, sA + (r * WAVES + w) * 1024, vo, soff);
+            const bool keep = !beyond & (!part | (((tailA >> r) & 1u) != 0));
+            const uint32_t vo = keep_or_oob(keep, voffA[r]);
+            if constexpr (ADMA)
+                buf_load16_to_lds(rA, sA + (r * WAVES + w) * 1024, vo, soff);
+            else
+                stA[r] = buf_load16(rA, vo, soff);
         }
+        stA_tile = kt;
+        issue_fence();
+    };
+    // ADMA == false: write the staged tile into its stage (lane l of round r
+    // at byte (r * WAVES + w) * 1024 + 16 l, the same place the DMA writes).
+    auto store_a = [&]() {
+        uint8_t *sA = lds + (stA_tile % NS) * BP_STAGE;
+#pragma unroll
+        for (int r = 0; r < BP_AR; ++r)
+            *(u32x4 *)(sA + (r * WAVES + w) * 1024 + l * 16) = stA[r];
     };
 
     // ---- B: n-block (w * FN + j) of the workgroup, k-blocks 2kt and 2kt+1.
@@ -127,9 +145,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
         const uint32_t soff = (uint32_t)kt * 2048u;
 #pragma unroll
         for (int j = 0; j < BP_FN; ++j) {
-            bq[S][j][0] = buf_load16(rB, beyond ? kOobOffset : voffB[j], soff);
-            bq[S][j][1] = buf_load16(rB, beyond || part ? kOobOffset : voffB[j] + 1024u, soff);
+            bq[S][j][0] = buf_load16(rB, keep_or_oob(!beyond, voffB[j]), soff);
+            bq[S][j][1] = buf_load16(rB, keep_or_oob(!beyond & !part, voffB[j] + 1024u), soff);
         }
+        issue_fence();
     };
 
     f32x4 acc[BP_FM][BP_FN];
@@ -174,8 +193,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
     // At start(k), B(k) needs the loads issued after it done except the
     // A(k+NS-2) DMA: vmcnt(AR).  At barrier(k), A tile k+1 (issued at
     // barrier(k+2-NS)) has (NS-2) B issues and (NS-3) A issues behind it.
+    // With ADMA == false the A loads land in VGPRs and the compiler waits for
+    // them before the ds_write; the barrier then needs no vmcnt, and the LDS
+    // stores of the previous barrier are covered by waiting until at most the
+    // fragment reads issued since remain (LDS operations retire in order).
     constexpr int kVmStart = BP_AR;
     constexpr int kVmBarrier = (NS - 2) * BP_BR + (NS - 3) * BP_AR;
+    constexpr int kLgkmBarrier = PD * (ELEM == kFp8 ? 2 : 1);
     static_assert(kVmBarrier < 64, "vmcnt is 6 bits");
     auto wait_vm = [&](auto n_c) {
         constexpr int n = decltype(n_c)::value;
@@ -197,9 +221,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             if (g == NG - PD) {
-                wait_vm(ic<kVmBarrier>{});
-                barrier();
-                issue_a(kt + NS - 1);
+                if constexpr (ADMA) {
+                    wait_vm(ic<kVmBarrier>{});
+                    barrier();
+                    issue_a(kt + NS - 1);
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00 | (kLgkmBarrier << 8));
+                    barrier();
+                    store_a();                       // tile kt+NS-2, loaded at barrier(kt-1)
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_a(kt + NS - 1);
+                }
             }
             // prefetch: group g + PD of this step, or group g + PD - NG of the next
             if (g + PD < NG)
@@ -217,9 +249,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
     for (int v = 1 - NS; v < 0; ++v) {
         if (v == -1)
             issue_b(0, ic<0>{});
+        if constexpr (!ADMA) {
+            if (v > 1 - NS) {
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                store_a();
+            }
+        }
         issue_a(v + NS - 1);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);      // vmcnt(0) lgkmcnt(0)
     barrier();
 #pragma unroll
     for (int g = 0; g < PD; ++g)
@@ -258,29 +296,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
     }
 }
 
-template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD>
+template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD, bool ADMA>
 static hipError_t launch_bpre(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_bpre_kernel<ELEM, OUT, WGM, WGN, NS, PD>), dim3(a.grid), dim3(64 * WGM * WGN), 0,
-                       s, a);
+    hipLaunchKernelGGL((gemm_bpre_kernel<ELEM, OUT, WGM, WGN, NS, PD, ADMA>), dim3(a.grid), dim3(64 * WGM * WGN),
+                       0, s, a);
     return hipGetLastError();
 }
 
-#define TG_BPRE(ELEM, OUT, WGM, WGN, NS, PD)                                                    \
+#define TG_BPRE(ELEM, OUT, WGM, WGN, NS, PD, ADMA)                                              \
     TiledVariant{BP_BM, BP_BN, WGM, WGN, ELEM, OUT, true, BpCfg<WGM, WGN, NS>::LDS,              \
-                 &launch_bpre<ELEM, OUT, WGM, WGN, NS, PD>}
+                 &launch_bpre<ELEM, OUT, WGM, WGN, NS, PD, ADMA>}
 
 // The first variant of each (elem, out) is the planner's choice; the rest
 // are alternatives selectable by index with TGEMM_BPRE_VARIANT (sweeps).
 static const TiledVariant kBpre[] = {
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 4),
-    TG_BPRE(kBf16, kOutF32, 1, 8, 4, 4),
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 2),
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 6),
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 5, 4),
-    TG_BPRE(kBf16, kOutBf16, 2, 4, 4, 4),
-    TG_BPRE(kBf16, kOutBf16, 2, 4, 5, 4),
-    TG_BPRE(kBf16, kOutBf16, 1, 4, 4, 4),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 4, true),
+    TG_BPRE(kBf16, kOutF32, 1, 8, 4, 4, true),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 4, false),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 5, 4, false),
+    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 6, false),
 };
 
 const TiledVariant *bpre_variants(int *count)
