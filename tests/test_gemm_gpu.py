@@ -18,13 +18,16 @@ from gpu_util import assert_within_bound, decode, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [  # (dtype, out, layout, tile) -- tile None = the planner's own choice
-    ("bf16", "f32", "bt", "128x128"), ("bf16", "f32", "bt", "256x256"),
-    ("bf16", "bf16", "bt", "128x128"), ("bf16", "bf16", "bt", "256x256"),
+# (dtype, out, layout, tile) -- tile None = the planner's own choice; "256x256"
+# is the software-pipelined kernel, "256x256g" the generic tiled kernel.
+PATHS = [
+    ("bf16", "f32", "bt", "128x128"), ("bf16", "f32", "bt", "256x256"), ("bf16", "f32", "bt", "256x256g"),
+    ("bf16", "bf16", "bt", "128x128"), ("bf16", "bf16", "bt", "256x256"), ("bf16", "bf16", "bt", "256x256g"),
     ("bf16", "bf16", "bt_preshuffled", "128x128"), ("bf16", "bf16", "bt_preshuffled", "256x256"),
-    ("bf16", "f32", "bt_preshuffled", "256x256"),
-    ("e4m3", "bf16", "bt", "128x128"), ("e4m3", "bf16", "bt", "256x256"),
+    ("bf16", "bf16", "bt_preshuffled", "256x256g"), ("bf16", "f32", "bt_preshuffled", "256x256"),
+    ("e4m3", "bf16", "bt", "128x128"), ("e4m3", "bf16", "bt", "256x256"), ("e4m3", "bf16", "bt", "256x256g"),
     ("e4m3", "bf16", "bt_preshuffled", "128x128"), ("e4m3", "bf16", "bt_preshuffled", "256x256"),
+    ("e4m3", "bf16", "bt_preshuffled", "256x256g"),
 ]
 
 
@@ -43,6 +46,10 @@ def _gpu():
 @pytest.fixture
 def tile_env(monkeypatch):
     def set_tile(t):
+        monkeypatch.delenv("TGEMM_PIPE", raising=False)
+        if t and t.endswith("g"):
+            monkeypatch.setenv("TGEMM_PIPE", "0")
+            t = t[:-1]
         if t:
             monkeypatch.setenv("TGEMM_TILE", t)
         else:

@@ -67,19 +67,20 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
         const int64_t big = ((I.M + 255) / 256) * ((I.N + 255) / 256);
         want_bm = want_bn = big >= 128 ? 256 : 128;
     }
-    // Pre-shuffled B at 256 x 256: the dedicated pipelined kernel, unless
-    // TGEMM_BPRE=0 asks for the generic one.
-    const char *bp = getenv("TGEMM_BPRE");
-    if (pre && want_bm == 256 && want_bn == 256 && !(bp && bp[0] == '0')) {
+    // 256 x 256 tiles: the software-pipelined kernel, unless TGEMM_PIPE=0
+    // asks for the generic one.  TGEMM_PIPE_VARIANT=<index> picks a sweep
+    // variant of the same element type, output and layout.
+    const char *pp = getenv("TGEMM_PIPE");
+    if (want_bm == 256 && want_bn == 256 && !(pp && pp[0] == '0')) {
         int nb = 0;
-        const tg::TiledVariant *b = tg::bpre_variants(&nb);
-        if (const char *e = getenv("TGEMM_BPRE_VARIANT")) {
+        const tg::TiledVariant *b = tg::pipe_variants(&nb);
+        if (const char *e = getenv("TGEMM_PIPE_VARIANT")) {
             const int k = atoi(e);
-            if (k >= 0 && k < nb && b[k].elem == elem && b[k].out == out)
+            if (k >= 0 && k < nb && b[k].elem == elem && b[k].out == out && b[k].preshuffled == pre)
                 return &b[k];
         }
         for (int i = 0; i < nb; ++i)
-            if (b[i].elem == elem && b[i].out == out)
+            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre)
                 return &b[i];
     }
     for (int i = 0; i < n; ++i)

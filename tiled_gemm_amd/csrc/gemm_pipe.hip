@@ -1,9 +1,15 @@
-// Pre-shuffled-B GEMM C = A * B^T, the kernel behind GEMM_LAYOUT_BT_PRESHUFFLED
-// for large M (FlyDSL "Kernel Authoring" skill, section 6 "GEMM Pattern
-// (Preshuffle)": B pre-shuffled into MFMA operand order, A staged through
-// XOR-swizzled LDS, 64-byte K micro-steps, LDS ping-pong; section 3 "Runtime
-// Loops with Loop-Carried Values" for the prefetch-next / compute-current
-// loop).
+// Software-pipelined GEMM C = A * B^T for 256 x 256 tiles, the kernel behind
+// both layouts at large sizes (FlyDSL "Kernel Authoring" skill, section 6
+// "GEMM Pattern (Preshuffle)": B pre-shuffled into MFMA operand order, A
+// staged through XOR-swizzled LDS, 64-byte K micro-steps, LDS ping-pong;
+// section 3 "Runtime Loops with Loop-Carried Values" for the prefetch-next /
+// compute-current loop).
+//
+// B goes straight to VGPRs in both layouts.  Pre-shuffled, one wave load is
+// one contiguous 1 KiB operand block; from the plain N x K layout, lane l
+// loads the 16 bytes of row l % 16 at K chunk l / 16, i.e. 16 rows x 64
+// contiguous bytes per wave load (the companion load for chunks 4..7 covers
+// the other half of each 128-byte row segment).
 //
 // Workgroup: WAVES waves (two per SIMD at 8), 256 x 256 output tile, waves
 // side by side along N (each wave owns all 256 rows and 256 / WAVES columns,
@@ -11,7 +17,7 @@
 //
 //   A   global -> LDS by 16-byte buffer loads that write LDS directly, into a
 //       ring of NS stages (NS - 2 tiles in flight beyond the one being read).
-//   B   global -> VGPRs, one 16-byte load per lane per 1 KiB operand block,
+//   B   global -> VGPRs, two 16-byte loads per lane per 16-column block,
 //       issued at the start of the step before its use, in two register sets
 //       renamed by unrolling the loop.
 //   LDS -> VGPR: the A fragments of a step form one ordered stream; each
@@ -62,10 +68,11 @@ using ic = std::integral_constant<int, N>;
 
 // ELEM: kBf16 (2 x 16x16x32 per step) or kFp8 (1 x 16x16x128 per step).
 // PD: fragment prefetch distance in groups.
+// BPRE: B is the pre-shuffled image (true) or plain N x K (false).
 // ADMA: A goes global -> LDS by the load's own LDS write (true) or through
 // VGPRs: loaded at barrier(k), written with ds_write_b128 at barrier(k+1).
-template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD, bool ADMA>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const TiledArgs p)
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int NS, int PD, bool ADMA>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const TiledArgs p)
 {
     using Cfg = BpCfg<WGM, WGN, NS>;
     constexpr int WAVES = Cfg::WAVES;
@@ -132,21 +139,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
             *(u32x4 *)(sA + (r * WAVES + w) * 1024 + l * 16) = stA[r];
     };
 
-    // ---- B: n-block (w * FN + j) of the workgroup, k-blocks 2kt and 2kt+1.
+    // ---- B: n-block (wn * FN + j) of the workgroup.  Pre-shuffled: k-blocks
+    // 2kt and 2kt+1 (1 KiB apart); plain: chunks q and q + 4 of row
+    // 16 * nb + r16 (64 bytes apart).
+    constexpr uint32_t kBHalf = BPRE ? 1024u : 64u;
+    constexpr uint32_t kBStep = BPRE ? 2048u : (uint32_t)kTileKBytes;
     uint32_t voffB[BP_FN];
 #pragma unroll
     for (int j = 0; j < BP_FN; ++j)
-        voffB[j] = (uint32_t)(wn * BP_FN + j) * 16u * kb + (uint32_t)l * 16u;
+        voffB[j] = BPRE ? (uint32_t)(wn * BP_FN + j) * 16u * kb + (uint32_t)l * 16u
+                        : (uint32_t)((wn * BP_FN + j) * 16 + r16) * kb + (uint32_t)q * kChunkBytes;
     u32x4 bq[2][BP_FN][2];
     auto issue_b = [&](int kt, auto set_c) {
         constexpr int S = decltype(set_c)::value;
         const bool beyond = kt >= nk;
         const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
-        const uint32_t soff = (uint32_t)kt * 2048u;
+        const uint32_t soff = (uint32_t)kt * kBStep;
 #pragma unroll
         for (int j = 0; j < BP_FN; ++j) {
             bq[S][j][0] = buf_load16(rB, keep_or_oob(!beyond, voffB[j]), soff);
-            bq[S][j][1] = buf_load16(rB, keep_or_oob(!beyond & !part, voffB[j] + 1024u), soff);
+            bq[S][j][1] = buf_load16(rB, keep_or_oob(!beyond & !part, voffB[j] + kBHalf), soff);
         }
         issue_fence();
     };
@@ -296,32 +308,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_bpre_kernel(const Tile
     }
 }
 
-template <int ELEM, int OUT, int WGM, int WGN, int NS, int PD, bool ADMA>
-static hipError_t launch_bpre(const TiledArgs &a, hipStream_t s)
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int NS, int PD, bool ADMA>
+static hipError_t launch_pipe(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_bpre_kernel<ELEM, OUT, WGM, WGN, NS, PD, ADMA>), dim3(a.grid), dim3(64 * WGM * WGN),
-                       0, s, a);
+    hipLaunchKernelGGL((gemm_pipe_kernel<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA>), dim3(a.grid),
+                       dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-#define TG_BPRE(ELEM, OUT, WGM, WGN, NS, PD, ADMA)                                              \
-    TiledVariant{BP_BM, BP_BN, WGM, WGN, ELEM, OUT, true, BpCfg<WGM, WGN, NS>::LDS,              \
-                 &launch_bpre<ELEM, OUT, WGM, WGN, NS, PD, ADMA>}
+#define TG_PIPE(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA)                                        \
+    TiledVariant{BP_BM, BP_BN, WGM, WGN, ELEM, OUT, BPRE, BpCfg<WGM, WGN, NS>::LDS,              \
+                 &launch_pipe<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA>}
 
-// The first variant of each (elem, out) is the planner's choice; the rest
-// are alternatives selectable by index with TGEMM_BPRE_VARIANT (sweeps).
-static const TiledVariant kBpre[] = {
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 4, true),
-    TG_BPRE(kBf16, kOutF32, 1, 8, 4, 4, true),
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 4, false),
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 5, 4, false),
-    TG_BPRE(kBf16, kOutBf16, 1, 8, 4, 6, false),
+// The first variant of each (elem, out, layout) is the planner's choice; the
+// rest are alternatives selectable by index with TGEMM_PIPE_VARIANT (sweeps).
+static const TiledVariant kPipe[] = {
+    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),
+    TG_PIPE(kBf16, kOutF32, true, 1, 8, 4, 4, true),
+    TG_PIPE(kBf16, kOutBf16, false, 1, 8, 4, 4, true),
+    TG_PIPE(kBf16, kOutF32, false, 1, 8, 4, 4, true),
+    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),
+    TG_PIPE(kFp8, kOutBf16, true, 1, 8, 4, 3, true),
+    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, false),
 };
 
-const TiledVariant *bpre_variants(int *count)
+const TiledVariant *pipe_variants(int *count)
 {
-    *count = (int)(sizeof(kBpre) / sizeof(kBpre[0]));
-    return kBpre;
+    *count = (int)(sizeof(kPipe) / sizeof(kPipe[0]));
+    return kPipe;
 }
 
 }  // namespace tg

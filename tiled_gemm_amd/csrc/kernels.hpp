@@ -65,7 +65,7 @@ constexpr int kSkinnyTileN = 32;
 constexpr int kTiledThreads = 256;
 
 const TiledVariant *tiled_variants(int *count);
-const TiledVariant *bpre_variants(int *count);
+const TiledVariant *pipe_variants(int *count);
 const SkinnyVariant *skinny_variants(int *count);
 hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
 
