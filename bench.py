@@ -29,6 +29,9 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}     # MI355X dense peaks
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_preshuffled"
+# HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE scaled by a copy of known size (see the file for the commands).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_pipe_bf16_8192_preshuffled.txt")
 
 
 def log(*a):
@@ -123,9 +126,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--only", default=None, help="time only this workload (profiling runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a device-to-device copy of MIB MiB (3 times): the reference "
+                         "kernel whose FETCH_SIZE / WRITE_SIZE scale the GEMM's HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (--gpus %d requested); "
+        print("bench.py: the benchmark runs on one GPU only (--gpus %d requested); "
               "the sharded design is described in DESIGN.md" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -137,6 +143,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     tg.load()
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copy calibration %d MiB x 3" % args.calibrate_copy)
+        del src, dst
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
         "bf16_4096", "bf16_skinny_32x8192x8192", "e4m3_8192"])
     results = {}
@@ -161,9 +176,14 @@ def main():
     w = W.WORKLOADS[head]
     r = results[head]
     bound = "hbm" if head == "bf16_skinny_32x8192x8192" else "mfma"
+    traffic = None
+    if head == HEADLINE:
+        from profile_summary import read_traffic
+        traffic = read_traffic(TRAFFIC_FILE)
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_TFLOPS[w.dtype],
-                "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_TFLOPS[w.dtype], 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_TFLOPS[w.dtype], 4),
+                "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(r["gbs"] / PEAK_HBM_GBS, 4), "traffic": None}

@@ -14,10 +14,40 @@ from __future__ import annotations
 
 import csv
 import glob
+import hashlib
 import os
 import re
 import statistics
 import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Sources that define the timed GEMM kernel; a traffic figure is valid only
+# for the exact sources it was measured on.
+KERNEL_SOURCES = ["tiled_gemm_amd/csrc/gemm_pipe.hip", "tiled_gemm_amd/csrc/device.hpp",
+                  "tiled_gemm_amd/csrc/layout.hpp", "tiled_gemm_amd/csrc/kernels.hpp"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str):
+    """TRAFFIC_BYTES from a committed summary, or None if the kernel sources
+    changed since it was measured."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] in ("TRAFFIC_BYTES", "SOURCE_SHA"):
+            vals[parts[0]] = parts[1]
+    if vals.get("SOURCE_SHA") != kernel_source_sha() or "TRAFFIC_BYTES" not in vals:
+        return None
+    return float(vals["TRAFFIC_BYTES"])
 
 
 def _one(pattern: str) -> str:
@@ -71,6 +101,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel_re: str, copy_mib: int = 512)
     print("HBM bytes per launch (scaled): read %.0f + write %.0f = %.0f" % (
         mf * sf * 1024, mw * sw * 1024, hbm))
     print("TRAFFIC_BYTES %.0f" % hbm)
+    print("SOURCE_SHA %s" % kernel_source_sha())
 
 
 if __name__ == "__main__":
