@@ -97,6 +97,11 @@ const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
     const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
     int n = 0;
     const tg::SkinnyVariant *v = tg::skinny_variants(&n);
+    if (const char *e = getenv("TGEMM_SKINNY_VARIANT")) {
+        const int k = atoi(e);
+        if (k >= 0 && k < n && v[k].mblocks == mb && v[k].elem == elem_of(I.dtype) && v[k].out == out_of(I.dtype))
+            return &v[k];
+    }
     for (int i = 0; i < n; ++i)
         if (v[i].mblocks == mb && v[i].elem == elem_of(I.dtype) && v[i].out == out_of(I.dtype))
             return &v[i];
@@ -245,13 +250,13 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         I.kernel = 1;
         I.tile_m = p->skinny->mblocks * 16;
         I.tile_n = tg::kSkinnyTileN;
-        I.threads = tg::kSkinnyThreads;
-        I.lds_stages = 0;
+        I.threads = 64 * p->skinny->waves;
+        I.lds_stages = p->skinny->stages;
         I.lds_bytes = p->skinny->lds_bytes;
         I.tiles_m = 1;
         I.tiles_n = (int32_t)(N / tg::kSkinnyTileN + (N % tg::kSkinnyTileN ? 1 : 0));
         I.group_m = 1;
-        I.split_k = tg::kSkinnyThreads / 64;
+        I.split_k = p->skinny->waves;
         I.grid = I.tiles_n;
     } else if ((p->tiled = pick_tiled(I)) != nullptr) {
         I.kernel = 0;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "layout.hpp"
 
 namespace tg {
@@ -116,6 +118,9 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
     __bf16 b = (__bf16)hi;
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
+
+template <int N>
+using ic_t = std::integral_constant<int, N>;
 
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ inline int lane_id() { return threadIdx.x & 63; }

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                     barrier();
                     issue_a(kt + NS - 1);
                 } else {
-                    __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00 | (kLgkmBarrier << 8));
+                    __builtin_amdgcn_s_waitcnt((0xC07F & ~0x0F00) | (kLgkmBarrier << 8));
                     barrier();
                     store_a();                       // tile kt+NS-2, loaded at barrier(kt-1)
                     __builtin_amdgcn_sched_barrier(0);

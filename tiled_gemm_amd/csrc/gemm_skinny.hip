@@ -1,29 +1,55 @@
 // Skinny GEMM (M <= 64): C = A * B^T when B is the only large operand and
 // the product is bound by streaming B from HBM once.
 //
-// One workgroup of 8 waves owns 32 columns of C (two 16-column MFMA blocks)
-// and every row.  The K range is split among the waves by interleaving
-// 128-byte steps (wave w takes steps w, w+8, ...), so at any moment the
-// workgroup streams one contiguous 1 KiB span of each of its 32 B rows.
-// Operands go straight from global memory into VGPRs with 16-byte buffer
-// loads, several steps ahead; the MFMA operand layout is the same as in the
-// tiled kernel (lane l: row l % 16, K chunks l / 16 and 4 + l / 16).  The
-// eight partial 16x16 tiles per output block are summed through LDS in a
-// fixed wave order (deterministic), then scaled, converted and stored.
+// One workgroup owns 32 columns of C (two 16-column MFMA blocks) and every
+// row.  Its WAVES waves split K: wave w takes a contiguous run of 128-byte K
+// steps, and with ROTATE each workgroup starts its sweep at a different step
+// (wrapping), so the concurrent loads of all workgroups spread over the rows
+// instead of hitting one K offset of rows 16 KiB apart.
+//
+// For this shape the per-CU vector-memory path, not HBM, sets the pace when
+// loads cover half cache lines, so every load here covers whole 128-byte
+// lines: one wave load brings 8 rows x 128 bytes straight into LDS (the
+// load's own LDS write, lane l writing bytes 16 l .. 16 l + 15 of the wave's
+// 1 KiB destination), each lane choosing its source chunk so that the LDS
+// image is XOR-swizzled (chunk c of row r sits at c ^ ((r >> 1) & 7), as in
+// the tiled kernels); the MFMA fragments are then read with conflict-free
+// 16-byte LDS reads.  Each wave owns a ring of DEPTH stages, so the loop needs
+// no workgroup barrier: wait until the oldest stage has landed (vmcnt), read
+// its fragments, run the MFMAs, then refill that stage with the step DEPTH
+// ahead.  Steps past the wave's run read out of range, i.e. zeros, which keeps
+// the number of loads in flight constant.
+//
+// The partial tiles of the waves are summed through LDS in a fixed wave order
+// (deterministic), then scaled, converted and stored.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace tg {
 
-constexpr int kSkinnyWaves = kSkinnyThreads / 64;
-constexpr int kSkinnyDepth = 4;        // K steps loaded before the first is consumed
+constexpr int kRedPitch = kSkinnyTileN + 1;   // padded reduction row (bank spread)
 
-template <int MB, int ELEM, int OUT>
-__global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_kernel(const SkinnyArgs p)
+template <int MB, int WAVES, int DEPTH>
+struct SkinnyCfg {
+    static constexpr int ROWS_A = MB * 16;
+    static constexpr int ROWS = ROWS_A + kSkinnyTileN;      // stage rows: A rows, then B rows
+    static constexpr int STAGE = ROWS * kTileKBytes;        // bytes per stage
+    static constexpr int RING = DEPTH * STAGE;              // bytes per wave
+    static constexpr int LOADS = ROWS / 8;                  // 1 KiB wave loads per stage
+    static constexpr int RED = WAVES * ROWS_A * kRedPitch * 4;
+    static constexpr int LDS = WAVES * RING > RED ? WAVES * RING : RED;
+    static_assert(ROWS_A % 8 == 0, "a wave load must not mix A and B rows");
+    static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+    static_assert((DEPTH - 1) * LOADS < 64, "vmcnt holds 6 bits");
+};
+
+template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool ROTATE>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_kernel(const SkinnyArgs p)
 {
-    constexpr int NB = kSkinnyTileN / 16;           // column blocks per workgroup
-    constexpr int ROWS = MB * 16;
-    __shared__ __attribute__((aligned(16))) float red[kSkinnyWaves][ROWS][kSkinnyTileN];
+    using Cfg = SkinnyCfg<MB, WAVES, DEPTH>;
+    constexpr int NB = kSkinnyTileN / 16;
+    constexpr int L = Cfg::LOADS;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
 
     const int w = wave_id();
     const int l = lane_id();
@@ -34,33 +60,43 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_kernel(const Sk
     const auto rA = make_rsrc(p.A, (uint32_t)p.M * kb);
     const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
     const int nk = p.k_tiles;
-    const bool ragged = p.tail_bytes != kTileKBytes;
+    const uint32_t tail = (uint32_t)p.tail_bytes;
+    uint8_t *const ring = lds + w * Cfg::RING;
 
-    uint32_t voffA[MB], voffB[NB];
+    // Wave load j of a stage covers stage rows 8j .. 8j + 7; lane l takes row
+    // 8j + l / 8 and the logical chunk that the swizzle puts in slot l % 8.
+    // Rows past M or N lie past their buffer's record count (zeros).
+    uint32_t voff[L];
+    uint32_t half_keep = 0;     // bit j: this lane's chunk lies in the first 64 bytes
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-        voffA[i] = (uint32_t)(i * 16 + r16) * kb + (uint32_t)q * kChunkBytes;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-        voffB[j] = (uint32_t)(j * 16 + r16) * kb + (uint32_t)q * kChunkBytes;
+    for (int j = 0; j < L; ++j) {
+        const int row = 8 * j + (l >> 3);
+        const int c = swz_chunk(row, l & 7);
+        const int src_row = row < Cfg::ROWS_A ? row : row - Cfg::ROWS_A;
+        voff[j] = (uint32_t)src_row * kb + (uint32_t)c * kChunkBytes;
+        half_keep |= (c < kChunksPerRow / 2 ? 1u : 0u) << j;
+    }
 
-    struct Step {
-        u32x4 a[MB][2];
-        u32x4 b[NB][2];
-    };
-    auto load = [&](int kt, Step &st) {
-        const uint32_t soff = (uint32_t)kt * kTileKBytes;
-        const bool part = ragged && kt == nk - 1;     // second 64 bytes absent
+    const int per = (nk + WAVES - 1) / WAVES;
+    const int first = w * per;
+    const int nt = max(0, min(per, nk - first));         // this wave's steps
+    const int rot = ROTATE ? (int)((blockIdx.x * 37u) % (uint32_t)max(nk, 1)) : 0;
+
+    // Step t of this wave into ring stage s (every load is issued; the ones
+    // past the run or past K in a half-filled last step are out of range).
+    auto issue = [&](int t, int s) {
+        int kt = first + t + rot;
+        kt = kt >= nk ? kt - nk : kt;
+        const bool in = t < nt;
+        const bool part = (kt == nk - 1) & (tail != (uint32_t)kTileKBytes);
+        const uint32_t soff = in ? (uint32_t)kt * kTileKBytes : 0u;
+        uint8_t *const dst = ring + s * Cfg::STAGE;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            st.b[j][0] = buf_load16(rB, voffB[j], soff);
-            st.b[j][1] = part ? u32x4{0, 0, 0, 0} : buf_load16(rB, voffB[j] + 64u, soff);
+        for (int j = 0; j < L; ++j) {
+            const bool keep = in & (!part | (((half_keep >> j) & 1u) != 0));
+            buf_load16_to_lds(8 * j < Cfg::ROWS_A ? rA : rB, dst + j * 1024, keep_or_oob(keep, voff[j]), soff);
         }
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            st.a[i][0] = buf_load16(rA, voffA[i], soff);
-            st.a[i][1] = part ? u32x4{0, 0, 0, 0} : buf_load16(rA, voffA[i] + 64u, soff);
-        }
+        issue_fence();
     };
 
     f32x4 acc[MB][NB];
@@ -70,39 +106,60 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_kernel(const Sk
         for (int j = 0; j < NB; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Step &st) {
+    // MFMA operands of one stage: lane l takes row l % 16 of each 16-row
+    // block and the logical chunks l / 16 and 4 + l / 16 (the tiled kernels'
+    // lane/K assignment).
+    auto compute = [&](int s) {
+        const uint8_t *const st = ring + s * Cfg::STAGE;
+        auto frag = [&](int row, int c) {
+            return lds_load16(st + row * kTileKBytes + swz_chunk(row, c) * kChunkBytes);
+        };
+        u32x4 a[MB][2], b[NB][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                b[j][h] = frag(Cfg::ROWS_A + j * 16 + r16, h * 4 + q);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                a[i][h] = frag(i * 16 + r16, h * 4 + q);
+        }
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 if constexpr (ELEM == kBf16) {
-                    acc[i][j] = mfma_bf16(st.b[j][0], st.a[i][0], acc[i][j]);
-                    acc[i][j] = mfma_bf16(st.b[j][1], st.a[i][1], acc[i][j]);
+                    acc[i][j] = mfma_bf16(b[j][0], a[i][0], acc[i][j]);
+                    acc[i][j] = mfma_bf16(b[j][1], a[i][1], acc[i][j]);
                 } else {
-                    acc[i][j] = mfma_fp8(st.b[j][0], st.b[j][1], st.a[i][0], st.a[i][1], acc[i][j]);
+                    acc[i][j] = mfma_fp8x8(join32(b[j][0], b[j][1]), join32(a[i][0], a[i][1]), acc[i][j]);
                 }
             }
     };
 
-    // Steps of this wave: w, w + 8, w + 16, ...  Process them in groups of
-    // kSkinnyDepth: all loads of a group are issued before its MFMAs.
-    Step st[kSkinnyDepth];
-    for (int base = w; base < nk; base += kSkinnyDepth * kSkinnyWaves) {
+    // Waiting for the oldest stage leaves the DEPTH - 1 younger ones in flight.
+    constexpr int kVm = (DEPTH - 1) * L;
+    constexpr int kWaitOldest = (kWaitVmcnt0 & ~0xC00F) | (kVm & 0xF) | ((kVm >> 4) << 14);
+    constexpr int kWaitLds = 0xC07F;                 // lgkmcnt(0) only
 #pragma unroll
-        for (int d = 0; d < kSkinnyDepth; ++d) {
-            const int kt = base + d * kSkinnyWaves;
-            if (kt < nk)
-                load(kt, st[d]);
-        }
-#pragma unroll
-        for (int d = 0; d < kSkinnyDepth; ++d) {
-            const int kt = base + d * kSkinnyWaves;
-            if (kt < nk)
-                compute(st[d]);
-        }
+    for (int s = 0; s < DEPTH; ++s)
+        issue(s, s);
+    int s = 0;
+    for (int t = 0; t < nt; ++t) {
+        __builtin_amdgcn_s_waitcnt(kWaitOldest);
+        compute(s);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);         // the stage's reads are done before its refill
+        issue(t + DEPTH, s);
+        s = s + 1 == DEPTH ? 0 : s + 1;
     }
+    // Out-of-range loads still write (zeros) into LDS: drain them before the
+    // ring is reused for the reduction.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);
+    __syncthreads();
 
     // ---- cross-wave reduction in a fixed order, then the epilogue.
+    using RedRows = float[Cfg::ROWS_A][kRedPitch];
+    RedRows *red = reinterpret_cast<RedRows *>(lds);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -121,41 +178,50 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_kernel(const Sk
     const uint32_t ldc = (uint32_t)p.N * OB;
     const auto rC = make_rsrc(p.C, (uint32_t)p.M * ldc);
     // Each thread finishes pairs of adjacent outputs.
-    for (int o = threadIdx.x * 2; o < ROWS * kSkinnyTileN; o += kSkinnyThreads * 2) {
+    for (int o = threadIdx.x * 2; o < Cfg::ROWS_A * kSkinnyTileN; o += 64 * WAVES * 2) {
         const int row = o / kSkinnyTileN, col = o % kSkinnyTileN;
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kSkinnyWaves; ++ww) {
+        for (int ww = 0; ww < WAVES; ++ww) {
             s0 += red[ww][row][col];
             s1 += red[ww][row][col + 1];
         }
         s0 = (s0 * sa) * sb;
         s1 = (s1 * sa) * sb;
         const int n = n0 + col;
-        const uint32_t voff = (row < p.M && n < p.N) ? (uint32_t)row * ldc + (uint32_t)n * OB : kOobOffset;
+        const uint32_t voffc = (row < p.M && n < p.N) ? (uint32_t)row * ldc + (uint32_t)n * OB : kOobOffset;
         if constexpr (OUT == kOutF32)
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, s0),
                                                         __builtin_bit_cast(uint32_t, s1)},
-                                                  rC, voff, 0, 0);
+                                                  rC, voffc, 0, 0);
         else
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(s0, s1), rC, voff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(s0, s1), rC, voffc, 0, 0);
     }
 }
 
-template <int MB, int ELEM, int OUT>
+template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool ROTATE>
 static hipError_t launch_skinny(const SkinnyArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ELEM, OUT>), dim3(grid), dim3(kSkinnyThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ELEM, OUT, WAVES, DEPTH, ROTATE>), dim3(grid), dim3(64 * WAVES), 0,
+                       s, a);
     return hipGetLastError();
 }
 
-#define TG_SKINNY(MB, ELEM, OUT) \
-    SkinnyVariant{MB, ELEM, OUT, kSkinnyWaves * MB * 16 * kSkinnyTileN * 4, &launch_skinny<MB, ELEM, OUT>}
+#define TG_SKINNY(MB, ELEM, OUT, WAVES, DEPTH, ROTATE)                                                       \
+    SkinnyVariant{MB, ELEM, OUT, WAVES, DEPTH, SkinnyCfg<MB, WAVES, DEPTH>::LDS,                             \
+                  &launch_skinny<MB, ELEM, OUT, WAVES, DEPTH, ROTATE>}
 
+// The first variant of each (rows, elem, out) is the planner's choice; the
+// rest are alternatives selectable by index with TGEMM_SKINNY_VARIANT.
 static const SkinnyVariant kSkinny[] = {
-    TG_SKINNY(1, kBf16, kOutBf16), TG_SKINNY(2, kBf16, kOutBf16), TG_SKINNY(4, kBf16, kOutBf16),
-    TG_SKINNY(1, kBf16, kOutF32),  TG_SKINNY(2, kBf16, kOutF32),  TG_SKINNY(4, kBf16, kOutF32),
-    TG_SKINNY(1, kFp8, kOutBf16),  TG_SKINNY(2, kFp8, kOutBf16),  TG_SKINNY(4, kFp8, kOutBf16),
+    TG_SKINNY(1, kBf16, kOutBf16, 8, 3, true), TG_SKINNY(2, kBf16, kOutBf16, 8, 2, true),
+    TG_SKINNY(4, kBf16, kOutBf16, 4, 3, true), TG_SKINNY(1, kBf16, kOutF32, 8, 3, true),
+    TG_SKINNY(2, kBf16, kOutF32, 8, 2, true),  TG_SKINNY(4, kBf16, kOutF32, 4, 3, true),
+    TG_SKINNY(1, kFp8, kOutBf16, 8, 3, true),  TG_SKINNY(2, kFp8, kOutBf16, 8, 2, true),
+    TG_SKINNY(4, kFp8, kOutBf16, 4, 3, true),
+    // alternatives for the 32-row bf16 shape
+    TG_SKINNY(2, kBf16, kOutBf16, 8, 2, false), TG_SKINNY(2, kBf16, kOutBf16, 4, 4, true),
+    TG_SKINNY(2, kBf16, kOutBf16, 2, 8, true),
 };
 
 const SkinnyVariant *skinny_variants(int *count)

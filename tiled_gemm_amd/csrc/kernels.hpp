@@ -56,11 +56,12 @@ struct TiledVariant {
 struct SkinnyVariant {
     int mblocks;            // 16-row blocks of M covered (M <= 16 * mblocks)
     int elem, out;
+    int waves;              // waves per workgroup, each taking a slice of K
+    int stages;             // LDS stages per wave
     int lds_bytes;
     hipError_t (*launch)(const SkinnyArgs &, int grid, hipStream_t);
 };
 
-constexpr int kSkinnyThreads = 512;
 constexpr int kSkinnyTileN = 32;
 constexpr int kTiledThreads = 256;
 
