@@ -19,7 +19,8 @@ from gpu_util import assert_within_bound, decode, run_gemm, sample_entries
 pytestmark = pytest.mark.gpu
 
 # (dtype, out, layout, tile) -- tile None = the planner's own choice; "256x256"
-# is the software-pipelined kernel, "256x256g" the generic tiled kernel.
+# is the software-pipelined kernel, "256x256g" the generic tiled kernel,
+# "256x256q" the 4-wave pipelined kernel.
 PATHS = [
     ("bf16", "f32", "bt", "128x128"), ("bf16", "f32", "bt", "256x256"), ("bf16", "f32", "bt", "256x256g"),
     ("bf16", "bf16", "bt", "128x128"), ("bf16", "bf16", "bt", "256x256"), ("bf16", "bf16", "bt", "256x256g"),
@@ -28,6 +29,9 @@ PATHS = [
     ("e4m3", "bf16", "bt", "128x128"), ("e4m3", "bf16", "bt", "256x256"), ("e4m3", "bf16", "bt", "256x256g"),
     ("e4m3", "bf16", "bt_preshuffled", "128x128"), ("e4m3", "bf16", "bt_preshuffled", "256x256"),
     ("e4m3", "bf16", "bt_preshuffled", "256x256g"),
+    ("bf16", "f32", "bt", "256x256q"), ("bf16", "bf16", "bt", "256x256q"),
+    ("bf16", "bf16", "bt_preshuffled", "256x256q"), ("bf16", "f32", "bt_preshuffled", "256x256q"),
+    ("e4m3", "bf16", "bt", "256x256q"), ("e4m3", "bf16", "bt_preshuffled", "256x256q"),
 ]
 
 
@@ -47,6 +51,10 @@ def _gpu():
 def tile_env(monkeypatch):
     def set_tile(t):
         monkeypatch.delenv("TGEMM_PIPE", raising=False)
+        monkeypatch.delenv("TGEMM_PIPE_WAVES", raising=False)
+        if t and t.endswith("q"):
+            monkeypatch.setenv("TGEMM_PIPE_WAVES", "4")
+            t = t[:-1]
         if t and t.endswith("g"):
             monkeypatch.setenv("TGEMM_PIPE", "0")
             t = t[:-1]
@@ -138,11 +146,14 @@ def test_random_within_bound(oracle_mod, tile_env, dtype, out, layout, tile):
 
 # ------------------------------------------------------------------ full-size workloads, sampled
 
-@pytest.mark.parametrize("name", ["bf16_4096", "bf16_8192_preshuffled", "bf16_skinny_32x8192x8192", "e4m3_8192"])
-def test_full_size_sampled(oracle_mod, tile_env, name):
-    tile_env(None)
+@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_8192_preshuffled", None),
+                                       ("bf16_skinny_32x8192x8192", None), ("e4m3_8192", None),
+                                       ("bf16_8192_preshuffled", "256x256q"), ("e4m3_8192", "256x256q"),
+                                       ("bf16_4096", "256x256q")])
+def test_full_size_sampled(oracle_mod, tile_env, name, tile):
+    tile_env(tile)
     w = W.WORKLOADS[name]
-    say("case full-size", name)
+    say("case full-size", name, tile)
     inp = W.make_inputs(w)
     C_bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout,
                             scale=(inp.scale_a, inp.scale_b), return_plan_info=True)

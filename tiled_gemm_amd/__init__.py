@@ -189,9 +189,11 @@ class Plan:
         self.handle = gemm_plan_create(M, N, K, dtype, layout)
 
     def close(self):
-        if self.handle:
-            gemm_plan_destroy(self.handle)
-            self.handle = 0
+        h, self.handle = self.handle, 0
+        # At interpreter exit the module's globals may already be cleared.
+        destroy = globals().get("gemm_plan_destroy")
+        if h and destroy is not None:
+            destroy(h)
 
     __del__ = close
 

@@ -79,8 +79,12 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
             if (k >= 0 && k < nb && b[k].elem == elem && b[k].out == out && b[k].preshuffled == pre)
                 return &b[k];
         }
+        // TGEMM_PIPE_WAVES=<n> restricts the choice to n-wave variants.
+        const char *ew = getenv("TGEMM_PIPE_WAVES");
+        const int waves = ew ? atoi(ew) : 0;
         for (int i = 0; i < nb; ++i)
-            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre)
+            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre &&
+                (waves == 0 || b[i].wgm * b[i].wgn == waves))
                 return &b[i];
     }
     for (int i = 0; i < n; ++i)
@@ -264,8 +268,7 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         I.tile_n = p->tiled->bn;
         I.threads = 64 * p->tiled->wgm * p->tiled->wgn;
         I.lds_bytes = p->tiled->lds_bytes;
-        I.lds_stages = I.lds_bytes / (I.tile_m * tg::kTileKBytes +
-                                      (p->tiled->preshuffled ? 0 : I.tile_n * tg::kTileKBytes));
+        I.lds_stages = p->tiled->lds_stages;
         I.tiles_m = (int32_t)((M + I.tile_m - 1) / I.tile_m);
         I.tiles_n = (int32_t)((N + I.tile_n - 1) / I.tile_n);
         I.group_m = I.tile_m >= 256 ? 4 : 8;

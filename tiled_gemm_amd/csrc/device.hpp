@@ -111,6 +111,28 @@ __device__ inline f32x4 mfma_fp8(u32x4 x_lo, u32x4 x_hi, u32x4 y_lo, u32x4 y_hi,
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc, 0, 0, 0, 127, 0, 127);
 }
 
+// The same two atoms with the accumulator pinned to AGPRs (inline assembly,
+// "+a"), for kernels whose accumulators fill the AGPR file (256 per lane): the
+// compiler then keeps every accumulator in place across the main loop instead
+// of copying between register files.  It does not know these are MFMAs, so
+// code that reads the accumulators with other instructions must first call
+// mfma_drain(); dependent MFMAs on one accumulator must be far apart (the
+// kernels using these issue at least 32 other MFMAs in between).
+// v_mfma_f32_16x16x128_f8f6f4 with its default format fields is e4m3 x e4m3,
+// the unscaled form of mfma_fp8x8 above.
+__device__ inline void mfma_bf16_a(f32x4 &acc, u32x4 x, u32x4 y)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+}
+
+__device__ inline void mfma_fp8x8_a(f32x4 &acc, i32x8 x, i32x8 y)
+{
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+}
+
+// 64 wait states: longer than any MFMA's result latency.
+__device__ inline void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }
+
 // Two fp32 -> two bf16 (round to nearest even), packed low-first.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {

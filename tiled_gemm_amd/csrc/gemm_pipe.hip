@@ -71,7 +71,7 @@ using ic = std::integral_constant<int, N>;
 // BPRE: B is the pre-shuffled image (true) or plain N x K (false).
 // ADMA: A goes global -> LDS by the load's own LDS write (true) or through
 // VGPRs: loaded at barrier(k), written with ds_write_b128 at barrier(k+1).
-template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int NS, int PD, bool ADMA>
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int NS, int PD, bool ADMA, bool ACCA, bool SPREAD>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const TiledArgs p)
 {
     using Cfg = BpCfg<WGM, WGN, NS>;
@@ -113,6 +113,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     }
     u32x4 stA[BP_AR];                           // staging (ADMA == false)
     int stA_tile = 0;
+    // One A load (round r of tile kt), for the spread schedule below.
+    auto issue_a_one = [&](int kt, int r) {
+        const bool beyond = kt >= nk;
+        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+        const bool keep = !beyond & (!part | (((tailA >> r) & 1u) != 0));
+        buf_load16_to_lds(rA, lds + (kt % NS) * BP_STAGE + (r * WAVES + w) * 1024, keep_or_oob(keep, voffA[r]),
+                          (uint32_t)kt * kTileKBytes);
+        issue_fence();
+    };
     auto issue_a = [&](int kt) {
         const bool beyond = kt >= nk;
         const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
@@ -150,6 +159,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         voffB[j] = BPRE ? (uint32_t)(wn * BP_FN + j) * 16u * kb + (uint32_t)l * 16u
                         : (uint32_t)((wn * BP_FN + j) * 16 + r16) * kb + (uint32_t)q * kChunkBytes;
     u32x4 bq[2][BP_FN][2];
+    auto issue_b_one = [&](int kt, auto set_c, int j, int h) {
+        constexpr int S = decltype(set_c)::value;
+        const bool beyond = kt >= nk;
+        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+        const bool keep = !beyond & ((h == 0) | !part);
+        bq[S][j][h] = buf_load16(rB, keep_or_oob(keep, voffB[j] + (uint32_t)h * kBHalf), (uint32_t)kt * kBStep);
+        issue_fence();
+    };
     auto issue_b = [&](int kt, auto set_c) {
         constexpr int S = decltype(set_c)::value;
         const bool beyond = kt >= nk;
@@ -192,8 +209,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         const int i = g % BP_FM;
 #pragma unroll
         for (int j = 0; j < BP_FN; ++j) {
-            if constexpr (ELEM == kBf16)
+            if constexpr (ELEM == kBf16 && ACCA)
+                mfma_bf16_a(acc[i][j], bq[S][j][g / BP_FM], fa[g]);
+            else if constexpr (ELEM == kBf16)
                 acc[i][j] = mfma_bf16(bq[S][j][g / BP_FM], fa[g], acc[i][j]);
+            else if constexpr (ACCA)
+                mfma_fp8x8_a(acc[i][j], join32(bq[S][j][0], bq[S][j][1]), fa[g]);
             else
                 acc[i][j] = mfma_fp8x8(join32(bq[S][j][0], bq[S][j][1]), fa[g], acc[i][j]);
         }
@@ -229,10 +250,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         const int st = kt % NS;
         wait_vm(ic<kVmStart>{});
         __builtin_amdgcn_sched_barrier(0);
-        issue_b(kt + 1, ic<1 - CUR>{});
+        if constexpr (!(SPREAD && ADMA))
+            issue_b(kt + 1, ic<1 - CUR>{});
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            if (g == NG - PD) {
+            if constexpr (SPREAD && ADMA) {
+                // B(kt+1) spread over the groups before the barrier, A(kt+NS-1)
+                // over the groups after it: the same issue order across the
+                // barrier (so the same vmcnt counts), without bursts that
+                // stall the wave at issue while the memory pipeline drains.
+                if (g < NG - PD) {
+#pragma unroll
+                    for (int b = g * BP_BR / (NG - PD); b < (g + 1) * BP_BR / (NG - PD); ++b)
+                        issue_b_one(kt + 1, ic<1 - CUR>{}, b >> 1, b & 1);
+                } else {
+                    const int go = g - (NG - PD);
+                    if (go == 0) {
+                        wait_vm(ic<kVmBarrier>{});
+                        barrier();
+                    }
+#pragma unroll
+                    for (int r = go * BP_AR / PD; r < (go + 1) * BP_AR / PD; ++r)
+                        issue_a_one(kt + NS - 1, r);
+                }
+            } else if (g == NG - PD) {
                 if constexpr (ADMA) {
                     wait_vm(ic<kVmBarrier>{});
                     barrier();
@@ -281,6 +322,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         step(kt + 1, ic<1>{});
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if constexpr (ACCA)
+        mfma_drain();
 
     // ---- epilogue
     float sa = 1.f, sb = 1.f;
@@ -308,28 +351,43 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     }
 }
 
-template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int NS, int PD, bool ADMA>
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int NS, int PD, bool ADMA, bool ACCA, bool SPREAD>
 static hipError_t launch_pipe(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_pipe_kernel<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA>), dim3(a.grid),
+    hipLaunchKernelGGL((gemm_pipe_kernel<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA, ACCA, SPREAD>), dim3(a.grid),
                        dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-#define TG_PIPE(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA)                                        \
-    TiledVariant{BP_BM, BP_BN, WGM, WGN, ELEM, OUT, BPRE, BpCfg<WGM, WGN, NS>::LDS,              \
-                 &launch_pipe<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA>}
+#define TG_PIPE_S(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA, SPREAD)                              \
+    TiledVariant{BP_BM, BP_BN, WGM, WGN, ELEM, OUT, BPRE, BpCfg<WGM, WGN, NS>::LDS, NS,          \
+                 &launch_pipe<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA, (WGM * WGN == 4), SPREAD>}
+#define TG_PIPE(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA) TG_PIPE_S(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA, false)
 
 // The first variant of each (elem, out, layout) is the planner's choice; the
 // rest are alternatives selectable by index with TGEMM_PIPE_VARIANT (sweeps).
 static const TiledVariant kPipe[] = {
-    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),
-    TG_PIPE(kBf16, kOutF32, true, 1, 8, 4, 4, true),
-    TG_PIPE(kBf16, kOutBf16, false, 1, 8, 4, 4, true),
-    TG_PIPE(kBf16, kOutF32, false, 1, 8, 4, 4, true),
-    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),
-    TG_PIPE(kFp8, kOutBf16, true, 1, 8, 4, 3, true),
-    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, false),
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kBf16, kOutF32, true, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kBf16, kOutBf16, false, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kBf16, kOutF32, false, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 3, true, true),
+    TG_PIPE_S(kFp8, kOutBf16, true, 1, 8, 4, 3, true, true),
+    // 4 waves, one per SIMD, 256 accumulators each in AGPRs
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kBf16, kOutBf16, false, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kBf16, kOutF32, true, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kBf16, kOutF32, false, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 4, 4, 6, true, true),
+    TG_PIPE_S(kFp8, kOutBf16, true, 1, 4, 4, 6, true, true),
+    // sweep alternatives
+    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),           // 12: loads in bursts
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 5, true, true),   // 13
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 7, true, true),   // 14
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 5, 6, true, true),   // 15
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 16
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 17
+    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 18: loads in bursts
 };
 
 const TiledVariant *pipe_variants(int *count)

@@ -261,7 +261,7 @@ static hipError_t launch_tiled(const TiledArgs &a, hipStream_t s)
 
 #define TG_TILED(BM, BN, WGM, WGN, ELEM, BPRE, OUT)                                        \
     TiledVariant{BM, BN, WGM, WGN, ELEM, OUT, BPRE,                                         \
-                 TiledCfg<BM, BN, WGM, WGN, ELEM, BPRE, OUT>::LDS,                          \
+                 TiledCfg<BM, BN, WGM, WGN, ELEM, BPRE, OUT>::LDS, 2,                       \
                  &launch_tiled<BM, BN, WGM, WGN, ELEM, BPRE, OUT>}
 
 static const TiledVariant kTiled[] = {

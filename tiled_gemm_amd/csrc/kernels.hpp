@@ -50,6 +50,7 @@ struct TiledVariant {
     int elem, out;
     bool preshuffled;
     int lds_bytes;
+    int lds_stages;         // K steps the LDS ring holds
     hipError_t (*launch)(const TiledArgs &, hipStream_t);
 };
 
