@@ -8,6 +8,8 @@ Contents
 --------
 * ``gemm_bt`` / ``gemm_bt_entries`` -- the fp64 triple loop in ``oracle.c``
   (plain i-j-k, sequential k, sigma = s_a * s_b for fp8), built with gcc.
+* ``epilogue`` -- the fused epilogue (scale vectors, bias, ReLU / SiLU /
+  GELU) applied in fp64 to the exact GEMM result.
 * ``round_bf16`` -- the oracle's own round-to-nearest-even to bf16.
 * ``bf16_value`` / ``e4m3fn_value`` -- element decoders from the format
   definitions.
@@ -153,3 +155,69 @@ def e4m3fn_value(bits: int) -> float:
 
 
 from . import layout  # noqa: E402,F401  (brute-force layout algebra)
+
+
+# ------------------------------------------------------------------ epilogue
+
+ACTIVATIONS = ("none", "bias", "bias_relu", "bias_silu", "bias_gelu")
+
+
+def _logistic(z: np.ndarray) -> np.ndarray:
+    """1 / (1 + e^-z), evaluated without overflow on either side."""
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def _std_normal_cdf(z: np.ndarray) -> np.ndarray:
+    """Phi(z) = (1 + erf(z / sqrt 2)) / 2, with math.erf per element (fp64)."""
+    import math
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def epilogue(acc: np.ndarray, scale_a=None, scale_b=None, bias=None, kind: str = "none") -> np.ndarray:
+    """The fused epilogue on an exact GEMM result ``acc`` (M x N, fp64).
+
+    FlyDSL "Kernel authoring guide", section 11 "Complete example: Preshuffle
+    GEMM": the GEMM takes scale_a, scale_b and bias tensors and an epilogue of
+    none / bias / bias_relu / bias_silu / bias_gelu; FlyDSL "Kernel Authoring"
+    skill, section 3, applies the scales as (acc * scale_a) * scale_b.  The
+    reading taken where the pages stop (shapes and activation formulas):
+
+        z = (acc * sa[m]) * sb[n] + bias[n]
+        relu: z if z > 0 else +0;   silu: z * logistic(z);
+        gelu: z * Phi(z)  (the definition, not the tanh approximation)
+
+    ``scale_a``: None, a scalar, or M values (per row); ``scale_b``: None, a
+    scalar, or N values (per column); ``bias``: N values, used by every kind
+    except "none".  Everything is fp64; no rounding to the output type.
+    """
+    if kind not in ACTIVATIONS:
+        raise ValueError("unknown epilogue %r" % kind)
+    z = np.array(acc, dtype=np.float64, copy=True)
+    if scale_a is not None:
+        sa = np.asarray(scale_a, dtype=np.float64)
+        z = z * (sa.reshape(-1, 1) if sa.ndim else sa)
+    if scale_b is not None:
+        sb = np.asarray(scale_b, dtype=np.float64)
+        z = z * (sb.reshape(1, -1) if sb.ndim else sb)
+    if kind == "none":
+        return z
+    z = z + np.asarray(bias, dtype=np.float64).reshape(1, -1)
+    if kind == "bias_relu":
+        return np.where(z > 0, z, 0.0)
+    if kind == "bias_silu":
+        return z * _logistic(z)
+    if kind == "bias_gelu":
+        return z * _std_normal_cdf(z)
+    return z
+
+
+# Largest slope of each activation (max over z of |d act / dz|), used by the
+# tests to carry the GEMM's error bound through the activation: 1 for the
+# identity and ReLU; SiLU peaks at 1.0998 (z ~ 2.40), GELU at 1.1290 (z ~ 1.41).
+ACT_LIPSCHITZ = {"none": 1.0, "bias": 1.0, "bias_relu": 1.0, "bias_silu": 1.1, "bias_gelu": 1.13}

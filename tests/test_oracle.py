@@ -234,3 +234,88 @@ def test_preshuffle_rejects_bad_shapes():
         L.preshuffle_b_bytes(np.zeros((24, 64), np.uint16))
     with pytest.raises(ValueError):
         L.preshuffle_b_bytes(np.zeros((32, 40), np.uint8))
+
+
+# ---------------------------------------------------------------- epilogue
+# Pins of oracle.epilogue: identities of the activations that do not restate
+# their formulas, values of the standard normal CDF and of e from tables and
+# math constants, and linearity against pre-scaled GEMM inputs.
+
+# Phi(z) to 16 digits, from a standard normal table.
+PHI = {1.0: 0.8413447460685429, 2.0: 0.9772498680518208, -1.0: 0.15865525393145707, 0.5: 0.6914624612740131}
+
+
+def _act(oracle_mod, z, kind):
+    z = np.asarray(z, np.float64).reshape(1, -1)
+    return oracle_mod.epilogue(z, bias=np.zeros(z.shape[1]), kind=kind)[0]
+
+
+def test_epilogue_relu_closed_form(oracle_mod):
+    z = np.array([-3.0, -0.0, 0.0, 1e-300, 2.5, -1e-300])
+    y = _act(oracle_mod, z, "bias_relu")
+    assert np.array_equal(y, [0.0, 0.0, 0.0, 1e-300, 2.5, 0.0])
+    assert not np.signbit(y).any()           # +0 for every z <= 0
+
+
+def test_epilogue_gelu_is_z_phi_z(oracle_mod):
+    for z, phi in PHI.items():
+        assert _act(oracle_mod, [z], "bias_gelu")[0] == pytest.approx(z * phi, rel=1e-14)
+    # the tanh approximation differs by ~1.5e-4 at z = 1: must not be what is computed
+    assert abs(_act(oracle_mod, [1.0], "bias_gelu")[0] - 0.8411919906082768) > 1e-4
+
+
+def test_epilogue_silu_values(oracle_mod):
+    e = np.e
+    assert _act(oracle_mod, [1.0], "bias_silu")[0] == pytest.approx(e / (1 + e), rel=1e-15)
+    assert _act(oracle_mod, [0.0], "bias_silu")[0] == 0.0
+    # far tails: z * logistic(z) -> z for large z, -> z e^z for very negative z
+    assert _act(oracle_mod, [40.0], "bias_silu")[0] == pytest.approx(40.0, rel=1e-15)
+    assert _act(oracle_mod, [-800.0], "bias_silu")[0] == 0.0 or abs(_act(oracle_mod, [-800.0], "bias_silu")[0]) < 1e-300
+    assert _act(oracle_mod, [-30.0], "bias_silu")[0] == pytest.approx(-30.0 * np.exp(-30.0), rel=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["bias_silu", "bias_gelu"])
+def test_epilogue_odd_part_identity(oracle_mod, kind):
+    # logistic(z) + logistic(-z) = 1 and Phi(z) + Phi(-z) = 1 give
+    # act(z) - act(-z) = z for both SiLU and GELU.
+    z = np.linspace(-12, 12, 97)
+    d = _act(oracle_mod, z, kind) - _act(oracle_mod, -z, kind)
+    assert np.allclose(d, z, rtol=0, atol=1e-13)
+
+
+def test_epilogue_order_scales_bias_then_activation(oracle_mod):
+    acc = np.array([[-1.0, 3.0], [2.0, -4.0]])
+    sa = np.array([2.0, -1.0])        # per row
+    sb = np.array([1.0, 0.5])         # per column
+    bias = np.array([3.0, -1.0])
+    # z = (acc * sa[m]) * sb[n] + bias[n], worked by hand
+    z = np.array([[-2.0 + 3.0, 3.0 - 1.0], [-2.0 + 3.0, 2.0 - 1.0]])
+    assert np.array_equal(oracle_mod.epilogue(acc, sa, sb, bias, "bias"), z)
+    assert np.array_equal(oracle_mod.epilogue(acc, sa, sb, bias, "bias_relu"), np.maximum(z, 0))
+    # ReLU after the bias, not before: relu(acc) + bias would give [3, 3.5] in row 0
+    assert oracle_mod.epilogue(acc, sa, sb, bias, "bias_relu")[0, 0] == 1.0
+    # scalar scales broadcast; "none" ignores the bias
+    assert np.array_equal(oracle_mod.epilogue(acc, 2.0, 0.5, None, "none"), acc)
+
+
+def test_epilogue_scale_vectors_equal_prescaled_inputs(oracle_mod):
+    # Per-row s_a scales row m of A, per-column s_b scales row n of B: with
+    # powers of two the pre-scaled bf16 inputs are exact, so the GEMM of the
+    # scaled inputs must equal the epilogue applied to the unscaled GEMM.
+    rng = np.random.default_rng(7)
+    M, N, K = 5, 6, 64
+    a = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    b = rng.integers(-4, 5, (N, K)).astype(np.float32)
+    sa = 2.0 ** rng.integers(-3, 4, M)
+    sb = 2.0 ** rng.integers(-3, 4, N)
+    acc, _ = oracle_mod.gemm_bt(bf16(a), bf16(b), dtype="bf16")
+    scaled, _ = oracle_mod.gemm_bt(bf16(a * sa[:, None].astype(np.float32)), bf16(b * sb[:, None].astype(np.float32)),
+                                   dtype="bf16")
+    assert np.array_equal(oracle_mod.epilogue(acc, sa, sb, None, "none"), scaled)
+    bias = rng.integers(-8, 9, N).astype(np.float64)
+    assert np.array_equal(oracle_mod.epilogue(acc, sa, sb, bias, "bias") - bias[None, :], scaled)
+
+
+def test_epilogue_rejects_unknown_kind(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.epilogue(np.zeros((1, 1)), kind="bias_tanh")
