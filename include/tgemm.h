@@ -118,6 +118,57 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
 int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C,
              const float *scale, hipStream_t stream);
 
+/*
+ * Fused epilogues.  The pages' GEMM takes scale_a, scale_b and bias tensors
+ * and an epilogue choice of "none", "bias", "bias_relu", "bias_silu" or
+ * "bias_gelu" (FlyDSL "Kernel authoring guide", section 11 "Complete
+ * example: Preshuffle GEMM"), applying the scales as (acc * scale_a) *
+ * scale_b in fp32 (FlyDSL "Kernel Authoring" skill, section 3).  This
+ * library's reading of the shapes and formulas, all in fp32:
+ *
+ *   z[m][n] = (acc[m][n] * sa(m)) * sb(n)  (+ bias[n])
+ *   C[m][n] = cvt( act(z[m][n]) )
+ *
+ *   sa(m) = scale_a[m] (per row of C) or scale_a[0], 1 when scale_a is NULL;
+ *   sb(n) = scale_b[n] (per column of C) or scale_b[0], 1 when NULL;
+ *   act:  none; ReLU z > 0 ? z : +0; SiLU z / (1 + e^-z);
+ *         GELU by its definition z * Phi(z) = z / 2 * (1 + erf(z / sqrt 2)).
+ */
+typedef enum {
+    GEMM_EPI_NONE = 0,           /* scales only; bias must be NULL            */
+    GEMM_EPI_BIAS = 1,           /* + bias                                    */
+    GEMM_EPI_BIAS_RELU = 2,      /* + bias, then ReLU                         */
+    GEMM_EPI_BIAS_SILU = 3,      /* + bias, then SiLU                         */
+    GEMM_EPI_BIAS_GELU = 4       /* + bias, then GELU (erf form)              */
+} gemm_epilogue;
+
+typedef struct {
+    const float *scale_a;        /* device; NULL, 1 value, or M values; 4-byte aligned           */
+    const float *scale_b;        /* device; NULL, 1 value, or N values; 4-byte aligned, 16-byte
+                                    aligned when per column                                      */
+    const float *bias;           /* device; N values, 16-byte aligned; required by the bias
+                                    epilogues, NULL for GEMM_EPI_NONE                             */
+    int32_t scale_a_per_row;     /* 0: scale_a[0] scales every row; 1: scale_a[m] scales row m    */
+    int32_t scale_b_per_col;     /* 0: scale_b[0] scales every column; 1: scale_b[n] column n     */
+    int32_t epilogue;            /* gemm_epilogue                                                 */
+} gemm_epilogue_args;
+
+/*
+ * gemm_run_ex -- gemm_run with the fused epilogue above.
+ *   A, B, C, stream  as for gemm_run.
+ *   epi      host pointer to the description (read during the call only; the
+ *            vectors it points to are read on the device, asynchronously, and
+ *            must stay valid until the launch completes).  NULL = no scaling,
+ *            no bias, no activation.
+ * gemm_run(plan, A, B, C, scale, s) is gemm_run_ex with scale_a = scale,
+ * scale_b = scale + 1 (per tensor) and GEMM_EPI_NONE.
+ * Errors: GEMM_ERR_INVALID_ARG for an unknown epilogue, a per-row/column flag
+ * other than 0 or 1, a missing bias (bias epilogues) or an unexpected one
+ * (GEMM_EPI_NONE), or a misaligned vector; otherwise as gemm_run.
+ */
+int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C,
+                const gemm_epilogue_args *epi, hipStream_t stream);
+
 /* gemm_last_error -- message for the calling thread's last failure ("" if none). */
 const char *gemm_last_error(void);
 

@@ -198,16 +198,30 @@ def epilogue(acc: np.ndarray, scale_a=None, scale_b=None, bias=None, kind: str =
     """
     if kind not in ACTIVATIONS:
         raise ValueError("unknown epilogue %r" % kind)
+    acc = np.asarray(acc, dtype=np.float64)
+    M, N = acc.shape
+    sa = None if scale_a is None else np.broadcast_to(
+        np.asarray(scale_a, np.float64).reshape(-1, 1) if np.ndim(scale_a) else np.float64(scale_a), (M, N))
+    sb = None if scale_b is None else np.broadcast_to(
+        np.asarray(scale_b, np.float64).reshape(1, -1) if np.ndim(scale_b) else np.float64(scale_b), (M, N))
+    bz = None if kind == "none" else np.broadcast_to(np.asarray(bias, np.float64).reshape(1, -1), (M, N))
+    return epilogue_entries(acc, sa, sb, bz, kind)
+
+
+def epilogue_entries(acc, sa=None, sb=None, bias=None, kind: str = "none") -> np.ndarray:
+    """The same epilogue element by element: z = (acc * sa) * sb + bias, then
+    the activation; every argument an array of the same shape (or None for
+    sa = 1, sb = 1, and no bias with kind "none")."""
+    if kind not in ACTIVATIONS:
+        raise ValueError("unknown epilogue %r" % kind)
     z = np.array(acc, dtype=np.float64, copy=True)
-    if scale_a is not None:
-        sa = np.asarray(scale_a, dtype=np.float64)
-        z = z * (sa.reshape(-1, 1) if sa.ndim else sa)
-    if scale_b is not None:
-        sb = np.asarray(scale_b, dtype=np.float64)
-        z = z * (sb.reshape(1, -1) if sb.ndim else sb)
+    if sa is not None:
+        z = z * np.asarray(sa, np.float64)
+    if sb is not None:
+        z = z * np.asarray(sb, np.float64)
     if kind == "none":
         return z
-    z = z + np.asarray(bias, dtype=np.float64).reshape(1, -1)
+    z = z + np.asarray(bias, np.float64)
     if kind == "bias_relu":
         return np.where(z > 0, z, 0.0)
     if kind == "bias_silu":

@@ -27,10 +27,17 @@ def to_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(bits).cuda()
 
 
+def _dev_f32(x):
+    return torch.tensor(np.atleast_1d(np.asarray(x, np.float32)), dtype=torch.float32, device="cuda")
+
+
 def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
-             scale=(1.0, 1.0), use_scale=True, stream=None, plan=None, return_plan_info=False):
-    """One C = A * B^T through gemm_plan_create / [gemm_preshuffle_b] / gemm_run.
-    Returns the raw bits of C as a numpy array (M x N)."""
+             scale=(1.0, 1.0), use_scale=True, stream=None, plan=None, return_plan_info=False, epi=None):
+    """One C = A * B^T through gemm_plan_create / [gemm_preshuffle_b] /
+    gemm_run, or gemm_run_ex when ``epi`` is given: a dict with optional
+    scale_a (scalar or M values), scale_b (scalar or N values), bias (N
+    values) and kind (a name in tg.EPILOGUES).  Returns the raw bits of C as a
+    numpy array (M x N)."""
     code = DTYPE_CODE[(dtype, out)]
     lay = tg.LAYOUTS[layout]
     own = plan is None
@@ -45,8 +52,18 @@ def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
         Bx = torch.empty(tg.gemm_preshuffled_b_bytes(plan.handle), dtype=torch.uint8, device="cuda")
         plan.preshuffle_b(B.data_ptr(), Bx.data_ptr(), s)
     C = torch.full((max(1, M * N * ob),), 0x5A, dtype=torch.uint8, device="cuda")
-    sc = torch.tensor(scale, dtype=torch.float32, device="cuda")
-    plan.run(A.data_ptr(), Bx.data_ptr(), C.data_ptr(), sc.data_ptr() if use_scale else None, s)
+    if epi is None:
+        sc = torch.tensor(scale, dtype=torch.float32, device="cuda")
+        plan.run(A.data_ptr(), Bx.data_ptr(), C.data_ptr(), sc.data_ptr() if use_scale else None, s)
+    else:
+        keep = {k: _dev_f32(epi[k]) for k in ("scale_a", "scale_b", "bias") if epi.get(k) is not None}
+        plan.run_ex(A.data_ptr(), Bx.data_ptr(), C.data_ptr(), stream=s,
+                    scale_a=keep["scale_a"].data_ptr() if "scale_a" in keep else None,
+                    scale_a_per_row=np.ndim(epi.get("scale_a")) > 0,
+                    scale_b=keep["scale_b"].data_ptr() if "scale_b" in keep else None,
+                    scale_b_per_col=np.ndim(epi.get("scale_b")) > 0,
+                    bias=keep["bias"].data_ptr() if "bias" in keep else None,
+                    epilogue=tg.EPILOGUES[epi.get("kind", "none")])
     torch.cuda.synchronize()
     raw = C.cpu().numpy()[:M * N * ob]
     info = plan.info()
@@ -71,6 +88,28 @@ def assert_within_bound(C: np.ndarray, C_ref: np.ndarray, S: np.ndarray, dtype: 
     if bad.any():
         idx = np.argwhere(bad)[:5]
         detail = ", ".join("(%s) got %r want %r bound %r" % (tuple(i), C[tuple(i)], C_ref[tuple(i)],
+                                                             bound[tuple(i)]) for i in idx)
+        raise AssertionError("%s: %d of %d elements outside the bound; %s" % (what, int(bad.sum()), bad.size, detail))
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+
+
+def assert_epilogue_within_bound(Y, Y_ref, S_z, Z_abs, bias_abs, dtype, kind, what=""):
+    """Bound for C = act((acc * sa) * sb + bias):
+    |Y - Y_ref| <= L * (4e-6 * S_z + 2^-20 * (Z_abs + bias_abs)) + rho * |Y_ref|,
+    with S_z = |sa * sb| * sum_k |a_ik b_jk| (the GEMM's own term, scaled),
+    Z_abs = |(acc * sa) * sb| of the exact result, L the activation's largest
+    slope (carries the pre-activation error through), 2^-20 covering the fp32
+    roundings of the scale, bias and activation evaluation, and rho the output
+    rounding term of the GEMM bound."""
+    import oracle
+    assert np.all(np.isfinite(Y)), "%s: non-finite output" % what
+    L = oracle.ACT_LIPSCHITZ[kind]
+    bound = L * (ABS_COEF * S_z + 2.0 ** -20 * (Z_abs + bias_abs)) + RHO[dtype] * np.abs(Y_ref)
+    err = np.abs(Y - Y_ref)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = ", ".join("(%s) got %r want %r bound %r" % (tuple(i), Y[tuple(i)], Y_ref[tuple(i)],
                                                              bound[tuple(i)]) for i in idx)
         raise AssertionError("%s: %d of %d elements outside the bound; %s" % (what, int(bad.sum()), bad.size, detail))
     return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0

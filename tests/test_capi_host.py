@@ -9,6 +9,7 @@
 * the XCD-aware raster is a bijection onto the tile grid;
 * argument validation rejects what it documents, before any device call.
 """
+import ctypes
 import itertools
 import json
 import os
@@ -195,3 +196,37 @@ def test_run_argument_errors_before_device(lib):
     # M == 0 is a successful no-op that touches no device
     with tg.Plan(0, 64, 64, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
         assert lib.gemm_run(p.handle, None, None, None, None, None) == tg.GEMM_OK
+
+
+def test_run_ex_argument_errors_before_device(lib):
+    """gemm_run_ex rejects a bad epilogue description before any device work."""
+    E = tg.gemm_epilogue_args
+    A, B, C = 0x100000, 0x200000, 0x300000
+    with tg.Plan(64, 64, 64, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        def run(epi):
+            return lib.gemm_run_ex(p.handle, A, B, C, ctypes.byref(epi), None)
+        assert run(E(None, None, None, 0, 0, 7)) == tg.GEMM_ERR_INVALID_ARG
+        assert "epilogue" in tg.gemm_last_error()
+        assert run(E(None, None, None, 2, 0, tg.GEMM_EPI_NONE)) == tg.GEMM_ERR_INVALID_ARG
+        assert run(E(None, None, None, 0, 0, tg.GEMM_EPI_BIAS_GELU)) == tg.GEMM_ERR_INVALID_ARG
+        assert "bias" in tg.gemm_last_error()
+        assert run(E(None, None, 0x400000, 0, 0, tg.GEMM_EPI_NONE)) == tg.GEMM_ERR_INVALID_ARG
+        assert run(E(0x400002, None, None, 1, 0, tg.GEMM_EPI_NONE)) == tg.GEMM_ERR_INVALID_ARG
+        assert "aligned" in tg.gemm_last_error()
+        assert run(E(None, 0x400004, None, 0, 1, tg.GEMM_EPI_NONE)) == tg.GEMM_ERR_INVALID_ARG   # per column: 16 B
+        assert run(E(None, None, 0x400008, 0, 0, tg.GEMM_EPI_BIAS)) == tg.GEMM_ERR_INVALID_ARG
+        # the plain checks still apply
+        assert lib.gemm_run_ex(p.handle, A, B, A, None, None) == tg.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_run_ex(None, A, B, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+    with tg.Plan(0, 64, 64, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        epi = E(None, None, 0x400000, 0, 0, tg.GEMM_EPI_BIAS_RELU)
+        assert lib.gemm_run_ex(p.handle, None, None, None, ctypes.byref(epi), None) == tg.GEMM_OK
+
+
+def test_epilogue_enum_matches_header():
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "tgemm.h")).read()
+    for name, value in [("GEMM_EPI_NONE", 0), ("GEMM_EPI_BIAS", 1), ("GEMM_EPI_BIAS_RELU", 2),
+                        ("GEMM_EPI_BIAS_SILU", 3), ("GEMM_EPI_BIAS_GELU", 4)]:
+        assert re.search(r"\b%s = %d\b" % (name, value), text), name
+        assert getattr(tg, name) == value
+    assert ctypes.sizeof(tg.gemm_epilogue_args) == 3 * 8 + 3 * 4 + 4    # 3 pointers, 3 int32, padding

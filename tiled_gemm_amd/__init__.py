@@ -29,12 +29,16 @@ GEMM_E4M3_OUT_BF16 = 2
 GEMM_LAYOUT_BT = 0
 GEMM_LAYOUT_BT_PRESHUFFLED = 1
 
+GEMM_EPI_NONE, GEMM_EPI_BIAS, GEMM_EPI_BIAS_RELU, GEMM_EPI_BIAS_SILU, GEMM_EPI_BIAS_GELU = range(5)
+EPILOGUES = {"none": GEMM_EPI_NONE, "bias": GEMM_EPI_BIAS, "bias_relu": GEMM_EPI_BIAS_RELU,
+             "bias_silu": GEMM_EPI_BIAS_SILU, "bias_gelu": GEMM_EPI_BIAS_GELU}
+
 GEMM_MAX_RANK = 8
 GEMM_VIEW_A, GEMM_VIEW_B, GEMM_VIEW_B_SHUF, GEMM_VIEW_B_SRC, GEMM_VIEW_C, GEMM_VIEW_LDS_A, GEMM_VIEW_TILE = range(7)
 
 EXPORTS = (
     "gemm_plan_create", "gemm_plan_destroy", "gemm_preshuffled_b_bytes", "gemm_preshuffle_b",
-    "gemm_run", "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
+    "gemm_run", "gemm_run_ex", "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
     "gemm_layout_idx2crd", "gemm_lds_swizzle", "gemm_tile_of_workgroup",
 )
 
@@ -43,6 +47,12 @@ class GemmError(RuntimeError):
     def __init__(self, code: int, where: str, msg: str):
         super().__init__("%s failed (%d): %s" % (where, code, msg))
         self.code = code
+
+
+class gemm_epilogue_args(ctypes.Structure):
+    _fields_ = [("scale_a", ctypes.c_void_p), ("scale_b", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("scale_a_per_row", ctypes.c_int32), ("scale_b_per_col", ctypes.c_int32),
+                ("epilogue", ctypes.c_int32)]
 
 
 class gemm_plan_info(ctypes.Structure):
@@ -77,6 +87,7 @@ def load() -> ctypes.CDLL:
         "gemm_preshuffled_b_bytes": (ctypes.c_size_t, [vp]),
         "gemm_preshuffle_b": (c_int, [vp, vp, vp, vp]),
         "gemm_run": (c_int, [vp, vp, vp, vp, vp, vp]),
+        "gemm_run_ex": (c_int, [vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp]),
         "gemm_last_error": (ctypes.c_char_p, []),
         "gemm_plan_query": (c_int, [vp, ctypes.POINTER(gemm_plan_info)]),
         "gemm_plan_layout": (c_int, [vp, c_int, p32, p64, p64]),
@@ -131,6 +142,14 @@ def gemm_preshuffle_b(plan: int, B: int, B_shuf: int, stream: int = 0) -> None:
 
 def gemm_run(plan: int, A: int, B: int, C: int, scale: int | None = None, stream: int = 0) -> None:
     _check(load().gemm_run(plan, A, B, C, scale or None, stream), "gemm_run")
+
+
+def gemm_run_ex(plan: int, A: int, B: int, C: int, scale_a: int | None = None, scale_a_per_row: bool = False,
+                scale_b: int | None = None, scale_b_per_col: bool = False, bias: int | None = None,
+                epilogue: int = GEMM_EPI_NONE, stream: int = 0) -> None:
+    epi = gemm_epilogue_args(scale_a or None, scale_b or None, bias or None, int(scale_a_per_row),
+                             int(scale_b_per_col), epilogue)
+    _check(load().gemm_run_ex(plan, A, B, C, ctypes.byref(epi), stream), "gemm_run_ex")
 
 
 def gemm_plan_query(plan: int) -> dict:
@@ -211,3 +230,7 @@ class Plan:
 
     def run(self, A: int, B: int, C: int, scale: int | None = None, stream: int = 0) -> None:
         gemm_run(self.handle, A, B, C, scale, stream)
+
+    def run_ex(self, A: int, B: int, C: int, stream: int = 0, **epi) -> None:
+        """gemm_run_ex; keyword arguments as for the module-level gemm_run_ex."""
+        gemm_run_ex(self.handle, A, B, C, stream=stream, **epi)

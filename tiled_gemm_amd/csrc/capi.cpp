@@ -428,7 +428,11 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
     return GEMM_OK;
 }
 
-int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const float *scale,
+}  // extern "C"
+
+namespace {
+
+int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const tg::EpiArgs &epi,
              hipStream_t stream)
 {
     if (!plan)
@@ -446,8 +450,6 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const
         return fail(GEMM_ERR_INVALID_ARG, "NULL C");
     if ((A && misaligned(A)) || (B && misaligned(B)) || misaligned(C))
         return fail(GEMM_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
-    if (scale && ((uintptr_t)scale & 3u))
-        return fail(GEMM_ERR_INVALID_ARG, "scale must be 4-byte aligned");
     const size_t cbytes = (size_t)I.M * I.N * I.out_bytes;
     if (overlap(C, cbytes, A, (size_t)I.M * plan->kbytes) || overlap(C, cbytes, B, (size_t)I.N * plan->kbytes))
         return fail(GEMM_ERR_INVALID_ARG, "C overlaps A or B");
@@ -459,7 +461,7 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.A = A;
         a.B = B;
         a.C = C;
-        a.scale = scale;
+        a.epi = epi;
         a.M = (int32_t)I.M;
         a.N = (int32_t)I.N;
         a.kbytes = (int32_t)plan->kbytes;
@@ -471,7 +473,7 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.A = A;
         a.B = B;
         a.C = C;
-        a.scale = scale;
+        a.epi = epi;
         a.M = (int32_t)I.M;
         a.N = (int32_t)I.N;
         a.kbytes = (int32_t)plan->kbytes;
@@ -487,6 +489,55 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const
         return fail(GEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     ok();
     return GEMM_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const float *scale,
+             hipStream_t stream)
+{
+    if (scale && !aligned(scale, 4))
+        return fail(GEMM_ERR_INVALID_ARG, "scale must be 4-byte aligned");
+    tg::EpiArgs e{};
+    e.sa = scale;
+    e.sb = scale ? scale + 1 : nullptr;
+    e.act = tg::kActNone;
+    return run_impl(plan, A, B, C, e, stream);
+}
+
+int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C, const gemm_epilogue_args *epi,
+                hipStream_t stream)
+{
+    tg::EpiArgs e{};
+    if (epi) {
+        if (epi->epilogue < GEMM_EPI_NONE || epi->epilogue > GEMM_EPI_BIAS_GELU)
+            return fail(GEMM_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi->epilogue);
+        if ((epi->scale_a_per_row != 0 && epi->scale_a_per_row != 1) ||
+            (epi->scale_b_per_col != 0 && epi->scale_b_per_col != 1))
+            return fail(GEMM_ERR_INVALID_ARG, "scale_a_per_row and scale_b_per_col must be 0 or 1");
+        const bool wants_bias = epi->epilogue != GEMM_EPI_NONE;
+        if (wants_bias && !epi->bias)
+            return fail(GEMM_ERR_INVALID_ARG, "the bias epilogues need a bias vector");
+        if (!wants_bias && epi->bias)
+            return fail(GEMM_ERR_INVALID_ARG, "bias given with GEMM_EPI_NONE");
+        if ((epi->scale_a && !aligned(epi->scale_a, 4)) ||
+            (epi->scale_b && !aligned(epi->scale_b, epi->scale_b_per_col ? 16 : 4)) ||
+            (epi->bias && !aligned(epi->bias, 16)))
+            return fail(GEMM_ERR_INVALID_ARG,
+                        "scale_a must be 4-byte aligned; per-column scale_b and bias 16-byte aligned");
+        e.sa = epi->scale_a;
+        e.sb = epi->scale_b;
+        e.bias = epi->bias;
+        e.sa_rows = epi->scale_a_per_row;
+        e.sb_cols = epi->scale_b_per_col;
+        static const int kAct[] = {tg::kActNone, tg::kActNone, tg::kActRelu, tg::kActSilu, tg::kActGelu};
+        e.act = kAct[epi->epilogue];
+    }
+    return run_impl(plan, A, B, C, e, stream);
 }
 
 }  // extern "C"

@@ -7,6 +7,7 @@
 
 #include <type_traits>
 
+#include "kernels.hpp"
 #include "layout.hpp"
 
 namespace tg {
@@ -143,6 +144,110 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 
 template <int N>
 using ic_t = std::integral_constant<int, N>;
+
+// ---------------------------------------------------------------------------
+// Fused epilogue: z = (acc * s_a[row]) * s_b[col] (+ bias[col]), then the
+// activation, in fp32.  The vectors are read through range-checked buffer
+// resources, so rows past M (whose stores are dropped anyway) read zeros
+// instead of memory past the caller's vectors.
+// ---------------------------------------------------------------------------
+struct EpiView {
+    __amdgpu_buffer_rsrc_t ra, rb, rz;
+    uint32_t sa_step, sb_step;   // bytes per row / column; 0 broadcasts element 0
+    bool has_a, has_b, has_bias;
+    int act;
+};
+
+__device__ inline EpiView epi_view(const EpiArgs &e, int M, int N)
+{
+    EpiView v;
+    v.has_a = e.sa != nullptr;
+    v.has_b = e.sb != nullptr;
+    v.has_bias = e.bias != nullptr;
+    v.sa_step = e.sa_rows ? 4u : 0u;
+    v.sb_step = e.sb_cols ? 4u : 0u;
+    v.ra = make_rsrc(e.sa, e.sa_rows ? (uint32_t)M * 4u : 4u);
+    v.rb = make_rsrc(e.sb, e.sb_cols ? (uint32_t)N * 4u : 4u);
+    v.rz = make_rsrc(e.bias, (uint32_t)N * 4u);
+    v.act = e.act;
+    return v;
+}
+
+__device__ inline float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// s_a of one row (row counted in the whole C).
+__device__ inline float epi_row_scale(const EpiView &v, int row)
+{
+    return v.has_a ? as_f32(__builtin_amdgcn_raw_buffer_load_b32(v.ra, (uint32_t)row * v.sa_step, 0, 0)) : 1.f;
+}
+
+// s_b and bias of the 4 columns col .. col+3 (col % 4 == 0; the vectors are
+// 16-byte aligned).
+__device__ inline f32x4 epi_col_scale4(const EpiView &v, int col)
+{
+    if (!v.has_b)
+        return f32x4{1.f, 1.f, 1.f, 1.f};
+    if (v.sb_step == 0) {
+        const float s = as_f32(__builtin_amdgcn_raw_buffer_load_b32(v.rb, 0u, 0, 0));
+        return f32x4{s, s, s, s};
+    }
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(v.rb, (uint32_t)col * 4u, 0, 0));
+}
+
+__device__ inline f32x4 epi_bias4(const EpiView &v, int col)
+{
+    if (!v.has_bias)
+        return f32x4{0.f, 0.f, 0.f, 0.f};
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(v.rz, (uint32_t)col * 4u, 0, 0));
+}
+
+// The same for the 2 columns col, col+1 (col even).
+__device__ inline void epi_col2(const EpiView &v, int col, float *sb, float *bz)
+{
+    sb[0] = sb[1] = 1.f;
+    bz[0] = bz[1] = 0.f;
+    if (v.has_b) {
+        if (v.sb_step == 0) {
+            sb[0] = sb[1] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(v.rb, 0u, 0, 0));
+        } else {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(v.rb, (uint32_t)col * 4u, 0, 0);
+            sb[0] = as_f32(t.x);
+            sb[1] = as_f32(t.y);
+        }
+    }
+    if (v.has_bias) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(v.rz, (uint32_t)col * 4u, 0, 0);
+        bz[0] = as_f32(t.x);
+        bz[1] = as_f32(t.y);
+    }
+}
+
+// ReLU max(z, 0) with +0 for every z <= 0; SiLU z / (1 + e^-z); GELU by its
+// definition z * Phi(z) = z / 2 * (1 + erf(z / sqrt 2)).
+__device__ inline float epi_act(float z, int act)
+{
+    if (act == kActRelu)
+        return z > 0.f ? z : 0.f;
+    if (act == kActSilu)
+        return z / (1.f + expf(-z));
+    if (act == kActGelu)
+        return 0.5f * z * (1.f + erff(z * 0.70710678118654752440f));
+    return z;
+}
+
+__device__ inline float epi_apply1(const EpiView &v, float acc, float sa, float sb, float bz)
+{
+    float z = (acc * sa) * sb;
+    if (v.has_bias)
+        z = z + bz;
+    return epi_act(z, v.act);
+}
+
+__device__ inline f32x4 epi_apply4(const EpiView &v, f32x4 acc, float sa, f32x4 sb, f32x4 bz)
+{
+    return f32x4{epi_apply1(v, acc.x, sa, sb.x, bz.x), epi_apply1(v, acc.y, sa, sb.y, bz.y),
+                 epi_apply1(v, acc.z, sa, sb.z, bz.z), epi_apply1(v, acc.w, sa, sb.w, bz.w)};
+}
 
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ inline int lane_id() { return threadIdx.x & 63; }

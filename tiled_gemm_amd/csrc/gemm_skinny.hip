@@ -169,11 +169,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_kernel(const Skinny
                 red[w][i * 16 + r16][j * 16 + 4 * q + v] = acc[i][j][v];
     __syncthreads();
 
-    float sa = 1.f, sb = 1.f;
-    if (p.scale != nullptr) {
-        sa = p.scale[0];
-        sb = p.scale[1];
-    }
+    const EpiView ev = epi_view(p.epi, p.M, p.N);
     constexpr int OB = OUT == kOutF32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)p.N * OB;
     const auto rC = make_rsrc(p.C, (uint32_t)p.M * ldc);
@@ -186,9 +182,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_kernel(const Skinny
             s0 += red[ww][row][col];
             s1 += red[ww][row][col + 1];
         }
-        s0 = (s0 * sa) * sb;
-        s1 = (s1 * sa) * sb;
         const int n = n0 + col;
+        float sb[2], bz[2];
+        epi_col2(ev, n, sb, bz);
+        const float sa = epi_row_scale(ev, row);
+        s0 = epi_apply1(ev, s0, sa, sb[0], bz[0]);
+        s1 = epi_apply1(ev, s1, sa, sb[1], bz[1]);
         const uint32_t voffc = (row < p.M && n < p.N) ? (uint32_t)row * ldc + (uint32_t)n * OB : kOobOffset;
         if constexpr (OUT == kOutF32)
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, s0),

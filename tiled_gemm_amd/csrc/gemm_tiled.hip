@@ -223,25 +223,22 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
         }
     }
 
-    // ---- epilogue: scale, convert, store.  Lane l holds C[row][col .. col+3]
-    // with row = l % 16 and col = 4 * (l / 16) inside each 16x16 tile.
-    float sa = 1.f, sb = 1.f;
-    if (p.scale != nullptr) {
-        sa = p.scale[0];
-        sb = p.scale[1];
-    }
+    // ---- epilogue: scale, bias, activation, convert, store.  Lane l holds
+    // C[row][col .. col+3] with row = l % 16 and col = 4 * (l / 16) inside
+    // each 16x16 tile.
+    const EpiView ev = epi_view(p.epi, p.M, p.N);
     constexpr int OB = OUT == kOutF32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)p.N * OB;
     const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = wm * Cfg::WTM + i * 16 + r16;
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * Cfg::WTN + j * 16 + 4 * q;
+        const f32x4 sb = epi_col_scale4(ev, col), bz = epi_bias4(ev, col);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * Cfg::WTN + j * 16 + 4 * q;
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * Cfg::WTM + i * 16 + r16;
             const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
-            f32x4 v = acc[i][j];
-            v = (v * sa) * sb;
+            const f32x4 v = epi_apply4(ev, acc[i][j], epi_row_scale(ev, m0 + row), sb, bz);
             if constexpr (OUT == kOutF32) {
                 buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
             } else {

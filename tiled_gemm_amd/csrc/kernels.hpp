@@ -12,11 +12,22 @@ namespace tg {
 enum Elem { kBf16 = 0, kFp8 = 1 };
 enum Out { kOutF32 = 0, kOutBf16 = 1 };
 
+// Epilogue operands (device pointers): C = act((acc * s_a) * s_b + bias).
+enum EpiAct { kActNone = 0, kActRelu = 1, kActSilu = 2, kActGelu = 3 };
+struct EpiArgs {
+    const float *sa;        // nullptr (1), one value for every row, or one per row of C
+    const float *sb;        // nullptr (1), one value for every column, or one per column
+    const float *bias;      // nullptr (0) or one per column
+    int32_t sa_rows;        // 0: sa[0] for every row; 1: sa[row]
+    int32_t sb_cols;        // 0: sb[0] for every column; 1: sb[col]
+    int32_t act;            // EpiAct
+};
+
 struct TiledArgs {
     const void *A;
     const void *B;
     void *C;
-    const float *scale;     // device {s_a, s_b} or nullptr
+    EpiArgs epi;
     int32_t M, N;
     int32_t kbytes;         // bytes of one row of A and of B (K * elem_bytes)
     int32_t k_tiles;        // ceil(kbytes / 128)
@@ -28,7 +39,7 @@ struct SkinnyArgs {
     const void *A;
     const void *B;
     void *C;
-    const float *scale;
+    EpiArgs epi;
     int32_t M, N;
     int32_t kbytes;
     int32_t k_tiles;
