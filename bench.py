@@ -38,10 +38,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1):
+def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
     """Time `steps` gemm_run launches (after `warmup`) with HIP events on the
     launch stream.  With rotate > 1, that many independent input/output sets
-    are cycled so the operands are not served from the last-level cache."""
+    are cycled so the operands are not served from the last-level cache.
+    With epi (an epilogue name), gemm_run_ex is timed instead, with per-row
+    and per-column scale vectors and a bias vector."""
     code = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
             ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}[(w.dtype, w.out)]
     plan = tg.Plan(w.M, w.N, w.K, code, tg.LAYOUTS[w.layout])
@@ -72,16 +74,29 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1):
         sets.append((A, B, C))
     scale = torch.tensor([inp.scale_a, inp.scale_b], dtype=torch.float32, device="cuda")
     sp = scale.data_ptr() if w.dtype == "e4m3" else None
+    if epi is None:
+        def launch(A, B, C):
+            plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
+    else:
+        g = torch.Generator(device="cpu").manual_seed(w.seed)
+        sa = (torch.rand(w.M, generator=g) * 0.04 + 0.01).cuda()
+        sb = (torch.rand(w.N, generator=g) * 1.5 + 0.5).cuda()
+        bias = torch.randn(w.N, generator=g).cuda()
+
+        def launch(A, B, C):
+            plan.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream=s, scale_a=sa.data_ptr(),
+                        scale_a_per_row=True, scale_b=sb.data_ptr(), scale_b_per_col=True,
+                        bias=bias.data_ptr(), epilogue=tg.EPILOGUES[epi])
     for i in range(warmup):
         A, B, C = sets[i % rotate]
-        plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
+        launch(A, B, C)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(steps):
         A, B, C = sets[i % rotate]
-        plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
+        launch(A, B, C)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -171,6 +186,16 @@ def main():
             name, ms, tflops, gbs, info["tile_m"], info["tile_n"], info["grid"]))
         if name == HEADLINE:
             inputs[name] = inp
+    if not args.only and not args.no_also:
+        # the headline shape again with the fused epilogue: per-row and
+        # per-column scales, bias and GELU
+        w = W.WORKLOADS[HEADLINE]
+        name = HEADLINE + "+scales+bias_gelu"
+        ms, wall, info, _ = time_gemm(torch, tg, w, inputs[HEADLINE], max(10, args.steps // 2), args.warmup,
+                                      1, epi="bias_gelu")
+        results[name] = dict(ms=ms, wall=wall, steps=max(10, args.steps // 2), tflops=w.flops / (ms * 1e-3) / 1e12,
+                             gbs=w.min_bytes / (ms * 1e-3) / 1e9, info=info, shuf_ms=None, rotate=1)
+        log("bench: %-26s %.4f ms  %.1f TFLOP/s" % (name, ms, results[name]["tflops"]))
 
     head = args.only or HEADLINE
     w = W.WORKLOADS[head]
@@ -213,7 +238,7 @@ def main():
     for name, rr in results.items():
         if name == head:
             continue
-        ww = W.WORKLOADS[name]
+        ww = W.WORKLOADS[name.split("+")[0]]
         also[name] = {"ms": round(rr["ms"], 5), "TFLOP/s": round(rr["tflops"], 2),
                       "frac_mfma_peak": round(rr["tflops"] / PEAK_TFLOPS[ww.dtype], 4),
                       "GB/s": round(rr["gbs"], 1), "frac_hbm_peak": round(rr["gbs"] / PEAK_HBM_GBS, 4),
