@@ -10,6 +10,9 @@ Contents
   (plain i-j-k, sequential k, sigma = s_a * s_b for fp8), built with gcc.
 * ``epilogue`` -- the fused epilogue (scale vectors, bias, ReLU / SiLU /
   GELU) applied in fp64 to the exact GEMM result.
+* ``gemm_bt_mx`` / ``gemm_bt_mx_entries`` -- the same loop for MX
+  block-scaled operands (MXFP8: e4m3 elements, MXFP4: e2m1 elements, one
+  E8M0 scale per 32 elements along K).
 * ``round_bf16`` -- the oracle's own round-to-nearest-even to bf16.
 * ``bf16_value`` / ``e4m3fn_value`` -- element decoders from the format
   definitions.
@@ -32,6 +35,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 BF16 = 0
 E4M3FN = 1
+MXFP8 = 2
+MXFP4 = 3
 
 _lib = None
 
@@ -63,6 +68,14 @@ def _load():
     lib.oracle_gemm_bt.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, dbl, vp, vp]
     lib.oracle_gemm_bt_entries.restype = None
     lib.oracle_gemm_bt_entries.argtypes = [i64, ctypes.c_int, vp, vp, dbl, i64, vp, vp, vp, vp]
+    lib.oracle_e2m1_value.restype = dbl
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_value.restype = dbl
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_gemm_bt_mx.restype = None
+    lib.oracle_gemm_bt_mx.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.oracle_gemm_bt_mx_entries.restype = None
+    lib.oracle_gemm_bt_mx_entries.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16_array.restype = None
@@ -235,3 +248,60 @@ def epilogue_entries(acc, sa=None, sb=None, bias=None, kind: str = "none") -> np
 # tests to carry the GEMM's error bound through the activation: 1 for the
 # identity and ReLU; SiLU peaks at 1.0998 (z ~ 2.40), GELU at 1.1290 (z ~ 1.41).
 ACT_LIPSCHITZ = {"none": 1.0, "bias": 1.0, "bias_relu": 1.0, "bias_silu": 1.1, "bias_gelu": 1.13}
+
+
+# ------------------------------------------------------------------ MX operands
+
+def e2m1_value(code: int) -> float:
+    return float(_load().oracle_e2m1_value(int(code) & 0xF))
+
+
+def e8m0_value(bits: int) -> float:
+    return float(_load().oracle_e8m0_value(int(bits) & 0xFF))
+
+
+def _mx(fmt: str):
+    if fmt == "mxfp8":
+        return MXFP8
+    if fmt == "mxfp4":
+        return MXFP4
+    raise ValueError("oracle: unknown MX format %r" % (fmt,))
+
+
+def _mx_operand(x, s, K: int, fmt: str):
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    rows = x.shape[0]
+    if K % 32 or x.shape[1] != (K if fmt == "mxfp8" else K // 2) or s.shape != (rows, K // 32):
+        raise ValueError("oracle: MX operand shape (rows x K%s, scales rows x K/32)" %
+                         ("" if fmt == "mxfp8" else "/2 bytes"))
+    return x, s
+
+
+def gemm_bt_mx(A, SA, B, SB, K: int, fmt: str = "mxfp8", want_s: bool = True):
+    """Full C_ref (fp64) and S for MX operands: A (M x K elements), B (N x K),
+    element bytes row-major (MXFP4: two per byte, even element in the low
+    nibble), scales SA (M x K/32), SB (N x K/32) E8M0 bytes."""
+    A, SA = _mx_operand(A, SA, K, fmt)
+    B, SB = _mx_operand(B, SB, K, fmt)
+    M, N = A.shape[0], B.shape[0]
+    C = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64) if want_s else None
+    _load().oracle_gemm_bt_mx(M, N, K, _mx(fmt), A.ctypes.data, SA.ctypes.data, B.ctypes.data, SB.ctypes.data,
+                              C.ctypes.data, S.ctypes.data if want_s else None)
+    return C, S
+
+
+def gemm_bt_mx_entries(A, SA, B, SB, K: int, rows, cols, fmt: str = "mxfp8"):
+    """C_ref and S of MX operands at the (rows[t], cols[t]) entries only."""
+    A, SA = _mx_operand(A, SA, K, fmt)
+    B, SB = _mx_operand(B, SB, K, fmt)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= A.shape[0] or cols.min() < 0 or cols.max() >= B.shape[0]):
+        raise IndexError("oracle: entry out of range")
+    C = np.empty(rows.shape, np.float64)
+    S = np.empty(rows.shape, np.float64)
+    _load().oracle_gemm_bt_mx_entries(K, _mx(fmt), A.ctypes.data, SA.ctypes.data, B.ctypes.data, SB.ctypes.data,
+                                      rows.size, rows.ctypes.data, cols.ctypes.data, C.ctypes.data, S.ctypes.data)
+    return C, S

@@ -26,6 +26,19 @@
  *               bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is
  *               NaN; no infinities; largest finite value 448.
  *
+ *   e2m1      : OCP MX 4-bit float, 1 sign, 2 exponent bits (bias 1), 1
+ *               fraction bit; exponent field 0 is subnormal (m * 2^-1); all
+ *               16 codes finite (largest 6).  Two per byte, element 2t in the
+ *               low nibble of byte t.
+ *   e8m0      : OCP MX block scale, 8 exponent bits (bias 127), value
+ *               2^(e-127); 0xFF is NaN.
+ *
+ * MX block-scaled operands (OCP Microscaling formats, block size 32; the
+ * pages' gfx950 scaled MFMA, "Kernel Authoring" skill section 9 "Math
+ * intrinsics" and section 5 "MX-scaled WMMA"): element k of row i counts as
+ * elem(i,k) * 2^(scale[i][k/32] - 127), the scales stored rows x K/32 bytes
+ * row-major.
+ *
  * The output rounding to bf16 is round-to-nearest, ties-to-even, done in
  * fp64 with nearbyint() under the default FE_TONEAREST mode.
  *
@@ -40,7 +53,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_BF16 = 0, ORACLE_E4M3FN = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_E4M3FN = 1, ORACLE_MXFP8 = 2, ORACLE_MXFP4 = 3 };
 
 double oracle_bf16_value(uint16_t bits)
 {
@@ -63,6 +76,50 @@ double oracle_e4m3fn_value(uint8_t bits)
     else
         mag = ldexp(1.0 + frac / 8.0, expo - 7);    /* normal: 1.m * 2^(e-7)    */
     return sign ? -mag : mag;
+}
+
+double oracle_e2m1_value(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int expo = (code >> 1) & 0x3;
+    int frac = code & 0x1;
+    double mag = expo == 0 ? 0.5 * frac                     /* subnormal: m * 2^(1-1-1) */
+                           : ldexp(1.0 + frac / 2.0, expo - 1); /* normal: 1.m * 2^(e-1) */
+    return sign ? -mag : mag;
+}
+
+double oracle_e8m0_value(uint8_t bits)
+{
+    if (bits == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)bits - 127);
+}
+
+/* Element k of row r of an MX operand (K elements per row). */
+static double mx_element(int kind, const void *base, const uint8_t *scale, int64_t K, int64_t r, int64_t k)
+{
+    const int64_t idx = r * K + k;
+    double v;
+    if (kind == ORACLE_MXFP8) {
+        v = oracle_e4m3fn_value(((const uint8_t *)base)[idx]);
+    } else {
+        const uint8_t byte = ((const uint8_t *)base)[idx / 2];
+        v = oracle_e2m1_value((idx % 2) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF));
+    }
+    return v * oracle_e8m0_value(scale[r * (K / 32) + k / 32]);
+}
+
+static void dot_entry_mx(int64_t K, int kind, const void *A, const uint8_t *SA, const void *B,
+                         const uint8_t *SB, int64_t i, int64_t j, double *c, double *s)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = mx_element(kind, A, SA, K, i, k) * mx_element(kind, B, SB, K, j, k);
+        acc += p;
+        mag += fabs(p);
+    }
+    *c = acc;
+    *s = mag;
 }
 
 static double element(int kind, const void *base, int64_t idx)
@@ -124,6 +181,38 @@ void oracle_gemm_bt_entries(int64_t K, int kind, const void *A, const void *B,
     for (t = 0; t < count; ++t) {
         double c, s;
         dot_entry(K, kind, A, B, rows[t], cols[t], sigma, &c, &s);
+        C[t] = c;
+        if (S)
+            S[t] = s;
+    }
+}
+
+/* MX product (K % 32 == 0; for MXFP4 K even): full and selected entries. */
+void oracle_gemm_bt_mx(int64_t M, int64_t N, int64_t K, int kind, const void *A, const uint8_t *SA,
+                       const void *B, const uint8_t *SB, double *C, double *S)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double c, s;
+            dot_entry_mx(K, kind, A, SA, B, SB, i, j, &c, &s);
+            C[i * N + j] = c;
+            if (S)
+                S[i * N + j] = s;
+        }
+    }
+}
+
+void oracle_gemm_bt_mx_entries(int64_t K, int kind, const void *A, const uint8_t *SA, const void *B,
+                               const uint8_t *SB, int64_t count, const int64_t *rows, const int64_t *cols,
+                               double *C, double *S)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < count; ++t) {
+        double c, s;
+        dot_entry_mx(K, kind, A, SA, B, SB, rows[t], cols[t], &c, &s);
         C[t] = c;
         if (S)
             S[t] = s;

@@ -319,3 +319,87 @@ def test_epilogue_scale_vectors_equal_prescaled_inputs(oracle_mod):
 def test_epilogue_rejects_unknown_kind(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.epilogue(np.zeros((1, 1)), kind="bias_tanh")
+
+
+# ---------------------------------------------------------------- MX operands
+# OCP Microscaling formats: E2M1 element values and E8M0 scales as the format
+# definitions list them; the MX GEMM against an exact rational brute force
+# whose element packing (even element in the low nibble) and scale placement
+# (one scale per 32 elements along K) are written independently here.
+
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decoder_table(oracle_mod):
+    for code in range(16):
+        mag = E2M1_TABLE[code & 7]
+        assert oracle_mod.e2m1_value(code) == (-mag if code & 8 else mag)
+
+
+def test_e8m0_decoder(oracle_mod):
+    assert oracle_mod.e8m0_value(127) == 1.0
+    assert oracle_mod.e8m0_value(128) == 2.0
+    assert oracle_mod.e8m0_value(126) == 0.5
+    assert oracle_mod.e8m0_value(0) == 2.0 ** -127
+    assert oracle_mod.e8m0_value(254) == 2.0 ** 127
+    assert np.isnan(oracle_mod.e8m0_value(255))
+
+
+def _mx_random(rng, rows, K, fmt):
+    """Random codes and scales, plus their exact rational values."""
+    if fmt == "mxfp8":
+        codes = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x38                  # no NaN codes
+        vals = [[Fraction(float(torch.tensor(int(c), dtype=torch.uint8).view(torch.float8_e4m3fn).float()))
+                 for c in r] for r in codes]
+        packed = codes
+    else:
+        codes = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+        vals = [[Fraction(-E2M1_TABLE[c & 7] if c & 8 else E2M1_TABLE[c & 7]) for c in r] for r in codes]
+        packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(120, 135, (rows, K // 32)).astype(np.uint8)
+    exact = [[vals[i][k] * Fraction(2) ** (int(scales[i][k // 32]) - 127) for k in range(K)] for i in range(rows)]
+    return packed, scales, exact
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(3, 5, 64), (2, 4, 96)])
+def test_mx_brute_force_rational(oracle_mod, fmt, M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K + len(fmt))
+    A, SA, ea = _mx_random(rng, M, K, fmt)
+    B, SB, eb = _mx_random(rng, N, K, fmt)
+    C, S = oracle_mod.gemm_bt_mx(A, SA, B, SB, K, fmt)
+    for i in range(M):
+        for j in range(N):
+            want = sum(ea[i][k] * eb[j][k] for k in range(K))
+            assert C[i, j] == float(want)
+            assert S[i, j] == float(sum(abs(ea[i][k] * eb[j][k]) for k in range(K)))
+    rows, cols = np.array([0, M - 1, 1]), np.array([N - 1, 0, 2])
+    Ce, Se = oracle_mod.gemm_bt_mx_entries(A, SA, B, SB, K, rows, cols, fmt)
+    assert np.array_equal(Ce, C[rows, cols]) and np.array_equal(Se, S[rows, cols])
+
+
+def test_mxfp8_with_unit_scales_is_the_e4m3_gemm(oracle_mod):
+    rng = np.random.default_rng(3)
+    A = e4m3(rng.normal(0, 2, (6, 128)))
+    B = e4m3(rng.normal(0, 2, (7, 128)))
+    ones_a = np.full((6, 4), 127, np.uint8)
+    ones_b = np.full((7, 4), 127, np.uint8)
+    C, _ = oracle_mod.gemm_bt_mx(A, ones_a, B, ones_b, 128, "mxfp8")
+    R, _ = oracle_mod.gemm_bt(A, B, dtype="e4m3")
+    assert np.array_equal(C, R)
+
+
+def test_mxfp4_nibble_order_and_block_of_scale(oracle_mod):
+    # one nonzero element in A at k = 33 (high nibble of byte 16, scale block 1)
+    K = 64
+    A = np.zeros((1, K // 2), np.uint8)
+    A[0, 16] = 0x2 << 4                      # element 33 = code 2 = 1.0
+    SA = np.array([[127, 129]], np.uint8)     # block 1 scaled by 4
+    B = np.zeros((1, K // 2), np.uint8)
+    B[0, 16] = 0x7 << 4                      # element 33 = 6.0
+    SB = np.array([[127, 127]], np.uint8)
+    C, _ = oracle_mod.gemm_bt_mx(A, SA, B, SB, K, "mxfp4")
+    assert C[0, 0] == 24.0
+    with pytest.raises(ValueError):
+        oracle_mod.gemm_bt_mx(A, SA[:, :1], B, SB, K, "mxfp4")
