@@ -52,7 +52,9 @@ typedef enum {
 typedef enum {
     GEMM_BF16_OUT_F32 = 0,       /* A, B bf16; C fp32 (no rounding of the fp32 sum)   */
     GEMM_BF16_OUT_BF16 = 1,      /* A, B bf16; C bf16                                 */
-    GEMM_E4M3_OUT_BF16 = 2       /* A, B OCP fp8 e4m3fn (max 448); C bf16             */
+    GEMM_E4M3_OUT_BF16 = 2,      /* A, B OCP fp8 e4m3fn (max 448); C bf16             */
+    GEMM_MXFP8_OUT_BF16 = 3,     /* A, B MX: e4m3fn elements + E8M0 scales; C bf16    */
+    GEMM_MXFP4_OUT_BF16 = 4      /* A, B MX: e2m1 elements (2 per byte) + E8M0; C bf16 */
 } gemm_dtype;
 
 typedef enum {
@@ -169,6 +171,55 @@ typedef struct {
 int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C,
                 const gemm_epilogue_args *epi, hipStream_t stream);
 
+/*
+ * MX block-scaled operands (GEMM_MXFP8_OUT_BF16, GEMM_MXFP4_OUT_BF16).  The
+ * pages' gfx950 scaled MFMA (FlyDSL "Kernel authoring guide", section 4.3
+ * "ROCm intrinsics", MFMA instructions: mfma_scale_f32_16x16x128_f8f6f4)
+ * takes E8M0 block scales per operand with block size 32 (FlyDSL "Kernel
+ * Authoring" skill, section 6 "MFMA Integration", gfx1250 WMMA entry); the
+ * element and scale formats are those of the OCP Microscaling formats:
+ *
+ *     C[m][n] = cvt( sum_k (a(m,k) * 2^(SA[m][k/32] - 127)) * (b(n,k) * 2^(SB[n][k/32] - 127)) )
+ *
+ *   A   M x K elements row-major (MXFP8: 1 byte each; MXFP4: 2 per byte,
+ *       element 2t in the low nibble of byte t); B likewise N x K, or its
+ *       pre-shuffled image (gemm_preshuffle_b on the bytes: for MXFP4 the
+ *       64-byte k-blocks hold 128 elements);
+ *   SA  M x K/32 E8M0 bytes row-major, SB N x K/32 (0xFF is NaN).
+ * Requirements beyond gemm_plan_create's: K % 32 == 0; K * elem_bits / 8 % 64 == 0.
+ * The scales go to the kernel as an image that lets each lane fetch the scales
+ * of 4 row blocks for 4 MFMA K-slices (128 elements each) in one 16-byte load:
+ * the bytes (ceil(R/64), G, 64, 4, 4), G = ceil(ceil(K/128)/4), row-major:
+ * row quad, slice group g, lane l, 16-row block b, slice s holds
+ * S[64 quad + 16 b + l % 16][4 (4 g + s) + l / 16] (127 past the rows or K).
+ */
+
+/* gemm_bscale_image_bytes -- bytes of the image of A's (operand 0) or B's
+ * (operand 1) block scales; 0 for a non-MX plan or another operand. */
+size_t gemm_bscale_image_bytes(const gemm_plan *plan, int operand);
+
+/*
+ * gemm_preshuffle_bscale -- write the image above from R x K/32 E8M0 bytes
+ * (R = M for operand 0, N for operand 1).
+ *   scales  device pointer, R * K/32 bytes;  image  device pointer, 16-byte
+ *   aligned, gemm_bscale_image_bytes(plan, operand) bytes, not overlapping.
+ * Asynchronous on `stream`; GEMM_OK or an error (non-MX plan, bad operand,
+ * NULL or misaligned pointers, overlap).
+ */
+int gemm_preshuffle_bscale(const gemm_plan *plan, int operand, const void *scales, void *image,
+                           hipStream_t stream);
+
+/*
+ * gemm_run_mx -- C = cvt(epilogue(A * B^T)) for an MX plan.
+ *   A, B, C    as for gemm_run (B plain or pre-shuffled per the plan's layout).
+ *   A_bscale, B_bscale  device pointers to the images of SA and SB, 16-byte
+ *              aligned (gemm_preshuffle_bscale).
+ *   epi        the fused epilogue (see gemm_run_ex), or NULL.
+ * gemm_run and gemm_run_ex reject MX plans.  Asynchronous; GEMM_OK or an error.
+ */
+int gemm_run_mx(const gemm_plan *plan, const void *A, const void *A_bscale, const void *B,
+                const void *B_bscale, void *C, const gemm_epilogue_args *epi, hipStream_t stream);
+
 /* gemm_last_error -- message for the calling thread's last failure ("" if none). */
 const char *gemm_last_error(void);
 
@@ -193,6 +244,8 @@ typedef struct {
     int32_t tiles_m, tiles_n;
     int32_t group_m;         /* tile rows per raster group within one XCD             */
     int32_t split_k;         /* K slices reduced inside a workgroup (skinny kernel)   */
+    int32_t elem_bits;       /* bits per input element (16, 8 or 4); elem_bytes is
+                                elem_bits / 8, so 0 for MXFP4                          */
 } gemm_plan_info;
 
 /* gemm_plan_query -- copy the plan's decisions into *info. */

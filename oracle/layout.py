@@ -98,3 +98,28 @@ def preshuffle_src_offset(n: int, kbyte: int, N: int, kbytes: int) -> int:
     kb, rem = divmod(kbyte, 64)
     kq, byte = divmod(rem, 16)
     return (((nb * (kbytes // 64) + kb) * 4 + kq) * 16 + nr) * 16 + byte
+
+
+def bscale_image(S: np.ndarray, K: int) -> np.ndarray:
+    """Block-scale image of MX scales S (R x K/32 E8M0 bytes): the bytes
+    (ceil(R/64), G, 64, 4, 4), G = ceil(ceil(K/128)/4), where entry
+    (quad, g, lane, b, s) is S[64 quad + 16 b + lane % 16][4 (4 g + s) + lane // 16],
+    or 127 past the rows or the blocks.  Written out index by index."""
+    S = np.asarray(S, np.uint8)
+    R, kb = S.shape
+    assert kb == K // 32
+    groups = ((K + 127) // 128 + 3) // 4
+    quads = (R + 63) // 64
+    img = np.full((quads, groups, 64, 4, 4), 127, np.uint8)
+    for quad in range(quads):
+        for g in range(groups):
+            for lane in range(64):
+                for b in range(4):
+                    row = 64 * quad + 16 * b + lane % 16
+                    if row >= R:
+                        continue
+                    for s in range(4):
+                        blk = 4 * (4 * g + s) + lane // 16
+                        if blk < kb:
+                            img[quad, g, lane, b, s] = S[row, blk]
+    return img.reshape(-1)

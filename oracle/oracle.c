@@ -33,9 +33,11 @@
  *   e8m0      : OCP MX block scale, 8 exponent bits (bias 127), value
  *               2^(e-127); 0xFF is NaN.
  *
- * MX block-scaled operands (OCP Microscaling formats, block size 32; the
- * pages' gfx950 scaled MFMA, "Kernel Authoring" skill section 9 "Math
- * intrinsics" and section 5 "MX-scaled WMMA"): element k of row i counts as
+ * MX block-scaled operands (the gfx950 scaled MFMA of FlyDSL "Kernel
+ * authoring guide", section 4.3 "ROCm intrinsics", MFMA instructions; E8M0
+ * block scales with block size 32, FlyDSL "Kernel Authoring" skill, section 6
+ * "MFMA Integration", gfx1250 WMMA entry; formats as the OCP Microscaling
+ * specification defines them): element k of row i counts as
  * elem(i,k) * 2^(scale[i][k/32] - 127), the scales stored rows x K/32 bytes
  * row-major.
  *

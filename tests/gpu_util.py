@@ -13,11 +13,14 @@ import torch
 
 import tiled_gemm_amd as tg
 
-RHO = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -3}
+# MX: products of the decoded elements are exact in fp32, so only the fp32
+# accumulation (the S term) and the output rounding (2^-8) remain.
+RHO = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -3, "mxfp8": 2.0 ** -8, "mxfp4": 2.0 ** -8}
 ABS_COEF = 4e-6
 
 DTYPE_CODE = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
-              ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}
+              ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16, ("mxfp8", "bf16"): tg.GEMM_MXFP8_OUT_BF16,
+              ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16}
 
 
 def to_dev(bits: np.ndarray) -> torch.Tensor:
@@ -32,11 +35,14 @@ def _dev_f32(x):
 
 
 def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
-             scale=(1.0, 1.0), use_scale=True, stream=None, plan=None, return_plan_info=False, epi=None):
+             scale=(1.0, 1.0), use_scale=True, stream=None, plan=None, return_plan_info=False, epi=None,
+             sa_blocks=None, sb_blocks=None):
     """One C = A * B^T through gemm_plan_create / [gemm_preshuffle_b] /
     gemm_run, or gemm_run_ex when ``epi`` is given: a dict with optional
     scale_a (scalar or M values), scale_b (scalar or N values), bias (N
-    values) and kind (a name in tg.EPILOGUES).  Returns the raw bits of C as a
+    values) and kind (a name in tg.EPILOGUES).  MX dtypes take the E8M0 block
+    scales sa_blocks (M x K/32) and sb_blocks (N x K/32) and run through
+    gemm_preshuffle_bscale + gemm_run_mx.  Returns the raw bits of C as a
     numpy array (M x N)."""
     code = DTYPE_CODE[(dtype, out)]
     lay = tg.LAYOUTS[layout]
@@ -52,7 +58,23 @@ def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
         Bx = torch.empty(tg.gemm_preshuffled_b_bytes(plan.handle), dtype=torch.uint8, device="cuda")
         plan.preshuffle_b(B.data_ptr(), Bx.data_ptr(), s)
     C = torch.full((max(1, M * N * ob),), 0x5A, dtype=torch.uint8, device="cuda")
-    if epi is None:
+    if dtype.startswith("mx"):
+        e = epi or {}
+        keep = {k: _dev_f32(e[k]) for k in ("scale_a", "scale_b", "bias") if e.get(k) is not None}
+        imgs = []
+        for operand, blocks in ((0, sa_blocks), (1, sb_blocks)):
+            src = torch.from_numpy(np.ascontiguousarray(blocks, np.uint8)).cuda()
+            img = torch.empty(max(16, plan.bscale_image_bytes(operand)), dtype=torch.uint8, device="cuda")
+            plan.preshuffle_bscale(operand, src.data_ptr(), img.data_ptr(), s)
+            imgs.append((src, img))
+        plan.run_mx(A.data_ptr(), imgs[0][1].data_ptr(), Bx.data_ptr(), imgs[1][1].data_ptr(), C.data_ptr(),
+                    stream=s, scale_a=keep["scale_a"].data_ptr() if "scale_a" in keep else None,
+                    scale_a_per_row=np.ndim(e.get("scale_a")) > 0,
+                    scale_b=keep["scale_b"].data_ptr() if "scale_b" in keep else None,
+                    scale_b_per_col=np.ndim(e.get("scale_b")) > 0,
+                    bias=keep["bias"].data_ptr() if "bias" in keep else None,
+                    epilogue=tg.EPILOGUES[e.get("kind", "none")])
+    elif epi is None:
         sc = torch.tensor(scale, dtype=torch.float32, device="cuda")
         plan.run(A.data_ptr(), Bx.data_ptr(), C.data_ptr(), sc.data_ptr() if use_scale else None, s)
     else:

@@ -230,3 +230,43 @@ def test_epilogue_enum_matches_header():
         assert re.search(r"\b%s = %d\b" % (name, value), text), name
         assert getattr(tg, name) == value
     assert ctypes.sizeof(tg.gemm_epilogue_args) == 3 * 8 + 3 * 4 + 4    # 3 pointers, 3 int32, padding
+
+
+@pytest.mark.parametrize("dtype,bits", [(tg.GEMM_MXFP8_OUT_BF16, 8), (tg.GEMM_MXFP4_OUT_BF16, 4)])
+@pytest.mark.parametrize("layout", [tg.GEMM_LAYOUT_BT, tg.GEMM_LAYOUT_BT_PRESHUFFLED])
+def test_mx_plans(lib, dtype, bits, layout):
+    for M, N, K in [(8192, 8192, 8192), (32, 4096, 1024), (300, 272, 1152)]:
+        with tg.Plan(M, N, K, dtype, layout) as p:
+            info = p.info()
+            assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 256   # 4-wave pipelined
+            assert info["elem_bits"] == bits and info["elem_bytes"] == bits // 8
+            assert tg.gemm_preshuffled_b_bytes(p.handle) == N * K * bits // 8
+            groups = ((K + 127) // 128 + 3) // 4
+            assert p.bscale_image_bytes(0) == (M + 63) // 64 * groups * 1024
+            assert p.bscale_image_bytes(1) == (N + 63) // 64 * groups * 1024
+            assert p.bscale_image_bytes(2) == 0
+    with pytest.raises(tg.GemmError):
+        tg.Plan(64, 64, 80, dtype, layout)              # K % 32
+    if bits == 4:
+        with pytest.raises(tg.GemmError):
+            tg.Plan(64, 64, 96, dtype, layout)          # K/2 bytes not a multiple of 64
+
+
+def test_mx_entry_point_guards(lib):
+    A, B, C, SA, SB = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    with tg.Plan(256, 256, 256, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert lib.gemm_run(p.handle, A, B, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert "gemm_run_mx" in tg.gemm_last_error()
+        assert lib.gemm_run_ex(p.handle, A, B, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_run_mx(p.handle, A, None, B, SB, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_run_mx(p.handle, A, SA + 4, B, SB, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_bscale(p.handle, 2, SA, SB, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_bscale(p.handle, 0, None, SB, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_bscale(p.handle, 0, SA, SA + 8, None) == tg.GEMM_ERR_INVALID_ARG   # misaligned
+        assert lib.gemm_preshuffle_bscale(p.handle, 0, SA, SA + 16, None) == tg.GEMM_ERR_INVALID_ARG  # overlap
+    with tg.Plan(256, 256, 256, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert lib.gemm_run_mx(p.handle, A, SA, B, SB, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_bscale(p.handle, 0, SA, SB, None) == tg.GEMM_ERR_INVALID_ARG
+        assert p.bscale_image_bytes(0) == 0
+    with tg.Plan(0, 256, 256, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert lib.gemm_run_mx(p.handle, None, None, None, None, None, None, None) == tg.GEMM_OK

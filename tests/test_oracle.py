@@ -403,3 +403,18 @@ def test_mxfp4_nibble_order_and_block_of_scale(oracle_mod):
     assert C[0, 0] == 24.0
     with pytest.raises(ValueError):
         oracle_mod.gemm_bt_mx(A, SA[:, :1], B, SB, K, "mxfp4")
+
+
+def test_bscale_image_hand_computed_entries():
+    # R = 70 rows, K = 256: 8 blocks per row, 2 K-slices -> 1 group; 2 row quads.
+    S = (np.arange(70 * 8) % 251).astype(np.uint8).reshape(70, 8)
+    img = L.bscale_image(S, 256).reshape(2, 1, 64, 4, 4)
+    # quad 1, group 0, lane 17 (row 1 of a block, lane group 1), block 0, slice 1:
+    # row 64 + 0 + 1 = 65, K block 4 * (0 + 1) + 1 = 5
+    assert img[1, 0, 17, 0, 1] == S[65, 5]
+    # quad 0, lane 63 (row 15, group 3), block 2, slice 0: row 47, K block 3
+    assert img[0, 0, 63, 2, 0] == S[47, 3]
+    # slices 2 and 3 lie past K (only 2 slices): unit scale 127
+    assert (img[:, :, :, :, 2:] == 127).all()
+    # rows 70.. of quad 1 (block 0 lanes with l % 16 >= 6) are padding
+    assert img[1, 0, 6, 0, 0] == 127 and img[1, 0, 5, 0, 0] == S[69, 0]

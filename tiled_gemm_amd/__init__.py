@@ -25,6 +25,8 @@ GEMM_ERR_HIP = -3
 GEMM_BF16_OUT_F32 = 0
 GEMM_BF16_OUT_BF16 = 1
 GEMM_E4M3_OUT_BF16 = 2
+GEMM_MXFP8_OUT_BF16 = 3
+GEMM_MXFP4_OUT_BF16 = 4
 
 GEMM_LAYOUT_BT = 0
 GEMM_LAYOUT_BT_PRESHUFFLED = 1
@@ -38,7 +40,8 @@ GEMM_VIEW_A, GEMM_VIEW_B, GEMM_VIEW_B_SHUF, GEMM_VIEW_B_SRC, GEMM_VIEW_C, GEMM_V
 
 EXPORTS = (
     "gemm_plan_create", "gemm_plan_destroy", "gemm_preshuffled_b_bytes", "gemm_preshuffle_b",
-    "gemm_run", "gemm_run_ex", "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
+    "gemm_run", "gemm_run_ex", "gemm_bscale_image_bytes", "gemm_preshuffle_bscale", "gemm_run_mx",
+    "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
     "gemm_layout_idx2crd", "gemm_lds_swizzle", "gemm_tile_of_workgroup",
 )
 
@@ -60,7 +63,7 @@ class gemm_plan_info(ctypes.Structure):
         (f, ctypes.c_int32) for f in (
             "dtype", "layout", "elem_bytes", "out_bytes", "kernel", "tile_m", "tile_n",
             "tile_k_bytes", "threads", "lds_stages", "lds_bytes", "grid", "tiles_m", "tiles_n",
-            "group_m", "split_k")]
+            "group_m", "split_k", "elem_bits")]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -88,6 +91,9 @@ def load() -> ctypes.CDLL:
         "gemm_preshuffle_b": (c_int, [vp, vp, vp, vp]),
         "gemm_run": (c_int, [vp, vp, vp, vp, vp, vp]),
         "gemm_run_ex": (c_int, [vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp]),
+        "gemm_bscale_image_bytes": (ctypes.c_size_t, [vp, c_int]),
+        "gemm_preshuffle_bscale": (c_int, [vp, c_int, vp, vp, vp]),
+        "gemm_run_mx": (c_int, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp]),
         "gemm_last_error": (ctypes.c_char_p, []),
         "gemm_plan_query": (c_int, [vp, ctypes.POINTER(gemm_plan_info)]),
         "gemm_plan_layout": (c_int, [vp, c_int, p32, p64, p64]),
@@ -152,6 +158,22 @@ def gemm_run_ex(plan: int, A: int, B: int, C: int, scale_a: int | None = None, s
     _check(load().gemm_run_ex(plan, A, B, C, ctypes.byref(epi), stream), "gemm_run_ex")
 
 
+def gemm_bscale_image_bytes(plan: int, operand: int) -> int:
+    return int(load().gemm_bscale_image_bytes(plan, operand))
+
+
+def gemm_preshuffle_bscale(plan: int, operand: int, scales: int, image: int, stream: int = 0) -> None:
+    _check(load().gemm_preshuffle_bscale(plan, operand, scales, image, stream), "gemm_preshuffle_bscale")
+
+
+def gemm_run_mx(plan: int, A: int, A_bscale: int, B: int, B_bscale: int, C: int, scale_a: int | None = None,
+                scale_a_per_row: bool = False, scale_b: int | None = None, scale_b_per_col: bool = False,
+                bias: int | None = None, epilogue: int = GEMM_EPI_NONE, stream: int = 0) -> None:
+    epi = gemm_epilogue_args(scale_a or None, scale_b or None, bias or None, int(scale_a_per_row),
+                             int(scale_b_per_col), epilogue)
+    _check(load().gemm_run_mx(plan, A, A_bscale, B, B_bscale, C, ctypes.byref(epi), stream), "gemm_run_mx")
+
+
 def gemm_plan_query(plan: int) -> dict:
     info = gemm_plan_info()
     _check(load().gemm_plan_query(plan, ctypes.byref(info)), "gemm_plan_query")
@@ -197,7 +219,8 @@ def gemm_tile_of_workgroup(plan: int, wg: int):
 
 # ---------------------------------------------------------------- conveniences
 
-DTYPES = {"bf16_f32": GEMM_BF16_OUT_F32, "bf16": GEMM_BF16_OUT_BF16, "e4m3": GEMM_E4M3_OUT_BF16}
+DTYPES = {"bf16_f32": GEMM_BF16_OUT_F32, "bf16": GEMM_BF16_OUT_BF16, "e4m3": GEMM_E4M3_OUT_BF16,
+          "mxfp8": GEMM_MXFP8_OUT_BF16, "mxfp4": GEMM_MXFP4_OUT_BF16}
 LAYOUTS = {"bt": GEMM_LAYOUT_BT, "bt_preshuffled": GEMM_LAYOUT_BT_PRESHUFFLED}
 
 
@@ -205,6 +228,7 @@ class Plan:
     """Owns one plan handle; ``with Plan(...) as p:`` destroys it on exit."""
 
     def __init__(self, M: int, N: int, K: int, dtype: int, layout: int):
+        self.handle = 0                      # set before create, which may raise
         self.handle = gemm_plan_create(M, N, K, dtype, layout)
 
     def close(self):
@@ -230,6 +254,15 @@ class Plan:
 
     def run(self, A: int, B: int, C: int, scale: int | None = None, stream: int = 0) -> None:
         gemm_run(self.handle, A, B, C, scale, stream)
+
+    def bscale_image_bytes(self, operand: int) -> int:
+        return gemm_bscale_image_bytes(self.handle, operand)
+
+    def preshuffle_bscale(self, operand: int, scales: int, image: int, stream: int = 0) -> None:
+        gemm_preshuffle_bscale(self.handle, operand, scales, image, stream)
+
+    def run_mx(self, A: int, A_bscale: int, B: int, B_bscale: int, C: int, stream: int = 0, **epi) -> None:
+        gemm_run_mx(self.handle, A, A_bscale, B, B_bscale, C, stream=stream, **epi)
 
     def run_ex(self, A: int, B: int, C: int, stream: int = 0, **epi) -> None:
         """gemm_run_ex; keyword arguments as for the module-level gemm_run_ex."""

@@ -46,9 +46,35 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxRowBytes = int64_t(1) << 23;    // 256 rows stay below 2^31 bytes of buffer range
 constexpr int kLdsLimit = 160 * 1024;                   // gfx950 LDS per workgroup
 
-int elem_bytes_of(int dtype) { return dtype == GEMM_E4M3_OUT_BF16 ? 1 : 2; }
+bool is_mx(int dtype) { return dtype == GEMM_MXFP8_OUT_BF16 || dtype == GEMM_MXFP4_OUT_BF16; }
+int elem_bits_of(int dtype)
+{
+    switch (dtype) {
+    case GEMM_E4M3_OUT_BF16:
+    case GEMM_MXFP8_OUT_BF16:
+        return 8;
+    case GEMM_MXFP4_OUT_BF16:
+        return 4;
+    default:
+        return 16;
+    }
+}
 int out_bytes_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? 4 : 2; }
-int elem_of(int dtype) { return dtype == GEMM_E4M3_OUT_BF16 ? tg::kFp8 : tg::kBf16; }
+int elem_of(int dtype)
+{
+    switch (dtype) {
+    case GEMM_E4M3_OUT_BF16:
+        return tg::kFp8;
+    case GEMM_MXFP8_OUT_BF16:
+        return tg::kMx8;
+    case GEMM_MXFP4_OUT_BF16:
+        return tg::kMx4;
+    default:
+        return tg::kBf16;
+    }
+}
+// 4-slice groups of K (one MFMA K-slice is 128 elements).
+int64_t scale_groups(int64_t K) { return ((K + 127) / 128 + 3) / 4; }
 int out_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? tg::kOutF32 : tg::kOutBf16; }
 
 // Static tile table: the first entry whose predicate holds.  An optional
@@ -59,6 +85,16 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     const tg::TiledVariant *v = tg::tiled_variants(&n);
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
     const int elem = elem_of(I.dtype), out = out_of(I.dtype);
+    if (is_mx(I.dtype)) {
+        // MX operands: only the pipelined 256 x 256 kernel (any M, N: tails
+        // are masked).
+        int nb = 0;
+        const tg::TiledVariant *b = tg::pipe_variants(&nb);
+        for (int i = 0; i < nb; ++i)
+            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre)
+                return &b[i];
+        return nullptr;
+    }
     int want_bm = 0, want_bn = 0;
     if (const char *e = getenv("TGEMM_TILE"))
         if (sscanf(e, "%dx%d", &want_bm, &want_bn) != 2)
@@ -96,7 +132,7 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
 
 const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
 {
-    if (I.layout != GEMM_LAYOUT_BT || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE"))
+    if (I.layout != GEMM_LAYOUT_BT || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") || is_mx(I.dtype))
         return nullptr;
     const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
     int n = 0;
@@ -190,7 +226,7 @@ const char *gemm_last_error(void) { return g_last_error.c_str(); }
 
 gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout)
 {
-    if (dtype < GEMM_BF16_OUT_F32 || dtype > GEMM_E4M3_OUT_BF16) {
+    if (dtype < GEMM_BF16_OUT_F32 || dtype > GEMM_MXFP4_OUT_BF16) {
         fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
         return nullptr;
     }
@@ -207,8 +243,12 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "size above 2^30");
         return nullptr;
     }
-    const int eb = elem_bytes_of(dtype), ob = out_bytes_of(dtype);
-    const int64_t kbytes = K * eb;
+    const int ebits = elem_bits_of(dtype), ob = out_bytes_of(dtype);
+    const int64_t kbytes = K * ebits / 8;
+    if (is_mx(dtype) && K % 32 != 0) {
+        fail(GEMM_ERR_UNSUPPORTED, "K=%lld must be a multiple of 32 (MX block)", (long long)K);
+        return nullptr;
+    }
     if (N % 16 != 0) {
         fail(GEMM_ERR_UNSUPPORTED, "N=%lld must be a multiple of 16", (long long)N);
         return nullptr;
@@ -242,7 +282,8 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     I.K = K;
     I.dtype = dtype;
     I.layout = layout;
-    I.elem_bytes = eb;
+    I.elem_bytes = ebits / 8;
+    I.elem_bits = ebits;
     I.out_bytes = ob;
     p->kbytes = kbytes;
     p->k_tiles = (int32_t)((kbytes + tg::kTileKBytes - 1) / tg::kTileKBytes);
@@ -433,7 +474,7 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
 namespace {
 
 int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const tg::EpiArgs &epi,
-             hipStream_t stream)
+             hipStream_t stream, const void *sa_img = nullptr, const void *sb_img = nullptr)
 {
     if (!plan)
         return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
@@ -483,6 +524,9 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.tiles_m = I.tiles_m;
         a.tiles_n = I.tiles_n;
         a.group_m = I.group_m;
+        a.sa_img = (const uint8_t *)sa_img;
+        a.sb_img = (const uint8_t *)sb_img;
+        a.s_groups = (int32_t)scale_groups(I.K);
         e = plan->tiled->launch(a, stream);
     }
     if (e != hipSuccess)
@@ -493,6 +537,44 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// The epilogue description -> kernel arguments (GEMM_OK or an error).
+int epi_from(const gemm_epilogue_args *epi, tg::EpiArgs *e)
+{
+    *e = tg::EpiArgs{};
+    if (!epi)
+        return GEMM_OK;
+    if (epi->epilogue < GEMM_EPI_NONE || epi->epilogue > GEMM_EPI_BIAS_GELU)
+        return fail(GEMM_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi->epilogue);
+    if ((epi->scale_a_per_row != 0 && epi->scale_a_per_row != 1) ||
+        (epi->scale_b_per_col != 0 && epi->scale_b_per_col != 1))
+        return fail(GEMM_ERR_INVALID_ARG, "scale_a_per_row and scale_b_per_col must be 0 or 1");
+    const bool wants_bias = epi->epilogue != GEMM_EPI_NONE;
+    if (wants_bias && !epi->bias)
+        return fail(GEMM_ERR_INVALID_ARG, "the bias epilogues need a bias vector");
+    if (!wants_bias && epi->bias)
+        return fail(GEMM_ERR_INVALID_ARG, "bias given with GEMM_EPI_NONE");
+    if ((epi->scale_a && !aligned(epi->scale_a, 4)) ||
+        (epi->scale_b && !aligned(epi->scale_b, epi->scale_b_per_col ? 16 : 4)) ||
+        (epi->bias && !aligned(epi->bias, 16)))
+        return fail(GEMM_ERR_INVALID_ARG,
+                    "scale_a must be 4-byte aligned; per-column scale_b and bias 16-byte aligned");
+    e->sa = epi->scale_a;
+    e->sb = epi->scale_b;
+    e->bias = epi->bias;
+    e->sa_rows = epi->scale_a_per_row;
+    e->sb_cols = epi->scale_b_per_col;
+    static const int kAct[] = {tg::kActNone, tg::kActNone, tg::kActRelu, tg::kActSilu, tg::kActGelu};
+    e->act = kAct[epi->epilogue];
+    return GEMM_OK;
+}
+
+int reject_mx(const gemm_plan *plan)
+{
+    if (plan && is_mx(plan->info.dtype))
+        return fail(GEMM_ERR_INVALID_ARG, "MX plans run through gemm_run_mx (block scales)");
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -500,6 +582,8 @@ extern "C" {
 int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const float *scale,
              hipStream_t stream)
 {
+    if (int rc = reject_mx(plan))
+        return rc;
     if (scale && !aligned(scale, 4))
         return fail(GEMM_ERR_INVALID_ARG, "scale must be 4-byte aligned");
     tg::EpiArgs e{};
@@ -512,32 +596,76 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, const
 int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C, const gemm_epilogue_args *epi,
                 hipStream_t stream)
 {
-    tg::EpiArgs e{};
-    if (epi) {
-        if (epi->epilogue < GEMM_EPI_NONE || epi->epilogue > GEMM_EPI_BIAS_GELU)
-            return fail(GEMM_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi->epilogue);
-        if ((epi->scale_a_per_row != 0 && epi->scale_a_per_row != 1) ||
-            (epi->scale_b_per_col != 0 && epi->scale_b_per_col != 1))
-            return fail(GEMM_ERR_INVALID_ARG, "scale_a_per_row and scale_b_per_col must be 0 or 1");
-        const bool wants_bias = epi->epilogue != GEMM_EPI_NONE;
-        if (wants_bias && !epi->bias)
-            return fail(GEMM_ERR_INVALID_ARG, "the bias epilogues need a bias vector");
-        if (!wants_bias && epi->bias)
-            return fail(GEMM_ERR_INVALID_ARG, "bias given with GEMM_EPI_NONE");
-        if ((epi->scale_a && !aligned(epi->scale_a, 4)) ||
-            (epi->scale_b && !aligned(epi->scale_b, epi->scale_b_per_col ? 16 : 4)) ||
-            (epi->bias && !aligned(epi->bias, 16)))
-            return fail(GEMM_ERR_INVALID_ARG,
-                        "scale_a must be 4-byte aligned; per-column scale_b and bias 16-byte aligned");
-        e.sa = epi->scale_a;
-        e.sb = epi->scale_b;
-        e.bias = epi->bias;
-        e.sa_rows = epi->scale_a_per_row;
-        e.sb_cols = epi->scale_b_per_col;
-        static const int kAct[] = {tg::kActNone, tg::kActNone, tg::kActRelu, tg::kActSilu, tg::kActGelu};
-        e.act = kAct[epi->epilogue];
-    }
+    if (int rc = reject_mx(plan))
+        return rc;
+    tg::EpiArgs e;
+    if (int rc = epi_from(epi, &e))
+        return rc;
     return run_impl(plan, A, B, C, e, stream);
+}
+
+size_t gemm_bscale_image_bytes(const gemm_plan *plan, int operand)
+{
+    if (!plan || !is_mx(plan->info.dtype) || (operand != 0 && operand != 1))
+        return 0;
+    const int64_t rows = operand ? plan->info.N : plan->info.M;
+    return (size_t)((rows + 63) / 64) * (size_t)scale_groups(plan->info.K) * 1024u;
+}
+
+int gemm_preshuffle_bscale(const gemm_plan *plan, int operand, const void *scales, void *image, hipStream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
+    if (!is_mx(plan->info.dtype))
+        return fail(GEMM_ERR_INVALID_ARG, "block scales belong to MX plans");
+    if (operand != 0 && operand != 1)
+        return fail(GEMM_ERR_INVALID_ARG, "operand must be 0 (A) or 1 (B)");
+    const size_t bytes = gemm_bscale_image_bytes(plan, operand);
+    const int64_t rows = operand ? plan->info.N : plan->info.M;
+    const size_t src_bytes = (size_t)rows * (size_t)(plan->info.K / 32);
+    if (bytes == 0 || src_bytes == 0) {
+        ok();
+        return GEMM_OK;
+    }
+    if (!scales || !image)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL scales or image");
+    if (!aligned(image, 16))
+        return fail(GEMM_ERR_INVALID_ARG, "image must be 16-byte aligned");
+    if (overlap(scales, src_bytes, image, bytes))
+        return fail(GEMM_ERR_INVALID_ARG, "image overlaps the scales");
+    if (int rc = check_device())
+        return rc;
+    tg::BscaleArgs a{};
+    a.src = (const uint8_t *)scales;
+    a.dst = (uint8_t *)image;
+    a.rows = (int32_t)rows;
+    a.kblocks = (int32_t)(plan->info.K / 32);
+    a.groups = (int32_t)scale_groups(plan->info.K);
+    a.quads = (int32_t)((rows + 63) / 64);
+    const hipError_t e = tg::launch_bscale_image(a, stream);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "block-scale image launch: %s", hipGetErrorString(e));
+    ok();
+    return GEMM_OK;
+}
+
+int gemm_run_mx(const gemm_plan *plan, const void *A, const void *A_bscale, const void *B, const void *B_bscale,
+                void *C, const gemm_epilogue_args *epi, hipStream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
+    if (!is_mx(plan->info.dtype))
+        return fail(GEMM_ERR_INVALID_ARG, "gemm_run_mx needs an MX plan");
+    if (plan->info.M && plan->info.N && plan->info.K) {
+        if (!A_bscale || !B_bscale)
+            return fail(GEMM_ERR_INVALID_ARG, "NULL block-scale image");
+        if (!aligned(A_bscale, 16) || !aligned(B_bscale, 16))
+            return fail(GEMM_ERR_INVALID_ARG, "block-scale images must be 16-byte aligned");
+    }
+    tg::EpiArgs e;
+    if (int rc = epi_from(epi, &e))
+        return rc;
+    return run_impl(plan, A, B, C, e, stream, A_bscale, B_bscale);
 }
 
 }  // extern "C"

@@ -131,6 +131,41 @@ __device__ inline void mfma_fp8x8_a(f32x4 &acc, i32x8 x, i32x8 y)
     asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
 }
 
+// MX block-scaled MFMA with the accumulator pinned to AGPRs:
+// D += (X * 2^(sx - 127)) * (Y * 2^(sy - 127))^T, sx and sy byte BYTE of the
+// lane's scale registers (each lane's scale covers its 32 K elements).
+// mx8: e4m3 operands (8 VGPRs); mx4: e2m1 operands (4 VGPRs; format fields 4).
+#define TG_MX_ASM(LO, HI, TAIL)                                                                 \
+    "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #LO "," #LO ",0] "     \
+    "op_sel_hi:[" #HI "," #HI ",0]" TAIL
+template <int BYTE>
+__device__ inline void mfma_mx8_a(f32x4 &acc, i32x8 x, i32x8 y, uint32_t sx, uint32_t sy)
+{
+    static_assert(BYTE >= 0 && BYTE < 4, "scale byte");
+    if constexpr (BYTE == 0)
+        asm volatile(TG_MX_ASM(0, 0, "") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 1)
+        asm volatile(TG_MX_ASM(1, 0, "") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 2)
+        asm volatile(TG_MX_ASM(0, 1, "") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else
+        asm volatile(TG_MX_ASM(1, 1, "") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+}
+template <int BYTE>
+__device__ inline void mfma_mx4_a(f32x4 &acc, u32x4 x, u32x4 y, uint32_t sx, uint32_t sy)
+{
+    static_assert(BYTE >= 0 && BYTE < 4, "scale byte");
+    if constexpr (BYTE == 0)
+        asm volatile(TG_MX_ASM(0, 0, " cbsz:4 blgp:4") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 1)
+        asm volatile(TG_MX_ASM(1, 0, " cbsz:4 blgp:4") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 2)
+        asm volatile(TG_MX_ASM(0, 1, " cbsz:4 blgp:4") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else
+        asm volatile(TG_MX_ASM(1, 1, " cbsz:4 blgp:4") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+}
+#undef TG_MX_ASM
+
 // 64 wait states: longer than any MFMA's result latency.
 __device__ inline void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }
 

@@ -80,7 +80,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     constexpr int BP_WTM = Cfg::WTM, BP_WTN = Cfg::WTN;
     // Fragment stream of one step: bf16 -> 2 sub-steps x 16 row blocks, one
     // 16-byte read each; fp8 -> 16 row blocks, two reads (chunks q, q+4).
-    constexpr int NG = ELEM == kBf16 ? 2 * BP_FM : BP_FM;   // groups (4 MFMAs each)
+    // WIDE: one 128-byte MFMA operand per block and step (fp8, MX e4m3);
+    // otherwise two 64-byte halves (bf16, MX e2m1).
+    constexpr bool WIDE = ELEM == kFp8 || ELEM == kMx8;
+    constexpr bool MX = ELEM == kMx8 || ELEM == kMx4;
+    constexpr int NG = WIDE ? BP_FM : 2 * BP_FM;            // groups (FN MFMAs each)
+    static_assert(!MX || (ACCA && ADMA && BP_WTM % 64 == 0 && BP_WTN % 64 == 0),
+                  "MX operands run on the AGPR-accumulator kernel, whole 64-row scale quads per wave");
     static_assert(PD >= 1 && PD < NG / 2, "prefetch distance");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
 
@@ -158,13 +164,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     for (int j = 0; j < BP_FN; ++j)
         voffB[j] = BPRE ? (uint32_t)(wn * BP_FN + j) * 16u * kb + (uint32_t)l * 16u
                         : (uint32_t)((wn * BP_FN + j) * 16 + r16) * kb + (uint32_t)q * kChunkBytes;
+    // A half-filled last step (K bytes 0..63 valid): half 1 is the missing part.
+    auto b_keep = [&](bool beyond, bool part, int h) { return !beyond & ((h == 0) | !part); };
     u32x4 bq[2][BP_FN][2];
     auto issue_b_one = [&](int kt, auto set_c, int j, int h) {
         constexpr int S = decltype(set_c)::value;
         const bool beyond = kt >= nk;
         const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
-        const bool keep = !beyond & ((h == 0) | !part);
-        bq[S][j][h] = buf_load16(rB, keep_or_oob(keep, voffB[j] + (uint32_t)h * kBHalf), (uint32_t)kt * kBStep);
+        bq[S][j][h] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, h), voffB[j] + (uint32_t)h * kBHalf),
+                                 (uint32_t)kt * kBStep);
         issue_fence();
     };
     auto issue_b = [&](int kt, auto set_c) {
@@ -174,8 +182,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         const uint32_t soff = (uint32_t)kt * kBStep;
 #pragma unroll
         for (int j = 0; j < BP_FN; ++j) {
-            bq[S][j][0] = buf_load16(rB, keep_or_oob(!beyond, voffB[j]), soff);
-            bq[S][j][1] = buf_load16(rB, keep_or_oob(!beyond & !part, voffB[j] + kBHalf), soff);
+            bq[S][j][0] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, 0), voffB[j]), soff);
+            bq[S][j][1] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, 1), voffB[j] + kBHalf), soff);
         }
         issue_fence();
     };
@@ -188,28 +196,81 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- fragment stream.  Group g of a step reads A row block g % FM at
-    // chunk (g / FM) * 4 + q (bf16) or chunks q and q + 4 (fp8).
-    using FragT = typename std::conditional<ELEM == kFp8, i32x8, u32x4>::type;
+    // chunk (g / FM) * 4 + q (bf16, MX e2m1) or chunks q and q + 4 (fp8, MX
+    // e4m3: the 16x16x128 e4m3 operand's own layout, in which lane group q
+    // holds K bytes 16 q .. +15 and 64 + 16 q .. +15 of the slice while the
+    // scale byte of lane group q serves K block q, elements 32 q .. 32 q + 31).
+    using FragT = typename std::conditional<WIDE, i32x8, u32x4>::type;
     FragT fa[NG];
     auto frag_addr = [&](int stage, int g, int half) -> const uint8_t * {
         const int i = g % BP_FM;
-        const int c = ELEM == kBf16 ? (g / BP_FM) * 4 + q : half * 4 + q;
+        const int c = !WIDE ? (g / BP_FM) * 4 + q : half * 4 + q;
         const int row = wm * BP_WTM + i * 16 + r16;
         return lds + stage * BP_STAGE + row * kTileKBytes + swz_chunk(row, c) * kChunkBytes;
     };
     auto load_frag = [&](int stage, int g) {
         const u32x4 lo = lds_load16(frag_addr(stage, g, 0));
-        if constexpr (ELEM == kFp8)
+        if constexpr (WIDE)
             fa[g] = join32(lo, lds_load16(frag_addr(stage, g, 1)));
         else
             fa[g] = lo;
     };
-    auto mma_group = [&](int g, auto set_c) {
+
+    // ---- MX block scales (see BscaleArgs): one 16-byte load per lane brings
+    // the scales of 4 row blocks for the 4 K-slices of a group; "cur" serves
+    // the current group, "nxt" is loaded one group ahead.  Slices: MX e4m3 one
+    // per step (4 steps per group), MX e2m1 two per step (2 steps per group).
+    constexpr int SPG = ELEM == kMx8 ? 4 : 2;
+    constexpr int SQA = MX ? BP_FM / 4 : 1, SQB = MX ? BP_FN / 4 : 1;
+    constexpr int SL = MX ? SQA + SQB : 0;                    // scale loads per group
+    u32x4 scA[SQA], scB[SQB], scA_n[SQA], scB_n[SQB];
+    const int G = p.s_groups;
+    const auto rSA = make_rsrc(p.sa_img, (uint32_t)((p.M + 63) / 64) * (uint32_t)G * 1024u);
+    const auto rSB = make_rsrc(p.sb_img, (uint32_t)((p.N + 63) / 64) * (uint32_t)G * 1024u);
+    const int qa0 = (m0 + wm * BP_WTM) / 64, qb0 = (n0 + wn * BP_WTN) / 64;
+    auto issue_scales = [&](int g2) {
+        const bool in = g2 < G;              // past the last group: out of range (not the next quad)
+#pragma unroll
+        for (int t = 0; t < SQA; ++t)
+            scA_n[t] = buf_load16(rSA, keep_or_oob(in, ((uint32_t)(qa0 + t) * (uint32_t)G + (uint32_t)g2) * 1024u +
+                                                           (uint32_t)l * 16u), 0);
+#pragma unroll
+        for (int t = 0; t < SQB; ++t)
+            scB_n[t] = buf_load16(rSB, keep_or_oob(in, ((uint32_t)(qb0 + t) * (uint32_t)G + (uint32_t)g2) * 1024u +
+                                                           (uint32_t)l * 16u), 0);
+        issue_fence();
+    };
+    // The scaled MFMA on block (i, j) with the scale byte of K-slice `byte`
+    // of the current group (the switch folds away: every index is a constant
+    // after unrolling).
+    auto mfma_mx = [&](int i, int j, auto bx, auto ay, int byte) {
+        const uint32_t sx = scB[j / 4][j % 4], sy = scA[i / 4][i % 4];
+        switch (byte) {
+        case 0:
+            if constexpr (ELEM == kMx8) mfma_mx8_a<0>(acc[i][j], bx, ay, sx, sy); else mfma_mx4_a<0>(acc[i][j], bx, ay, sx, sy);
+            break;
+        case 1:
+            if constexpr (ELEM == kMx8) mfma_mx8_a<1>(acc[i][j], bx, ay, sx, sy); else mfma_mx4_a<1>(acc[i][j], bx, ay, sx, sy);
+            break;
+        case 2:
+            if constexpr (ELEM == kMx8) mfma_mx8_a<2>(acc[i][j], bx, ay, sx, sy); else mfma_mx4_a<2>(acc[i][j], bx, ay, sx, sy);
+            break;
+        default:
+            if constexpr (ELEM == kMx8) mfma_mx8_a<3>(acc[i][j], bx, ay, sx, sy); else mfma_mx4_a<3>(acc[i][j], bx, ay, sx, sy);
+            break;
+        }
+    };
+    auto mma_group = [&](int g, auto set_c, auto gp_c) {
         constexpr int S = decltype(set_c)::value;
+        constexpr int GP = decltype(gp_c)::value;            // step position in its scale group
         const int i = g % BP_FM;
 #pragma unroll
         for (int j = 0; j < BP_FN; ++j) {
-            if constexpr (ELEM == kBf16 && ACCA)
+            if constexpr (ELEM == kMx8)
+                mfma_mx(i, j, join32(bq[S][j][0], bq[S][j][1]), fa[g], GP);
+            else if constexpr (ELEM == kMx4)
+                mfma_mx(i, j, bq[S][j][g / BP_FM], fa[g], 2 * GP + g / BP_FM);
+            else if constexpr (ELEM == kBf16 && ACCA)
                 mfma_bf16_a(acc[i][j], bq[S][j][g / BP_FM], fa[g]);
             else if constexpr (ELEM == kBf16)
                 acc[i][j] = mfma_bf16(bq[S][j][g / BP_FM], fa[g], acc[i][j]);
@@ -230,10 +291,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     // them before the ds_write; the barrier then needs no vmcnt, and the LDS
     // stores of the previous barrier are covered by waiting until at most the
     // fragment reads issued since remain (LDS operations retire in order).
+    // MX: the scale loads of a group are issued at the start of its first step
+    // (before that step's B loads), so they add SL loads behind A tile k+1 for
+    // every group start among steps k-(NS-3) .. k.
     constexpr int kVmStart = BP_AR;
-    constexpr int kVmBarrier = (NS - 2) * BP_BR + (NS - 3) * BP_AR;
-    constexpr int kLgkmBarrier = PD * (ELEM == kFp8 ? 2 : 1);
-    static_assert(kVmBarrier < 64, "vmcnt is 6 bits");
+    constexpr auto scale_starts = [](int gp) {
+        int n = 0;
+        for (int d = 0; d <= NS - 3; ++d)
+            n += (((gp - d) % SPG + SPG) % SPG) == 0;
+        return n;
+    };
+    constexpr int kVmBarrier0 = (NS - 2) * BP_BR + (NS - 3) * BP_AR;
+    static_assert(kVmBarrier0 + SL * (NS - 2) < 64, "vmcnt is 6 bits");
+    constexpr int kLgkmBarrier = PD * (WIDE ? 2 : 1);
     auto wait_vm = [&](auto n_c) {
         constexpr int n = decltype(n_c)::value;
         __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | (n & 0xF) | ((n >> 4) << 14));
@@ -244,12 +314,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One step.  Set CUR holds B(kt); set 1-CUR receives B(kt+1).
-    auto step = [&](int kt, auto cur_c) {
+    // One step.  Set CUR holds B(kt); set 1-CUR receives B(kt+1).  GP: the
+    // step's position in its scale group (MX).
+    auto step = [&](int kt, auto cur_c, auto gp_c) {
         constexpr int CUR = decltype(cur_c)::value;
+        constexpr int GP = decltype(gp_c)::value;
+        constexpr int kVmBar = kVmBarrier0 + SL * scale_starts(GP);
         const int st = kt % NS;
         wait_vm(ic<kVmStart>{});
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MX && GP == 0) {
+#pragma unroll
+            for (int t = 0; t < SQA; ++t)
+                scA[t] = scA_n[t];
+#pragma unroll
+            for (int t = 0; t < SQB; ++t)
+                scB[t] = scB_n[t];
+            issue_scales(kt / SPG + 1);
+        }
         if constexpr (!(SPREAD && ADMA))
             issue_b(kt + 1, ic<1 - CUR>{});
 #pragma unroll
@@ -266,7 +348,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                 } else {
                     const int go = g - (NG - PD);
                     if (go == 0) {
-                        wait_vm(ic<kVmBarrier>{});
+                        wait_vm(ic<kVmBar>{});
                         barrier();
                     }
 #pragma unroll
@@ -275,7 +357,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                 }
             } else if (g == NG - PD) {
                 if constexpr (ADMA) {
-                    wait_vm(ic<kVmBarrier>{});
+                    wait_vm(ic<kVmBar>{});
                     barrier();
                     issue_a(kt + NS - 1);
                 } else {
@@ -291,7 +373,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                 load_frag(st, g + PD);
             else
                 load_frag((kt + 1) % NS, g + PD - NG);
-            mma_group(g, ic<CUR>{});
+            mma_group(g, ic<CUR>{}, ic<GP>{});
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -299,6 +381,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     // ---- prologue: the loads of virtual steps 1-NS .. -1 (B(k+1) only for
     // k+1 >= 0, so the first barriers wait for everything), then the first
     // fragments.
+    if constexpr (MX)
+        issue_scales(0);
     for (int v = 1 - NS; v < 0; ++v) {
         if (v == -1)
             issue_b(0, ic<0>{});
@@ -315,11 +399,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
 #pragma unroll
     for (int g = 0; g < PD; ++g)
         load_frag(0, g);
-    // Steps run in pairs; when nk is odd the last one is a phantom step whose
-    // operands are all out of range, i.e. zeros, and adds exact zeros.
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, ic<0>{});
-        step(kt + 1, ic<1>{});
+    // Steps run in pairs (MX e4m3: in fours, one scale group); steps past nk
+    // are phantom steps whose operands are all out of range, i.e. zeros, and
+    // add exact zeros.
+    if constexpr (ELEM == kMx8) {
+        for (int kt = 0; kt < nk; kt += 4) {
+            step(kt, ic<0>{}, ic<0>{});
+            step(kt + 1, ic<1>{}, ic<1>{});
+            step(kt + 2, ic<0>{}, ic<2>{});
+            step(kt + 3, ic<1>{}, ic<3>{});
+        }
+    } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, ic<0>{}, ic<0>{});
+            step(kt + 1, ic<1>{}, ic<1>{});
+        }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if constexpr (ACCA)
@@ -376,6 +470,11 @@ static const TiledVariant kPipe[] = {
     TG_PIPE_S(kBf16, kOutF32, false, 1, 4, 4, 12, true, true),
     TG_PIPE_S(kFp8, kOutBf16, false, 1, 4, 4, 6, true, true),
     TG_PIPE_S(kFp8, kOutBf16, true, 1, 4, 4, 6, true, true),
+    // MX block-scaled operands (4 waves, AGPR accumulators)
+    TG_PIPE_S(kMx8, kOutBf16, true, 1, 4, 4, 3, true, true),
+    TG_PIPE_S(kMx8, kOutBf16, false, 1, 4, 4, 3, true, true),
+    TG_PIPE_S(kMx4, kOutBf16, true, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kMx4, kOutBf16, false, 1, 4, 4, 12, true, true),
     // sweep alternatives
     TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),           // 12: loads in bursts
     TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 5, true, true),   // 13

@@ -9,7 +9,9 @@
 
 namespace tg {
 
-enum Elem { kBf16 = 0, kFp8 = 1 };
+// kMx8 / kMx4: MX block-scaled e4m3 / e2m1 operands, one E8M0 scale per 32
+// elements along K.
+enum Elem { kBf16 = 0, kFp8 = 1, kMx8 = 2, kMx4 = 3 };
 enum Out { kOutF32 = 0, kOutBf16 = 1 };
 
 // Epilogue operands (device pointers): C = act((acc * s_a) * s_b + bias).
@@ -33,6 +35,28 @@ struct TiledArgs {
     int32_t k_tiles;        // ceil(kbytes / 128)
     int32_t tail_bytes;     // valid bytes of the last K tile: 64 or 128
     int32_t grid, tiles_m, tiles_n, group_m;
+    // MX operands only: the block-scale images of A and B (see
+    // BscaleArgs) and their number of 4-slice groups along K.
+    const uint8_t *sa_img;
+    const uint8_t *sb_img;
+    int32_t s_groups;
+};
+
+// Block-scale image of an MX operand with R rows: the bytes
+// (ceil(R / 64), G, 64, 4, 4) in row-major order -- row quad (64 rows), group
+// of 4 MFMA K-slices (128 elements each), lane l, 16-row block b of the quad,
+// slice s of the group -- holding the E8M0 scale of row 64 quad + 16 b + l % 16
+// for the 32 elements of slice 4 g + s that lane l feeds the MFMA
+// (elements 32 (l / 16) .. +31 of the slice); 127 (unit scale) past the rows
+// or the blocks.  One 16-byte load per lane brings a wave the scales of 4 row
+// blocks for 4 K-slices.
+struct BscaleArgs {
+    const uint8_t *src;     // R x (K / 32) E8M0 bytes, row-major
+    uint8_t *dst;           // the image
+    int32_t rows;           // R
+    int32_t kblocks;        // K / 32
+    int32_t groups;         // G = ceil(ceil(K / 128) / 4)
+    int32_t quads;          // ceil(R / 64)
 };
 
 struct SkinnyArgs {
@@ -81,5 +105,6 @@ const TiledVariant *tiled_variants(int *count);
 const TiledVariant *pipe_variants(int *count);
 const SkinnyVariant *skinny_variants(int *count);
 hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
+hipError_t launch_bscale_image(const BscaleArgs &, hipStream_t);
 
 }  // namespace tg

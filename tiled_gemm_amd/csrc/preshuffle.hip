@@ -45,4 +45,41 @@ hipError_t launch_preshuffle(const PreshuffleArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Block-scale image of an MX operand (layout in BscaleArgs): thread t writes
+// the 16 bytes of lane t % 64 of (row quad, group) t / 64.
+__global__ __launch_bounds__(256) void bscale_image_kernel(const BscaleArgs p)
+{
+    const int64_t total = (int64_t)p.quads * p.groups * 64;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(t & 63);
+        const int64_t qg = t >> 6;
+        const int g = (int)(qg % p.groups);
+        const int64_t quad = qg / p.groups;
+        uint32_t word[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t row = quad * 64 + b * 16 + (lane & 15);
+            uint32_t w = 0;
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                const int64_t blk = (int64_t)(4 * g + sl) * 4 + (lane >> 4);   // 32-element block along K
+                const uint32_t v = (row < p.rows && blk < p.kblocks) ? p.src[row * p.kblocks + blk] : 127u;
+                w |= v << (8 * sl);
+            }
+            word[b] = w;
+        }
+        *(u32x4 *)(p.dst + t * 16) = u32x4{word[0], word[1], word[2], word[3]};
+    }
+}
+
+hipError_t launch_bscale_image(const BscaleArgs &a, hipStream_t s)
+{
+    const int64_t total = (int64_t)a.quads * a.groups * 64;
+    if (total == 0)
+        return hipSuccess;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(bscale_image_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace tg

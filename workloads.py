@@ -15,6 +15,11 @@ Recipe (every array is raw element bits in row-major order):
 * e4m3 (OCP e4m3fn): per-tensor scale s = float32(amax(|X|) / 448), then
   q = e4m3fn(clamp(X / s, -448, 448)) by torch's CPU cast; the scale pair is
   returned so that C = (acc * s_a) * s_b.
+* MX (OCP Microscaling, block size 32 along K): per block, the E8M0 scale
+  exponent is floor(log2(amax)) - emax (emax 8 for e4m3, 2 for e2m1; 2^-127
+  for an all-zero block), and each element is X / 2^exp rounded to the
+  element format (nearest, ties to even, saturating).  MXFP4 packs two
+  elements per byte, the even one in the low nibble.
 
 A is M x K, B is N x K (K contiguous in both), C is M x N.
 """
@@ -33,7 +38,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str          # "bf16" or "e4m3" (element type of A and B)
+    dtype: str          # "bf16", "e4m3", "mxfp8" or "mxfp4" (element type of A and B)
     out: str            # "f32" or "bf16"
     layout: str         # "bt" (B as N x K) or "bt_preshuffled"
     dist_a: tuple
@@ -46,8 +51,8 @@ class Workload:
         return 2 * self.M * self.N * self.K
 
     @property
-    def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 1
+    def elem_bytes(self) -> float:
+        return {"bf16": 2, "e4m3": 1, "mxfp8": 1, "mxfp4": 0.5}[self.dtype]
 
     @property
     def out_bytes(self) -> int:
@@ -56,7 +61,8 @@ class Workload:
     @property
     def min_bytes(self) -> int:
         """Each operand read once and C written once."""
-        return (self.M * self.K + self.N * self.K) * self.elem_bytes + self.M * self.N * self.out_bytes
+        scales = (self.M + self.N) * (self.K // 32) if self.dtype.startswith("mx") else 0
+        return int((self.M * self.K + self.N * self.K) * self.elem_bytes) + scales + self.M * self.N * self.out_bytes
 
 
 WORKLOADS = {
@@ -75,6 +81,12 @@ WORKLOADS = {
     "e4m3_8192": Workload("e4m3_8192", 8192, 8192, 8192, "e4m3", "bf16", "bt",
                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1005,
                           "per-tensor scales amax/448"),
+    "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "mxfp8", "bf16", "bt_preshuffled",
+                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1006,
+                           "MX block scales, e4m3 elements"),
+    "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "mxfp4", "bf16", "bt_preshuffled",
+                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1007,
+                           "MX block scales, e2m1 elements"),
 }
 
 
@@ -109,12 +121,65 @@ def quantize_e4m3(x: np.ndarray):
     return t.view(torch.uint8).numpy().copy(), float(s)
 
 
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float64)
+MX_EMAX = {"mxfp8": 8, "mxfp4": 2}
+
+
+def _e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 code (ties to the even code, saturating at 6)."""
+    a = np.minimum(np.abs(v.astype(np.float64)), 6.0)
+    hi = np.clip(np.searchsorted(E2M1_GRID, a), 1, 7)
+    lo = hi - 1
+    d_lo, d_hi = a - E2M1_GRID[lo], E2M1_GRID[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(np.signbit(v) & (pick > 0), 8, 0)).astype(np.uint8)
+
+
+def quantize_mx(x: np.ndarray, fmt: str):
+    """MX quantisation of rows x K float32 data: (element bytes, E8M0 scales rows x K/32)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    blk = x.reshape(rows, K // 32, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - MX_EMAX[fmt], -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    v = (blk / np.ldexp(1.0, e)[:, :, None]).reshape(rows, K)
+    if fmt == "mxfp8":
+        t = torch.from_numpy(np.clip(v, -E4M3_MAX, E4M3_MAX).astype(np.float32)).to(torch.float8_e4m3fn)
+        q = t.view(torch.uint8).numpy().copy()
+    else:
+        c = _e2m1_codes(v)
+        q = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    return q, (e + 127).astype(np.uint8)
+
+
+def mx_int_inputs(M: int, N: int, K: int, fmt: str, seed: int):
+    """Small MX inputs whose products and sums are exact in fp32: e4m3
+    integers in [-4, 4] or any e2m1 code, with scales 2^-2 .. 2^2."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for rows in (M, N):
+        if fmt == "mxfp8":
+            import torch
+            vals = rng.integers(-4, 5, size=(rows, K)).astype(np.float32)
+            q = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        else:
+            c = rng.integers(0, 16, size=(rows, K)).astype(np.uint8)
+            q = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        out.append((q, rng.integers(125, 130, size=(rows, K // 32)).astype(np.uint8)))
+    return Inputs(out[0][0], out[1][0], sa_blocks=out[0][1], sb_blocks=out[1][1])
+
+
 @dataclass
 class Inputs:
-    A: np.ndarray          # raw bits, M x K
+    A: np.ndarray          # raw bits, M x K (MXFP4: M x K/2 bytes)
     B: np.ndarray          # raw bits, N x K
     scale_a: float = 1.0
     scale_b: float = 1.0
+    sa_blocks: np.ndarray | None = None   # MX: E8M0 scales, M x K/32
+    sb_blocks: np.ndarray | None = None   # MX: E8M0 scales, N x K/32
 
 
 def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
@@ -128,6 +193,10 @@ def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
     b = _draw(rng, w.dist_b, (N, K))
     if w.dtype == "bf16":
         return Inputs(to_bf16_bits(a), to_bf16_bits(b))
+    if w.dtype.startswith("mx"):
+        qa, ea = quantize_mx(a, w.dtype)
+        qb, eb = quantize_mx(b, w.dtype)
+        return Inputs(qa, qb, sa_blocks=ea, sb_blocks=eb)
     qa, sa = quantize_e4m3(a)
     qb, sb = quantize_e4m3(b)
     return Inputs(qa, qb, sa, sb)
