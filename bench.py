@@ -26,7 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}     # MI355X dense peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}   # MI355X dense peaks
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_preshuffled"
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE /
@@ -45,7 +45,8 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
     With epi (an epilogue name), gemm_run_ex is timed instead, with per-row
     and per-column scale vectors and a bias vector."""
     code = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
-            ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}[(w.dtype, w.out)]
+            ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16, ("mxfp8", "bf16"): tg.GEMM_MXFP8_OUT_BF16,
+            ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16}[(w.dtype, w.out)]
     plan = tg.Plan(w.M, w.N, w.K, code, tg.LAYOUTS[w.layout])
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
@@ -74,7 +75,17 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
         sets.append((A, B, C))
     scale = torch.tensor([inp.scale_a, inp.scale_b], dtype=torch.float32, device="cuda")
     sp = scale.data_ptr() if w.dtype == "e4m3" else None
-    if epi is None:
+    if w.dtype.startswith("mx"):
+        imgs = []
+        for operand, blocks in ((0, inp.sa_blocks), (1, inp.sb_blocks)):
+            src = torch.from_numpy(np.ascontiguousarray(blocks)).cuda()
+            img = torch.empty(plan.bscale_image_bytes(operand), dtype=torch.uint8, device="cuda")
+            plan.preshuffle_bscale(operand, src.data_ptr(), img.data_ptr(), s)
+            imgs.append(img)
+
+        def launch(A, B, C):
+            plan.run_mx(A.data_ptr(), imgs[0].data_ptr(), B.data_ptr(), imgs[1].data_ptr(), C.data_ptr(), stream=s)
+    elif epi is None:
         def launch(A, B, C):
             plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
     else:
@@ -168,7 +179,7 @@ def main():
         log("bench: copy calibration %d MiB x 3" % args.calibrate_copy)
         del src, dst
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
-        "bf16_4096", "bf16_skinny_32x8192x8192", "e4m3_8192"])
+        "bf16_4096", "bf16_skinny_32x8192x8192", "e4m3_8192", "mxfp8_8192", "mxfp4_8192"])
     results = {}
     inputs = {}
     for name in names:
