@@ -13,6 +13,8 @@ Contents
 * ``gemm_bt_mx`` / ``gemm_bt_mx_entries`` -- the same loop for MX
   block-scaled operands (MXFP8: e4m3 elements, MXFP4: e2m1 elements, one
   E8M0 scale per 32 elements along K).
+* ``gemm_bt_int`` / ``gemm_bt_int_entries`` -- exact integer sums (int64)
+  for an int8 A and an int8 or packed int4 B (W4A8).
 * ``round_bf16`` -- the oracle's own round-to-nearest-even to bf16.
 * ``bf16_value`` / ``e4m3fn_value`` -- element decoders from the format
   definitions.
@@ -76,6 +78,14 @@ def _load():
     lib.oracle_gemm_bt_mx.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
     lib.oracle_gemm_bt_mx_entries.restype = None
     lib.oracle_gemm_bt_mx_entries.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.oracle_int8_value.restype = ctypes.c_int
+    lib.oracle_int8_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_int4_value.restype = ctypes.c_int
+    lib.oracle_int4_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_gemm_bt_int.restype = None
+    lib.oracle_gemm_bt_int.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
+    lib.oracle_gemm_bt_int_entries.restype = None
+    lib.oracle_gemm_bt_int_entries.argtypes = [i64, ctypes.c_int, vp, vp, i64, vp, vp, vp, vp]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16_array.restype = None
@@ -305,3 +315,55 @@ def gemm_bt_mx_entries(A, SA, B, SB, K: int, rows, cols, fmt: str = "mxfp8"):
     _load().oracle_gemm_bt_mx_entries(K, _mx(fmt), A.ctypes.data, SA.ctypes.data, B.ctypes.data, SB.ctypes.data,
                                       rows.size, rows.ctypes.data, cols.ctypes.data, C.ctypes.data, S.ctypes.data)
     return C, S
+
+
+# ---------------------------------------------------------------------------
+# Integer operands: int8 A, int8 or packed int4 B (W4A8).
+# ---------------------------------------------------------------------------
+INT_B_BITS = {"i8": 8, "w4a8": 4}
+
+
+def int8_value(bits: int) -> int:
+    return int(_load().oracle_int8_value(int(bits) & 0xFF))
+
+
+def int4_value(nibble: int) -> int:
+    return int(_load().oracle_int4_value(int(nibble) & 0xF))
+
+
+def _int_operands(A, B, K: int, fmt: str):
+    if fmt not in INT_B_BITS:
+        raise ValueError("oracle: unknown integer format %r" % (fmt,))
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    bb = INT_B_BITS[fmt]
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != K or B.shape[1] * 8 != K * bb:
+        raise ValueError("oracle: integer operands are M x K bytes and N x K*%d/8 bytes" % bb)
+    return A, B, bb
+
+
+def gemm_bt_int(A, B, K: int, fmt: str = "i8", want_s: bool = True):
+    """Exact acc = A * B^T and S = sum |a b| (as float64, exact below 2^53)
+    for an int8 A (M x K) and B int8 (N x K, fmt "i8") or packed int4
+    (N x K/2 bytes, fmt "w4a8")."""
+    A, B, bb = _int_operands(A, B, K, fmt)
+    M, N = A.shape[0], B.shape[0]
+    C = np.empty((M, N), np.int64)
+    S = np.empty((M, N), np.int64) if want_s else None
+    _load().oracle_gemm_bt_int(M, N, K, bb, A.ctypes.data, B.ctypes.data, C.ctypes.data,
+                               S.ctypes.data if want_s else None)
+    return C.astype(np.float64), (S.astype(np.float64) if want_s else None)
+
+
+def gemm_bt_int_entries(A, B, K: int, rows, cols, fmt: str = "i8"):
+    """acc and S of the integer product at the (rows[t], cols[t]) entries."""
+    A, B, bb = _int_operands(A, B, K, fmt)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= A.shape[0] or cols.min() < 0 or cols.max() >= B.shape[0]):
+        raise IndexError("oracle: entry out of range")
+    C = np.empty(rows.shape, np.int64)
+    S = np.empty(rows.shape, np.int64)
+    _load().oracle_gemm_bt_int_entries(K, bb, A.ctypes.data, B.ctypes.data, rows.size, rows.ctypes.data,
+                                       cols.ctypes.data, C.ctypes.data, S.ctypes.data)
+    return C.astype(np.float64), S.astype(np.float64)

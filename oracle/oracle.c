@@ -41,6 +41,17 @@
  * elem(i,k) * 2^(scale[i][k/32] - 127), the scales stored rows x K/32 bytes
  * row-major.
  *
+ * Integer operands (int8 MFMA with int32 accumulation: FlyDSL "Kernel
+ * authoring guide", section 4.3 "ROCm intrinsics", MFMA instructions, and
+ * the "Kernel Authoring" skill, section 6 "MFMA Integration"; W4A8: the same
+ * skill, section 10 "Troubleshooting", item INT4, an int8 A with a B of
+ * packed int4 values):
+ *   int8      : two's complement byte, -128 .. 127.
+ *   int4      : two's complement nibble, -8 .. 7; two per byte, element 2t
+ *               in the low nibble of byte t (the order MX e2m1 uses).
+ * The products are summed exactly in int64: acc[i][j] = sum_k a(i,k) b(j,k)
+ * and S[i][j] = sum_k |a(i,k) b(j,k)|.
+ *
  * The output rounding to bf16 is round-to-nearest, ties-to-even, done in
  * fp64 with nearbyint() under the default FE_TONEAREST mode.
  *
@@ -215,6 +226,70 @@ void oracle_gemm_bt_mx_entries(int64_t K, int kind, const void *A, const uint8_t
     for (t = 0; t < count; ++t) {
         double c, s;
         dot_entry_mx(K, kind, A, SA, B, SB, rows[t], cols[t], &c, &s);
+        C[t] = c;
+        if (S)
+            S[t] = s;
+    }
+}
+
+int oracle_int8_value(uint8_t bits) { return bits < 128 ? (int)bits : (int)bits - 256; }
+
+int oracle_int4_value(uint8_t nibble)
+{
+    nibble &= 0xF;
+    return nibble < 8 ? (int)nibble : (int)nibble - 16;
+}
+
+/* Element k of row r of an integer operand with K elements per row:
+ * bits 8 (one byte each) or 4 (two per byte, the even element low). */
+static int64_t int_element(int bits, const uint8_t *base, int64_t K, int64_t r, int64_t k)
+{
+    const int64_t idx = r * K + k;
+    if (bits == 8)
+        return oracle_int8_value(base[idx]);
+    const uint8_t byte = base[idx / 2];
+    return oracle_int4_value((idx % 2) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF));
+}
+
+static void dot_entry_int(int64_t K, int b_bits, const uint8_t *A, const uint8_t *B, int64_t i, int64_t j,
+                          int64_t *c, int64_t *s)
+{
+    int64_t acc = 0, mag = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t p = int_element(8, A, K, i, k) * int_element(b_bits, B, K, j, k);
+        acc += p;
+        mag += p < 0 ? -p : p;
+    }
+    *c = acc;
+    *s = mag;
+}
+
+/* int8 A (M x K bytes) times B^T, B int8 (b_bits 8, N x K bytes) or packed
+ * int4 (b_bits 4, N x K/2 bytes): exact sums, full and selected entries. */
+void oracle_gemm_bt_int(int64_t M, int64_t N, int64_t K, int b_bits, const uint8_t *A, const uint8_t *B,
+                        int64_t *C, int64_t *S)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            int64_t c, s;
+            dot_entry_int(K, b_bits, A, B, i, j, &c, &s);
+            C[i * N + j] = c;
+            if (S)
+                S[i * N + j] = s;
+        }
+    }
+}
+
+void oracle_gemm_bt_int_entries(int64_t K, int b_bits, const uint8_t *A, const uint8_t *B, int64_t count,
+                                const int64_t *rows, const int64_t *cols, int64_t *C, int64_t *S)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < count; ++t) {
+        int64_t c, s;
+        dot_entry_int(K, b_bits, A, B, rows[t], cols[t], &c, &s);
         C[t] = c;
         if (S)
             S[t] = s;

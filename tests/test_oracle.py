@@ -418,3 +418,86 @@ def test_bscale_image_hand_computed_entries():
     assert (img[:, :, :, :, 2:] == 127).all()
     # rows 70.. of quad 1 (block 0 lanes with l % 16 >= 6) are padding
     assert img[1, 0, 6, 0, 0] == 127 and img[1, 0, 5, 0, 0] == S[69, 0]
+
+
+# ---------------------------------------------------------------------------
+# Integer operands (int8 A; int8 or packed int4 B)
+# ---------------------------------------------------------------------------
+INT4_TABLE = [0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]
+
+
+def test_int_decoder_tables(oracle_mod):
+    assert [oracle_mod.int4_value(n) for n in range(16)] == INT4_TABLE
+    assert oracle_mod.int8_value(0x00) == 0 and oracle_mod.int8_value(0x7F) == 127
+    assert oracle_mod.int8_value(0x80) == -128 and oracle_mod.int8_value(0xFF) == -1
+    assert oracle_mod.int8_value(0x9C) == -100
+
+
+def _int_random(rng, rows, K, bits):
+    """Random bytes and their values decoded independently of the oracle."""
+    if bits == 8:
+        b = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+        vals = [[int(v) - 256 if v >= 128 else int(v) for v in r] for r in b]
+        return b, vals
+    nib = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+    vals = [[INT4_TABLE[int(v)] for v in r] for r in nib]
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8), vals
+
+
+@pytest.mark.parametrize("fmt", ["i8", "w4a8"])
+@pytest.mark.parametrize("M,N,K", [(3, 5, 64), (2, 4, 6), (1, 1, 2)])
+def test_int_brute_force(oracle_mod, fmt, M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K + len(fmt))
+    A, va = _int_random(rng, M, K, 8)
+    B, vb = _int_random(rng, N, K, 8 if fmt == "i8" else 4)
+    C, S = oracle_mod.gemm_bt_int(A, B, K, fmt)
+    for i in range(M):
+        for j in range(N):
+            assert C[i, j] == sum(va[i][k] * vb[j][k] for k in range(K))
+            assert S[i, j] == sum(abs(va[i][k] * vb[j][k]) for k in range(K))
+    rows, cols = np.array([0, M - 1]), np.array([N - 1, 0])
+    Ce, Se = oracle_mod.gemm_bt_int_entries(A, B, K, rows, cols, fmt)
+    assert np.array_equal(Ce, C[rows, cols]) and np.array_equal(Se, S[rows, cols])
+
+
+def test_w4a8_nibble_order(oracle_mod):
+    # byte 0x21: element 0 = 1 (low nibble), element 1 = 2 (high nibble)
+    A = np.array([[10, 100]], np.uint8)
+    B = np.array([[0x21]], np.uint8)
+    C, _ = oracle_mod.gemm_bt_int(A, B, 2, "w4a8")
+    assert C[0, 0] == 10 * 1 + 100 * 2
+    # 0xF8: element 0 = -8, element 1 = -1
+    C, _ = oracle_mod.gemm_bt_int(A, np.array([[0xF8]], np.uint8), 2, "w4a8")
+    assert C[0, 0] == 10 * -8 + 100 * -1
+
+
+def test_int_extremes_closed_form(oracle_mod):
+    K = 4096
+    A = np.full((2, K), 0x80, np.uint8)                  # -128
+    C, S = oracle_mod.gemm_bt_int(A, np.full((3, K), 0x80, np.uint8), K, "i8")
+    assert np.all(C == K * 16384) and np.all(S == K * 16384)
+    C, _ = oracle_mod.gemm_bt_int(A, np.full((3, K // 2), 0x88, np.uint8), K, "w4a8")   # -8, -8
+    assert np.all(C == K * 1024)
+    C, _ = oracle_mod.gemm_bt_int(A, np.full((3, K), 0x7F, np.uint8), K, "i8")
+    assert np.all(C == -K * 128 * 127)
+
+
+def test_int8_agrees_with_the_bf16_gemm_on_exact_values(oracle_mod):
+    # every int8 value is exact in bf16 and every partial sum here is exact
+    # in fp64, so the float oracle must give the same numbers
+    rng = np.random.default_rng(11)
+    A = rng.integers(0, 256, (5, 96)).astype(np.uint8)
+    B = rng.integers(0, 256, (7, 96)).astype(np.uint8)
+    C, S = oracle_mod.gemm_bt_int(A, B, 96, "i8")
+    as_bf16 = lambda x: bf16(x.view(np.int8).astype(np.float32))
+    R, RS = oracle_mod.gemm_bt(as_bf16(A), as_bf16(B), dtype="bf16")
+    assert np.array_equal(C, R) and np.array_equal(S, RS)
+
+
+def test_int_rejects_bad_shapes(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.gemm_bt_int(np.zeros((2, 64), np.uint8), np.zeros((2, 64), np.uint8), 64, "w4a8")
+    with pytest.raises(ValueError):
+        oracle_mod.gemm_bt_int(np.zeros((2, 64), np.uint8), np.zeros((2, 32), np.uint8), 64, "i8")
+    with pytest.raises(ValueError):
+        oracle_mod.gemm_bt_int(np.zeros((2, 64), np.uint8), np.zeros((2, 64), np.uint8), 64, "i4")
