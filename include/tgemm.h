@@ -54,7 +54,9 @@ typedef enum {
     GEMM_BF16_OUT_BF16 = 1,      /* A, B bf16; C bf16                                 */
     GEMM_E4M3_OUT_BF16 = 2,      /* A, B OCP fp8 e4m3fn (max 448); C bf16             */
     GEMM_MXFP8_OUT_BF16 = 3,     /* A, B MX: e4m3fn elements + E8M0 scales; C bf16    */
-    GEMM_MXFP4_OUT_BF16 = 4      /* A, B MX: e2m1 elements (2 per byte) + E8M0; C bf16 */
+    GEMM_MXFP4_OUT_BF16 = 4,     /* A, B MX: e2m1 elements (2 per byte) + E8M0; C bf16 */
+    GEMM_I8_OUT_BF16 = 5,        /* A, B int8, exact int32 sums; C bf16               */
+    GEMM_W4A8_OUT_BF16 = 6       /* A int8, B int4 (2 per byte), int32 sums; C bf16   */
 } gemm_dtype;
 
 typedef enum {
@@ -85,14 +87,14 @@ void gemm_plan_destroy(gemm_plan *plan);
 
 /*
  * gemm_preshuffled_b_bytes -- bytes of the pre-shuffled B image:
- * N * K * elem_bytes (a pure permutation of B).  0 for a NULL plan.
+ * N * K * b_elem_bits / 8 (a pure permutation of B).  0 for a NULL plan.
  */
 size_t gemm_preshuffled_b_bytes(const gemm_plan *plan);
 
 /*
  * gemm_preshuffle_b -- write B (N x K row-major) in MFMA operand order.
  * The image is the 5-mode byte array (N/16, Kb/64, 4, 16, 16) taken in
- * row-major order, with Kb = K * elem_bytes: n-block, 64-byte k-block,
+ * row-major order, with Kb = K * b_elem_bits / 8 (B's row bytes): n-block, 64-byte k-block,
  * 16-byte k-quarter q, row r within the n-block, byte.  Each 1 KiB block is
  * therefore one wave's B operand for a 64-byte K step: lane 16*q + r loads
  * the 16 bytes of row 16*nb + r at k-bytes 64*kb + 16*q.  (Kernel Authoring
@@ -220,6 +222,32 @@ int gemm_preshuffle_bscale(const gemm_plan *plan, int operand, const void *scale
 int gemm_run_mx(const gemm_plan *plan, const void *A, const void *A_bscale, const void *B,
                 const void *B_bscale, void *C, const gemm_epilogue_args *epi, hipStream_t stream);
 
+/*
+ * Integer operands (GEMM_I8_OUT_BF16, GEMM_W4A8_OUT_BF16).  The pages' int8
+ * MFMA accumulates i8 x i8 products in int32 (FlyDSL "Kernel authoring
+ * guide", section 4.3 "ROCm intrinsics", MFMA instructions; "Kernel
+ * Authoring" skill, section 6 "MFMA Integration"), and their W4A8 GEMM takes
+ * an int8 A with a B of packed int4 values unpacked to int8 inside the kernel
+ * (the same skill, section 10 "Troubleshooting", INT4 item).  This library's
+ * reading:
+ *
+ *     acc[m][n] = sum_k a(m,k) * b(n,k)            exact, in int32
+ *     C[m][n]   = cvt( act( (float(acc) * sa(m)) * sb(n) (+ bias[n]) ) )
+ *
+ *   int8 two's complement (-128 .. 127); int4 two's complement (-8 .. 7), two
+ *   per byte, element 2t in the low nibble of byte t.  float() rounds to
+ *   nearest even (exact while |acc| < 2^24).  The scales and epilogue are
+ *   those of gemm_run / gemm_run_ex, typically per-row and per-column
+ *   dequantisation scales.
+ *   A   M x K bytes row-major;  B  N x K bytes (int8) or N x K/2 bytes (int4)
+ *       row-major, or the pre-shuffled image (gemm_preshuffle_b on B's bytes:
+ *       for int4 a 64-byte k-block holds 128 values).
+ * Requirements beyond gemm_plan_create's: K % 64 == 0 (int8) or K % 128 == 0
+ * (W4A8), so every row of B is whole 64-byte K steps; K < 2^17, so no sum of
+ * products (each at most 2^14 in magnitude) can leave the int32 range.
+ * Run through gemm_run or gemm_run_ex.
+ */
+
 /* gemm_last_error -- message for the calling thread's last failure ("" if none). */
 const char *gemm_last_error(void);
 
@@ -244,16 +272,17 @@ typedef struct {
     int32_t tiles_m, tiles_n;
     int32_t group_m;         /* tile rows per raster group within one XCD             */
     int32_t split_k;         /* K slices reduced inside a workgroup (skinny kernel)   */
-    int32_t elem_bits;       /* bits per input element (16, 8 or 4); elem_bytes is
-                                elem_bits / 8, so 0 for MXFP4                          */
+    int32_t elem_bits;       /* bits per input element of A (16, 8 or 4); elem_bytes
+                                is elem_bits / 8, so 0 for MXFP4                       */
+    int32_t b_elem_bits;     /* bits per input element of B (4 for W4A8, else elem_bits) */
 } gemm_plan_info;
 
 /* gemm_plan_query -- copy the plan's decisions into *info. */
 int gemm_plan_query(const gemm_plan *plan, gemm_plan_info *info);
 
 typedef enum {
-    GEMM_VIEW_A = 0,          /* A bytes:       (M, Kb):(Kb, 1)                              */
-    GEMM_VIEW_B = 1,          /* B bytes:       (N, Kb):(Kb, 1)                              */
+    GEMM_VIEW_A = 0,          /* A bytes:       (M, Ka):(Ka, 1), Ka = K * elem_bits / 8      */
+    GEMM_VIEW_B = 1,          /* B bytes:       (N, Kb):(Kb, 1), Kb = K * b_elem_bits / 8    */
     GEMM_VIEW_B_SHUF = 2,     /* pre-shuffled:  (N/16, Kb/64, 4, 16, 16):(16Kb, 1024, 256, 16, 1) */
     GEMM_VIEW_B_SRC = 3,      /* B bytes seen through the same 5 coordinates:
                                  (N/16, Kb/64, 4, 16, 16):(16Kb, 64, 16, Kb, 1)           */

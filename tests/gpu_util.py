@@ -15,12 +15,15 @@ import tiled_gemm_amd as tg
 
 # MX: products of the decoded elements are exact in fp32, so only the fp32
 # accumulation (the S term) and the output rounding (2^-8) remain.
-RHO = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -3, "mxfp8": 2.0 ** -8, "mxfp4": 2.0 ** -8}
+# Integer operands: the sums are exact, so only the output rounding remains.
+RHO = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -3, "mxfp8": 2.0 ** -8, "mxfp4": 2.0 ** -8, "i8": 2.0 ** -8,
+       "w4a8": 2.0 ** -8}
 ABS_COEF = 4e-6
 
 DTYPE_CODE = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
               ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16, ("mxfp8", "bf16"): tg.GEMM_MXFP8_OUT_BF16,
-              ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16}
+              ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16, ("i8", "bf16"): tg.GEMM_I8_OUT_BF16,
+              ("w4a8", "bf16"): tg.GEMM_W4A8_OUT_BF16}
 
 
 def to_dev(bits: np.ndarray) -> torch.Tensor:

@@ -252,6 +252,47 @@ def test_mx_plans(lib, dtype, bits, layout):
             tg.Plan(64, 64, 96, dtype, layout)          # K/2 bytes not a multiple of 64
 
 
+@pytest.mark.parametrize("dtype,b_bits", [(tg.GEMM_I8_OUT_BF16, 8), (tg.GEMM_W4A8_OUT_BF16, 4)])
+@pytest.mark.parametrize("layout", [tg.GEMM_LAYOUT_BT, tg.GEMM_LAYOUT_BT_PRESHUFFLED])
+def test_int_plans(lib, monkeypatch, dtype, b_bits, layout):
+    for M, N, K in [(8192, 8192, 8192), (32, 4096, 1024), (300, 272, 1152), (1, 16, 128)]:
+        with tg.Plan(M, N, K, dtype, layout) as p:
+            info = p.info()
+            assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 512   # 8-wave pipelined
+            assert info["elem_bits"] == 8 and info["elem_bytes"] == 1 and info["b_elem_bits"] == b_bits
+            assert info["out_bytes"] == 2
+            assert tg.gemm_preshuffled_b_bytes(p.handle) == N * K * b_bits // 8
+            assert tuple(map(tuple, tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_A))) == ((M, K), (K, 1))
+            kb = K * b_bits // 8
+            assert tuple(map(tuple, tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B))) == ((N, kb), (kb, 1))
+            assert tuple(map(tuple, tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B_SHUF)))[0] == (N // 16, kb // 64, 4, 16, 16)
+            assert p.bscale_image_bytes(0) == 0
+    monkeypatch.setenv("TGEMM_PIPE_WAVES", "4")
+    with tg.Plan(512, 512, 1024, dtype, layout) as p:
+        assert p.info()["threads"] == 256
+    monkeypatch.delenv("TGEMM_PIPE_WAVES")
+    with pytest.raises(tg.GemmError):
+        tg.Plan(64, 64, 96, dtype, layout)                    # K % 64
+    if b_bits == 4:
+        with pytest.raises(tg.GemmError):
+            tg.Plan(64, 64, 192, dtype, layout)               # K/2 bytes not whole 64-byte steps
+    tg.Plan(64, 64, (1 << 17) - 128, dtype, layout).close()   # largest K without int32 overflow
+    with pytest.raises(tg.GemmError, match="2\\^17"):
+        tg.Plan(64, 64, 1 << 17, dtype, layout)
+    with pytest.raises(tg.GemmError):
+        tg.Plan(64, 64, 128, dtype + 2, layout)               # past the last dtype
+
+
+def test_int_run_guards(lib):
+    A, B, C = 0x100000, 0x200000, 0x300000
+    with tg.Plan(256, 256, 256, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert lib.gemm_run_mx(p.handle, A, A, B, B, C, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_bscale(p.handle, 0, A, B, None) == tg.GEMM_ERR_INVALID_ARG
+        # C overlapping B: B has N * K / 2 bytes
+        assert lib.gemm_run(p.handle, A, B, B + 256 * 128 - 16, None, None) == tg.GEMM_ERR_INVALID_ARG
+        assert lib.gemm_preshuffle_b(p.handle, B, B + 256 * 128 - 16, None) == tg.GEMM_ERR_INVALID_ARG
+
+
 def test_mx_entry_point_guards(lib):
     A, B, C, SA, SB = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
     with tg.Plan(256, 256, 256, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:

@@ -27,6 +27,8 @@ GEMM_BF16_OUT_BF16 = 1
 GEMM_E4M3_OUT_BF16 = 2
 GEMM_MXFP8_OUT_BF16 = 3
 GEMM_MXFP4_OUT_BF16 = 4
+GEMM_I8_OUT_BF16 = 5           # int8 A and B, int32 sums
+GEMM_W4A8_OUT_BF16 = 6         # int8 A, packed int4 B (two per byte, even element low)
 
 GEMM_LAYOUT_BT = 0
 GEMM_LAYOUT_BT_PRESHUFFLED = 1
@@ -63,7 +65,7 @@ class gemm_plan_info(ctypes.Structure):
         (f, ctypes.c_int32) for f in (
             "dtype", "layout", "elem_bytes", "out_bytes", "kernel", "tile_m", "tile_n",
             "tile_k_bytes", "threads", "lds_stages", "lds_bytes", "grid", "tiles_m", "tiles_n",
-            "group_m", "split_k", "elem_bits")]
+            "group_m", "split_k", "elem_bits", "b_elem_bits")]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -220,7 +222,8 @@ def gemm_tile_of_workgroup(plan: int, wg: int):
 # ---------------------------------------------------------------- conveniences
 
 DTYPES = {"bf16_f32": GEMM_BF16_OUT_F32, "bf16": GEMM_BF16_OUT_BF16, "e4m3": GEMM_E4M3_OUT_BF16,
-          "mxfp8": GEMM_MXFP8_OUT_BF16, "mxfp4": GEMM_MXFP4_OUT_BF16}
+          "mxfp8": GEMM_MXFP8_OUT_BF16, "mxfp4": GEMM_MXFP4_OUT_BF16, "i8": GEMM_I8_OUT_BF16,
+          "w4a8": GEMM_W4A8_OUT_BF16}
 LAYOUTS = {"bt": GEMM_LAYOUT_BT, "bt_preshuffled": GEMM_LAYOUT_BT_PRESHUFFLED}
 
 

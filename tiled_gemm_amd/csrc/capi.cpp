@@ -19,7 +19,8 @@ using tg::Layout;
 
 struct gemm_plan {
     gemm_plan_info info;
-    int64_t kbytes;
+    int64_t kbytes;                    // bytes of one row of A
+    int64_t kbytes_b;                  // bytes of one row of B
     int32_t k_tiles, tail_bytes;
     const tg::TiledVariant *tiled;     // kernel == 0
     const tg::SkinnyVariant *skinny;   // kernel == 1
@@ -47,11 +48,15 @@ constexpr int64_t kMaxRowBytes = int64_t(1) << 23;    // 256 rows stay below 2^3
 constexpr int kLdsLimit = 160 * 1024;                   // gfx950 LDS per workgroup
 
 bool is_mx(int dtype) { return dtype == GEMM_MXFP8_OUT_BF16 || dtype == GEMM_MXFP4_OUT_BF16; }
+bool is_int(int dtype) { return dtype == GEMM_I8_OUT_BF16 || dtype == GEMM_W4A8_OUT_BF16; }
+// Bits per element of A.
 int elem_bits_of(int dtype)
 {
     switch (dtype) {
     case GEMM_E4M3_OUT_BF16:
     case GEMM_MXFP8_OUT_BF16:
+    case GEMM_I8_OUT_BF16:
+    case GEMM_W4A8_OUT_BF16:
         return 8;
     case GEMM_MXFP4_OUT_BF16:
         return 4;
@@ -59,6 +64,7 @@ int elem_bits_of(int dtype)
         return 16;
     }
 }
+int b_elem_bits_of(int dtype) { return dtype == GEMM_W4A8_OUT_BF16 ? 4 : elem_bits_of(dtype); }
 int out_bytes_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? 4 : 2; }
 int elem_of(int dtype)
 {
@@ -69,6 +75,10 @@ int elem_of(int dtype)
         return tg::kMx8;
     case GEMM_MXFP4_OUT_BF16:
         return tg::kMx4;
+    case GEMM_I8_OUT_BF16:
+        return tg::kI8;
+    case GEMM_W4A8_OUT_BF16:
+        return tg::kW4A8;
     default:
         return tg::kBf16;
     }
@@ -85,13 +95,17 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     const tg::TiledVariant *v = tg::tiled_variants(&n);
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
     const int elem = elem_of(I.dtype), out = out_of(I.dtype);
-    if (is_mx(I.dtype)) {
-        // MX operands: only the pipelined 256 x 256 kernel (any M, N: tails
-        // are masked).
+    if (is_mx(I.dtype) || is_int(I.dtype)) {
+        // MX and integer operands: only the pipelined 256 x 256 kernel (any
+        // M, N: tails are masked).  TGEMM_PIPE_WAVES=<n> restricts the choice
+        // to n-wave variants.
+        const char *ew = getenv("TGEMM_PIPE_WAVES");
+        const int waves = ew ? atoi(ew) : 0;
         int nb = 0;
         const tg::TiledVariant *b = tg::pipe_variants(&nb);
         for (int i = 0; i < nb; ++i)
-            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre)
+            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre &&
+                (waves == 0 || b[i].wgm * b[i].wgn == waves))
                 return &b[i];
         return nullptr;
     }
@@ -132,7 +146,8 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
 
 const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
 {
-    if (I.layout != GEMM_LAYOUT_BT || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") || is_mx(I.dtype))
+    if (I.layout != GEMM_LAYOUT_BT || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") || is_mx(I.dtype) ||
+        is_int(I.dtype))
         return nullptr;
     const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
     int n = 0;
@@ -164,11 +179,11 @@ Layout make(std::initializer_list<int64_t> shape, std::initializer_list<int64_t>
 Layout view_of(const gemm_plan &p, int view, bool *okv)
 {
     const gemm_plan_info &I = p.info;
-    const int64_t Kb = p.kbytes;
+    const int64_t Kb = p.kbytes_b;
     *okv = true;
     switch (view) {
     case GEMM_VIEW_A:
-        return make({I.M, Kb}, {Kb, 1});
+        return make({I.M, p.kbytes}, {p.kbytes, 1});
     case GEMM_VIEW_B:
         return make({I.N, Kb}, {Kb, 1});
     case GEMM_VIEW_B_SHUF:
@@ -226,7 +241,7 @@ const char *gemm_last_error(void) { return g_last_error.c_str(); }
 
 gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout)
 {
-    if (dtype < GEMM_BF16_OUT_F32 || dtype > GEMM_MXFP4_OUT_BF16) {
+    if (dtype < GEMM_BF16_OUT_F32 || dtype > GEMM_W4A8_OUT_BF16) {
         fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
         return nullptr;
     }
@@ -245,8 +260,18 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     }
     const int ebits = elem_bits_of(dtype), ob = out_bytes_of(dtype);
     const int64_t kbytes = K * ebits / 8;
+    const int64_t kbytes_b = K * b_elem_bits_of(dtype) / 8;
     if (is_mx(dtype) && K % 32 != 0) {
         fail(GEMM_ERR_UNSUPPORTED, "K=%lld must be a multiple of 32 (MX block)", (long long)K);
+        return nullptr;
+    }
+    if (dtype == GEMM_W4A8_OUT_BF16 && K % 128 != 0) {
+        fail(GEMM_ERR_UNSUPPORTED, "K=%lld must be a multiple of 128 for W4A8 (64-byte steps of int4 B)",
+             (long long)K);
+        return nullptr;
+    }
+    if (is_int(dtype) && K >= (int64_t(1) << 17)) {
+        fail(GEMM_ERR_UNSUPPORTED, "K=%lld: integer sums need K < 2^17 to stay inside int32", (long long)K);
         return nullptr;
     }
     if (N % 16 != 0) {
@@ -284,8 +309,10 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     I.layout = layout;
     I.elem_bytes = ebits / 8;
     I.elem_bits = ebits;
+    I.b_elem_bits = b_elem_bits_of(dtype);
     I.out_bytes = ob;
     p->kbytes = kbytes;
+    p->kbytes_b = kbytes_b;
     p->k_tiles = (int32_t)((kbytes + tg::kTileKBytes - 1) / tg::kTileKBytes);
     p->tail_bytes = kbytes % tg::kTileKBytes ? (int32_t)(kbytes % tg::kTileKBytes) : tg::kTileKBytes;
     I.tile_k_bytes = tg::kTileKBytes;
@@ -342,7 +369,7 @@ size_t gemm_preshuffled_b_bytes(const gemm_plan *plan)
 {
     if (!plan)
         return 0;
-    return (size_t)plan->info.N * (size_t)plan->kbytes;
+    return (size_t)plan->info.N * (size_t)plan->kbytes_b;
 }
 
 int gemm_plan_query(const gemm_plan *plan, gemm_plan_info *info)
@@ -461,7 +488,7 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
     a.src = view_of(*plan, GEMM_VIEW_B_SRC, &okv);
     a.dst = view_of(*plan, GEMM_VIEW_B_SHUF, &okv);
     a.nblocks = (int32_t)(plan->info.N / 16);
-    a.kblocks = (int32_t)(plan->kbytes / 64);
+    a.kblocks = (int32_t)(plan->kbytes_b / 64);
     const hipError_t e = tg::launch_preshuffle(a, stream);
     if (e != hipSuccess)
         return fail(GEMM_ERR_HIP, "preshuffle launch: %s", hipGetErrorString(e));
@@ -492,7 +519,7 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
     if ((A && misaligned(A)) || (B && misaligned(B)) || misaligned(C))
         return fail(GEMM_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
     const size_t cbytes = (size_t)I.M * I.N * I.out_bytes;
-    if (overlap(C, cbytes, A, (size_t)I.M * plan->kbytes) || overlap(C, cbytes, B, (size_t)I.N * plan->kbytes))
+    if (overlap(C, cbytes, A, (size_t)I.M * plan->kbytes) || overlap(C, cbytes, B, (size_t)I.N * plan->kbytes_b))
         return fail(GEMM_ERR_INVALID_ARG, "C overlaps A or B");
     if (int rc = check_device())
         return rc;
@@ -518,6 +545,7 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.M = (int32_t)I.M;
         a.N = (int32_t)I.N;
         a.kbytes = (int32_t)plan->kbytes;
+        a.kbytes_b = (int32_t)plan->kbytes_b;
         a.k_tiles = plan->k_tiles;
         a.tail_bytes = plan->tail_bytes;
         a.grid = I.grid;

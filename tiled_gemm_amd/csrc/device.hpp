@@ -16,6 +16,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -165,6 +166,53 @@ __device__ inline void mfma_mx4_a(f32x4 &acc, u32x4 x, u32x4 y, uint32_t sx, uin
         asm volatile(TG_MX_ASM(1, 1, " cbsz:4 blgp:4") : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
 }
 #undef TG_MX_ASM
+
+// int8 atom: D += X * Y^T over 64 int8 values per row (16 bytes per lane, the
+// same lane / K slot assignment as the bf16 atom), int32 sums.  The
+// accumulator travels as f32x4 storage holding the int32 bits, so the
+// kernels keep one accumulator type; the epilogue converts.
+__device__ inline f32x4 mfma_i8(u32x4 x, u32x4 y, f32x4 acc)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, x),
+                                                                           __builtin_bit_cast(i32x4, y),
+                                                                           __builtin_bit_cast(i32x4, acc), 0, 0, 0));
+}
+
+__device__ inline void mfma_i8_a(f32x4 &acc, u32x4 x, u32x4 y)
+{
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+}
+
+// Eight packed int4 values (one word: element 2t in the low nibble of byte
+// t, two's complement) -> eight int8 bytes in element order, each holding 16
+// times its value (the nibble moved to the high half of its byte, where the
+// int8 sign bit is the int4 sign bit).  Sums of such bytes are 16 times the
+// int4 sums, exactly; the caller divides by 16.
+__device__ inline u32x2 int4x8_to_i8x16(uint32_t w)
+{
+    const uint32_t ev = (w << 4) & 0xF0F0F0F0u;    // elements 0, 2, 4, 6 in bytes 0..3
+    const uint32_t od = w & 0xF0F0F0F0u;           // elements 1, 3, 5, 7
+    // v_perm_b32 byte select over {od, ev}: selectors 0-3 pick bytes of ev,
+    // 4-7 bytes of od.  lo = [ev0, od0, ev1, od1], hi = [ev2, od2, ev3, od3].
+    return u32x2{__builtin_amdgcn_perm(od, ev, 0x05010400u), __builtin_amdgcn_perm(od, ev, 0x07030602u)};
+}
+
+// Half h (elements 16 h .. 16 h + 15) of 32 packed int4 values, as one int8
+// atom operand.
+__device__ inline u32x4 int4x32_half_to_i8(u32x4 w, int h)
+{
+    const u32x2 a = int4x8_to_i8x16(h ? w.z : w.x);
+    const u32x2 b = int4x8_to_i8x16(h ? w.w : w.y);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+
+// The int32 sums held in an accumulator's bits -> fp32 (nearest even), times
+// `unit` (a power of two, so exact).
+__device__ inline f32x4 int_acc_to_f32(f32x4 acc, float unit)
+{
+    const i32x4 v = __builtin_bit_cast(i32x4, acc);
+    return f32x4{(float)v.x * unit, (float)v.y * unit, (float)v.z * unit, (float)v.w * unit};
+}
 
 // 64 wait states: longer than any MFMA's result latency.
 __device__ inline void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }

@@ -55,7 +55,6 @@ struct BpCfg {
     static constexpr int FM = WTM / 16;                            // 16-row blocks per wave
     static constexpr int FN = WTN / 16;                            // 16-column blocks per wave
     static constexpr int AR = BP_STAGE / (THREADS * kChunkBytes);  // DMA rounds per stage
-    static constexpr int BR = FN * 2;                              // B loads per lane per step
     static constexpr int LDS = NS * BP_STAGE;
     static_assert(NS >= 4, "the barrier schedule needs two stages beyond read/ready");
     static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
@@ -76,7 +75,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
 {
     using Cfg = BpCfg<WGM, WGN, NS>;
     constexpr int WAVES = Cfg::WAVES;
-    constexpr int BP_FM = Cfg::FM, BP_FN = Cfg::FN, BP_AR = Cfg::AR, BP_BR = Cfg::BR;
+    constexpr int BP_FM = Cfg::FM, BP_FN = Cfg::FN, BP_AR = Cfg::AR;
+    constexpr int BP_BR = BP_FN * (ELEM == kW4A8 ? 1 : 2);    // B loads per lane per step
     constexpr int BP_WTM = Cfg::WTM, BP_WTN = Cfg::WTN;
     // Fragment stream of one step: bf16 -> 2 sub-steps x 16 row blocks, one
     // 16-byte read each; fp8 -> 16 row blocks, two reads (chunks q, q+4).
@@ -84,6 +84,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     // otherwise two 64-byte halves (bf16, MX e2m1).
     constexpr bool WIDE = ELEM == kFp8 || ELEM == kMx8;
     constexpr bool MX = ELEM == kMx8 || ELEM == kMx4;
+    // Integer operands: int8 A with int8 B (kI8) or packed int4 B (kW4A8).
+    // An int4 step of B is 64 bytes per row: one 16-byte load per lane and
+    // 16-column block (lane group q: values 32 q .. 32 q + 31 of the step),
+    // unpacked into two int8 atom operands, half h pairing with A chunk
+    // 2 q + h.
+    constexpr bool INT = ELEM == kI8 || ELEM == kW4A8;
+    constexpr bool W4 = ELEM == kW4A8;
+    constexpr int BH = W4 ? 1 : 2;                           // B loads per block and step
+    static_assert(!INT || OUT == kOutBf16, "integer GEMMs write bf16");
     constexpr int NG = WIDE ? BP_FM : 2 * BP_FM;            // groups (FN MFMAs each)
     static_assert(!MX || (ACCA && ADMA && BP_WTM % 64 == 0 && BP_WTN % 64 == 0),
                   "MX operands run on the AGPR-accumulator kernel, whole 64-row scale quads per wave");
@@ -101,8 +110,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     const int rows_a = min(p.M - m0, BP_BM);
     const int rows_b = min(p.N - n0, BP_BN);
     const uint32_t kb = (uint32_t)p.kbytes;
+    const uint32_t kbB = (uint32_t)p.kbytes_b;
     const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
-    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
     const int nk = p.k_tiles;
     const uint32_t tail = (uint32_t)p.tail_bytes;
 
@@ -156,17 +166,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
 
     // ---- B: n-block (wn * FN + j) of the workgroup.  Pre-shuffled: k-blocks
     // 2kt and 2kt+1 (1 KiB apart); plain: chunks q and q + 4 of row
-    // 16 * nb + r16 (64 bytes apart).
+    // 16 * nb + r16 (64 bytes apart).  Packed int4: the one k-block kt, or
+    // chunk q of the row's 64 bytes of the step.
     constexpr uint32_t kBHalf = BPRE ? 1024u : 64u;
-    constexpr uint32_t kBStep = BPRE ? 2048u : (uint32_t)kTileKBytes;
+    constexpr uint32_t kBStep = W4 ? (BPRE ? 1024u : 64u) : (BPRE ? 2048u : (uint32_t)kTileKBytes);
     uint32_t voffB[BP_FN];
 #pragma unroll
     for (int j = 0; j < BP_FN; ++j)
-        voffB[j] = BPRE ? (uint32_t)(wn * BP_FN + j) * 16u * kb + (uint32_t)l * 16u
-                        : (uint32_t)((wn * BP_FN + j) * 16 + r16) * kb + (uint32_t)q * kChunkBytes;
+        voffB[j] = BPRE ? (uint32_t)(wn * BP_FN + j) * 16u * kbB + (uint32_t)l * 16u
+                        : (uint32_t)((wn * BP_FN + j) * 16 + r16) * kbB + (uint32_t)q * kChunkBytes;
     // A half-filled last step (K bytes 0..63 valid): half 1 is the missing part.
     auto b_keep = [&](bool beyond, bool part, int h) { return !beyond & ((h == 0) | !part); };
-    u32x4 bq[2][BP_FN][2];
+    u32x4 bq[2][BP_FN][BH];
     auto issue_b_one = [&](int kt, auto set_c, int j, int h) {
         constexpr int S = decltype(set_c)::value;
         const bool beyond = kt >= nk;
@@ -181,10 +192,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
         const uint32_t soff = (uint32_t)kt * kBStep;
 #pragma unroll
-        for (int j = 0; j < BP_FN; ++j) {
-            bq[S][j][0] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, 0), voffB[j]), soff);
-            bq[S][j][1] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, 1), voffB[j] + kBHalf), soff);
-        }
+        for (int j = 0; j < BP_FN; ++j)
+#pragma unroll
+            for (int h = 0; h < BH; ++h)
+                bq[S][j][h] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, h), voffB[j] + (uint32_t)h * kBHalf),
+                                         soff);
         issue_fence();
     };
 
@@ -204,7 +216,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     FragT fa[NG];
     auto frag_addr = [&](int stage, int g, int half) -> const uint8_t * {
         const int i = g % BP_FM;
-        const int c = !WIDE ? (g / BP_FM) * 4 + q : half * 4 + q;
+        const int c = W4 ? 2 * q + g / BP_FM : (!WIDE ? (g / BP_FM) * 4 + q : half * 4 + q);
         const int row = wm * BP_WTM + i * 16 + r16;
         return lds + stage * BP_STAGE + row * kTileKBytes + swz_chunk(row, c) * kChunkBytes;
     };
@@ -260,13 +272,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
             break;
         }
     };
+    // W4: the current step's B operands unpacked to int8 (set at step start).
+    u32x4 ub[BP_FN][2];
     auto mma_group = [&](int g, auto set_c, auto gp_c) {
         constexpr int S = decltype(set_c)::value;
         constexpr int GP = decltype(gp_c)::value;            // step position in its scale group
         const int i = g % BP_FM;
 #pragma unroll
         for (int j = 0; j < BP_FN; ++j) {
-            if constexpr (ELEM == kMx8)
+            if constexpr (INT) {
+                const u32x4 bx = W4 ? ub[j][g / BP_FM] : bq[S][j][W4 ? 0 : g / BP_FM];
+                if constexpr (ACCA)
+                    mfma_i8_a(acc[i][j], bx, fa[g]);
+                else
+                    acc[i][j] = mfma_i8(bx, fa[g], acc[i][j]);
+            } else if constexpr (ELEM == kMx8)
                 mfma_mx(i, j, join32(bq[S][j][0], bq[S][j][1]), fa[g], GP);
             else if constexpr (ELEM == kMx4)
                 mfma_mx(i, j, bq[S][j][g / BP_FM], fa[g], 2 * GP + g / BP_FM);
@@ -323,6 +343,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         const int st = kt % NS;
         wait_vm(ic<kVmStart>{});
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (W4) {
+#pragma unroll
+            for (int j = 0; j < BP_FN; ++j) {
+                ub[j][0] = int4x32_half_to_i8(bq[CUR][j][0], 0);
+                ub[j][1] = int4x32_half_to_i8(bq[CUR][j][0], 1);
+            }
+        }
         if constexpr (MX && GP == 0) {
 #pragma unroll
             for (int t = 0; t < SQA; ++t)
@@ -344,7 +371,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                 if (g < NG - PD) {
 #pragma unroll
                     for (int b = g * BP_BR / (NG - PD); b < (g + 1) * BP_BR / (NG - PD); ++b)
-                        issue_b_one(kt + 1, ic<1 - CUR>{}, b >> 1, b & 1);
+                        issue_b_one(kt + 1, ic<1 - CUR>{}, b / BH, b % BH);
                 } else {
                     const int go = g - (NG - PD);
                     if (go == 0) {
@@ -432,7 +459,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
         for (int i = 0; i < BP_FM; ++i) {
             const int row = wm * BP_WTM + i * 16 + r16;
             const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
-            const f32x4 v = epi_apply4(ev, acc[i][j], epi_row_scale(ev, m0 + row), sb, bz);
+            const f32x4 a = INT ? int_acc_to_f32(acc[i][j], W4 ? 0.0625f : 1.f) : acc[i][j];
+            const f32x4 v = epi_apply4(ev, a, epi_row_scale(ev, m0 + row), sb, bz);
             if constexpr (OUT == kOutF32)
                 buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
             else
@@ -475,14 +503,23 @@ static const TiledVariant kPipe[] = {
     TG_PIPE_S(kMx8, kOutBf16, false, 1, 4, 4, 3, true, true),
     TG_PIPE_S(kMx4, kOutBf16, true, 1, 4, 4, 12, true, true),
     TG_PIPE_S(kMx4, kOutBf16, false, 1, 4, 4, 12, true, true),
+    // integer operands: 8 waves, then 4 waves with AGPR accumulators
+    TG_PIPE_S(kI8, kOutBf16, true, 1, 8, 4, 6, true, true),     // 16
+    TG_PIPE_S(kI8, kOutBf16, false, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kW4A8, kOutBf16, true, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kW4A8, kOutBf16, false, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kI8, kOutBf16, true, 1, 4, 4, 12, true, true),    // 20
+    TG_PIPE_S(kI8, kOutBf16, false, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kW4A8, kOutBf16, true, 1, 4, 4, 12, true, true),
+    TG_PIPE_S(kW4A8, kOutBf16, false, 1, 4, 4, 12, true, true),
     // sweep alternatives
-    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),           // 12: loads in bursts
-    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 5, true, true),   // 13
-    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 7, true, true),   // 14
-    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 5, 6, true, true),   // 15
-    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 16
-    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 17
-    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 18: loads in bursts
+    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),           // 24: loads in bursts
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 5, true, true),   // 25
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 7, true, true),   // 26
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 5, 6, true, true),   // 27
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 28
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 29
+    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 30: loads in bursts
 };
 
 const TiledVariant *pipe_variants(int *count)

@@ -10,8 +10,8 @@
 namespace tg {
 
 // kMx8 / kMx4: MX block-scaled e4m3 / e2m1 operands, one E8M0 scale per 32
-// elements along K.
-enum Elem { kBf16 = 0, kFp8 = 1, kMx8 = 2, kMx4 = 3 };
+// elements along K.  kI8: int8 A and B; kW4A8: int8 A, packed int4 B.
+enum Elem { kBf16 = 0, kFp8 = 1, kMx8 = 2, kMx4 = 3, kI8 = 4, kW4A8 = 5 };
 enum Out { kOutF32 = 0, kOutBf16 = 1 };
 
 // Epilogue operands (device pointers): C = act((acc * s_a) * s_b + bias).
@@ -31,7 +31,7 @@ struct TiledArgs {
     void *C;
     EpiArgs epi;
     int32_t M, N;
-    int32_t kbytes;         // bytes of one row of A and of B (K * elem_bytes)
+    int32_t kbytes;         // bytes of one row of A (K * elem_bytes)
     int32_t k_tiles;        // ceil(kbytes / 128)
     int32_t tail_bytes;     // valid bytes of the last K tile: 64 or 128
     int32_t grid, tiles_m, tiles_n, group_m;
@@ -40,6 +40,7 @@ struct TiledArgs {
     const uint8_t *sa_img;
     const uint8_t *sb_img;
     int32_t s_groups;
+    int32_t kbytes_b;       // bytes of one row of B (kbytes, or kbytes / 2 for int4 B)
 };
 
 // Block-scale image of an MX operand with R rows: the bytes

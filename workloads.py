@@ -20,6 +20,12 @@ Recipe (every array is raw element bits in row-major order):
   for an all-zero block), and each element is X / 2^exp rounded to the
   element format (nearest, ties to even, saturating).  MXFP4 packs two
   elements per byte, the even one in the low nibble.
+* int8 / W4A8 (int8 A, packed int4 B): symmetric absmax quantisation per row
+  of A and per row of B (one output channel of C): s = float32(amax / 127)
+  (int8) or float32(amax / 7) (int4), q = clip(rint(X / s), -127, 127) or
+  (-7, 7).  int4 packs two values per byte, the even element in the low
+  nibble.  The per-row scales are returned as vectors for the epilogue,
+  C = (acc * s_a[row]) * s_b[col].
 
 A is M x K, B is N x K (K contiguous in both), C is M x N.
 """
@@ -38,7 +44,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str          # "bf16", "e4m3", "mxfp8" or "mxfp4" (element type of A and B)
+    dtype: str          # "bf16", "e4m3", "mxfp8", "mxfp4", "i8" or "w4a8" (int8 A, int4 B)
     out: str            # "f32" or "bf16"
     layout: str         # "bt" (B as N x K) or "bt_preshuffled"
     dist_a: tuple
@@ -52,7 +58,12 @@ class Workload:
 
     @property
     def elem_bytes(self) -> float:
-        return {"bf16": 2, "e4m3": 1, "mxfp8": 1, "mxfp4": 0.5}[self.dtype]
+        """Bytes per element of A."""
+        return {"bf16": 2, "e4m3": 1, "mxfp8": 1, "mxfp4": 0.5, "i8": 1, "w4a8": 1}[self.dtype]
+
+    @property
+    def b_elem_bytes(self) -> float:
+        return 0.5 if self.dtype == "w4a8" else self.elem_bytes
 
     @property
     def out_bytes(self) -> int:
@@ -61,8 +72,14 @@ class Workload:
     @property
     def min_bytes(self) -> int:
         """Each operand read once and C written once."""
-        scales = (self.M + self.N) * (self.K // 32) if self.dtype.startswith("mx") else 0
-        return int((self.M * self.K + self.N * self.K) * self.elem_bytes) + scales + self.M * self.N * self.out_bytes
+        if self.dtype.startswith("mx"):
+            scales = (self.M + self.N) * (self.K // 32)
+        elif self.dtype in ("i8", "w4a8"):
+            scales = (self.M + self.N) * 4              # fp32 per-row / per-column scale vectors
+        else:
+            scales = 0
+        return (int(self.M * self.K * self.elem_bytes + self.N * self.K * self.b_elem_bytes) + scales
+                + self.M * self.N * self.out_bytes)
 
 
 WORKLOADS = {
@@ -87,6 +104,12 @@ WORKLOADS = {
     "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "mxfp4", "bf16", "bt_preshuffled",
                            ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1007,
                            "MX block scales, e2m1 elements"),
+    "i8_8192": Workload("i8_8192", 8192, 8192, 8192, "i8", "bf16", "bt_preshuffled",
+                        ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1008,
+                        "per-row / per-channel absmax scales"),
+    "w4a8_8192": Workload("w4a8_8192", 8192, 8192, 8192, "w4a8", "bf16", "bt_preshuffled",
+                          ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1009,
+                          "int8 A, int4 B, per-row / per-channel absmax scales"),
 }
 
 
@@ -155,6 +178,22 @@ def quantize_mx(x: np.ndarray, fmt: str):
     return q, (e + 127).astype(np.uint8)
 
 
+def quantize_int_rows(x: np.ndarray, qmax: int):
+    """Symmetric per-row absmax quantisation: (int8 values, float32 scales)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=1) if x.size else np.zeros(x.shape[0], np.float32)
+    s = np.where(amax > 0, amax / np.float32(qmax), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(x / s[:, None]), -qmax, qmax).astype(np.int8)
+    return q, s
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """rows x K int4 values (int8 storage, -8..7) -> rows x K/2 bytes, the
+    even element in the low nibble."""
+    n = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+
+
 def mx_int_inputs(M: int, N: int, K: int, fmt: str, seed: int):
     """Small MX inputs whose products and sums are exact in fp32: e4m3
     integers in [-4, 4] or any e2m1 code, with scales 2^-2 .. 2^2."""
@@ -180,6 +219,8 @@ class Inputs:
     scale_b: float = 1.0
     sa_blocks: np.ndarray | None = None   # MX: E8M0 scales, M x K/32
     sb_blocks: np.ndarray | None = None   # MX: E8M0 scales, N x K/32
+    sa_rows: np.ndarray | None = None     # int8 / W4A8: float32 scale per row of A
+    sb_cols: np.ndarray | None = None     # int8 / W4A8: float32 scale per row of B (column of C)
 
 
 def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
@@ -197,14 +238,30 @@ def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
         qa, ea = quantize_mx(a, w.dtype)
         qb, eb = quantize_mx(b, w.dtype)
         return Inputs(qa, qb, sa_blocks=ea, sb_blocks=eb)
+    if w.dtype in ("i8", "w4a8"):
+        qa, sa = quantize_int_rows(a, 127)
+        if w.dtype == "i8":
+            qb, sb = quantize_int_rows(b, 127)
+            qb = qb.view(np.uint8)
+        else:
+            qb, sb = quantize_int_rows(b, 7)
+            qb = pack_int4(qb)
+        return Inputs(qa.view(np.uint8), qb, sa_rows=sa, sb_cols=sb)
     qa, sa = quantize_e4m3(a)
     qb, sb = quantize_e4m3(b)
     return Inputs(qa, qb, sa, sb)
 
 
 def int_inputs(M: int, N: int, K: int, dtype: str, seed: int, lo: int = -4, hi: int = 4) -> Inputs:
-    """Integer-valued inputs in [lo, hi] (exact in bf16 and e4m3 for |v| <= 16)."""
+    """Integer-valued inputs in [lo, hi] (exact in bf16 and e4m3 for |v| <= 16;
+    for "i8" any range within int8, for "w4a8" B clipped to the int4 range)."""
     rng = np.random.Generator(np.random.PCG64(seed))
+    if dtype in ("i8", "w4a8"):
+        a = rng.integers(lo, hi + 1, size=(M, K)).astype(np.int8)
+        if dtype == "i8":
+            return Inputs(a.view(np.uint8), rng.integers(lo, hi + 1, size=(N, K)).astype(np.int8).view(np.uint8))
+        b = rng.integers(max(lo, -8), min(hi, 7) + 1, size=(N, K)).astype(np.int8)
+        return Inputs(a.view(np.uint8), pack_int4(b))
     a = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
     b = rng.integers(lo, hi + 1, size=(N, K)).astype(np.float32)
     if dtype == "bf16":
