@@ -13,6 +13,9 @@ Contents
 * ``gemm_bt_mx`` / ``gemm_bt_mx_entries`` -- the same loop for MX
   block-scaled operands (MXFP8: e4m3 elements, MXFP4: e2m1 elements, one
   E8M0 scale per 32 elements along K).
+* ``gemm_ab`` / ``gemm_ab_entries`` -- C = A * B with B stored K x N (the
+  naive template's layout): b(n, k) is B[k][n], i.e. the same sum with the
+  stored B read column-wise.
 * ``gemm_bt_int`` / ``gemm_bt_int_entries`` -- exact integer sums (int64)
   for an int8 A and an int8 or packed int4 B (W4A8).
 * ``round_bf16`` -- the oracle's own round-to-nearest-even to bf16.
@@ -367,3 +370,20 @@ def gemm_bt_int_entries(A, B, K: int, rows, cols, fmt: str = "i8"):
     _load().oracle_gemm_bt_int_entries(K, bb, A.ctypes.data, B.ctypes.data, rows.size, rows.ctypes.data,
                                        cols.ctypes.data, C.ctypes.data, S.ctypes.data)
     return C.astype(np.float64), S.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# B stored K x N (C = A * B)
+# ---------------------------------------------------------------------------
+def gemm_ab(A: np.ndarray, B_kn: np.ndarray, dtype: str = "bf16", sigma: float = 1.0, want_s: bool = True):
+    """C_ref[m][n] = sigma * sum_k a(m,k) * B_kn[k][n] for B stored K x N:
+    the element B_kn[k][n] is b(n,k) of the N x K form, so this is gemm_bt on
+    the transposed copy."""
+    B_kn = _operand(B_kn, dtype)
+    return gemm_bt(A, np.ascontiguousarray(B_kn.T), dtype=dtype, sigma=sigma, want_s=want_s)
+
+
+def gemm_ab_entries(A: np.ndarray, B_kn: np.ndarray, rows, cols, dtype: str = "bf16", sigma: float = 1.0):
+    """gemm_ab at the (rows[t], cols[t]) entries only."""
+    B_kn = _operand(B_kn, dtype)
+    return gemm_bt_entries(A, np.ascontiguousarray(B_kn.T), rows, cols, dtype=dtype, sigma=sigma)

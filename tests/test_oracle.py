@@ -501,3 +501,32 @@ def test_int_rejects_bad_shapes(oracle_mod):
         oracle_mod.gemm_bt_int(np.zeros((2, 64), np.uint8), np.zeros((2, 32), np.uint8), 64, "i8")
     with pytest.raises(ValueError):
         oracle_mod.gemm_bt_int(np.zeros((2, 64), np.uint8), np.zeros((2, 64), np.uint8), 64, "i4")
+
+
+# ---------------------------------------------------------------------------
+# B stored K x N
+# ---------------------------------------------------------------------------
+def test_gemm_ab_is_the_plain_matrix_product(oracle_mod):
+    # integer values: every sum exact; numpy's int64 matmul is an independent
+    # definition of C = A @ B with B as K x N (non-square, so a transposed
+    # operand would not even have the right shape)
+    rng = np.random.default_rng(21)
+    a = rng.integers(-9, 10, (5, 24))
+    b = rng.integers(-9, 10, (24, 7))
+    C, S = oracle_mod.gemm_ab(bf16(a.astype(np.float32)), bf16(b.astype(np.float32)))
+    assert C.shape == (5, 7)
+    assert np.array_equal(C, (a @ b).astype(np.float64))
+    assert np.array_equal(S, (np.abs(a) @ np.abs(b)).astype(np.float64))
+    rows, cols = np.array([0, 4, 2]), np.array([6, 0, 3])
+    Ce, Se = oracle_mod.gemm_ab_entries(bf16(a.astype(np.float32)), bf16(b.astype(np.float32)), rows, cols)
+    assert np.array_equal(Ce, C[rows, cols]) and np.array_equal(Se, S[rows, cols])
+
+
+def test_gemm_ab_unit_vectors(oracle_mod):
+    # A = e_1 picks row 1 of B: C[0][n] = B[1][n]
+    K, N = 4, 6
+    a = np.zeros((1, K), np.float32)
+    a[0, 1] = 1.0
+    b = np.arange(K * N, dtype=np.float32).reshape(K, N)
+    C, _ = oracle_mod.gemm_ab(bf16(a), bf16(b))
+    assert np.array_equal(C[0], b[1].astype(np.float64))
