@@ -26,7 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}   # MI355X dense peaks
+# MI355X dense peaks (TFLOP/s; int8: TOP/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "i8": 5000.0, "w4a8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_preshuffled"
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE /
@@ -43,10 +44,13 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
     launch stream.  With rotate > 1, that many independent input/output sets
     are cycled so the operands are not served from the last-level cache.
     With epi (an epilogue name), gemm_run_ex is timed instead, with per-row
-    and per-column scale vectors and a bias vector."""
+    and per-column scale vectors and a bias vector.  Integer workloads run
+    through gemm_run_ex with their per-row / per-channel dequantisation
+    scales."""
     code = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
             ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16, ("mxfp8", "bf16"): tg.GEMM_MXFP8_OUT_BF16,
-            ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16}[(w.dtype, w.out)]
+            ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16, ("i8", "bf16"): tg.GEMM_I8_OUT_BF16,
+            ("w4a8", "bf16"): tg.GEMM_W4A8_OUT_BF16}[(w.dtype, w.out)]
     plan = tg.Plan(w.M, w.N, w.K, code, tg.LAYOUTS[w.layout])
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
@@ -85,6 +89,13 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
 
         def launch(A, B, C):
             plan.run_mx(A.data_ptr(), imgs[0].data_ptr(), B.data_ptr(), imgs[1].data_ptr(), C.data_ptr(), stream=s)
+    elif w.dtype in ("i8", "w4a8"):
+        qa = torch.from_numpy(inp.sa_rows).cuda()
+        qb = torch.from_numpy(inp.sb_cols).cuda()
+
+        def launch(A, B, C):
+            plan.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream=s, scale_a=qa.data_ptr(),
+                        scale_a_per_row=True, scale_b=qb.data_ptr(), scale_b_per_col=True)
     elif epi is None:
         def launch(A, B, C):
             plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
@@ -179,7 +190,8 @@ def main():
         log("bench: copy calibration %d MiB x 3" % args.calibrate_copy)
         del src, dst
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
-        "bf16_4096", "bf16_skinny_32x8192x8192", "e4m3_8192", "mxfp8_8192", "mxfp4_8192"])
+        "bf16_4096", "bf16_4096_bn", "bf16_skinny_32x8192x8192", "e4m3_8192", "mxfp8_8192", "mxfp4_8192",
+        "i8_8192", "w4a8_8192"])
     results = {}
     inputs = {}
     for name in names:
@@ -244,13 +256,13 @@ def main():
     }
     if r["shuf_ms"] is not None:
         line["preshuffle"] = {"ms": round(r["shuf_ms"], 4),
-                              "GB/s": round(2 * w.N * w.K * w.elem_bytes / (r["shuf_ms"] * 1e-3) / 1e9, 1)}
+                              "GB/s": round(2 * w.N * w.K * w.b_elem_bytes / (r["shuf_ms"] * 1e-3) / 1e9, 1)}
     also = {}
     for name, rr in results.items():
         if name == head:
             continue
         ww = W.WORKLOADS[name.split("+")[0]]
-        also[name] = {"ms": round(rr["ms"], 5), "TFLOP/s": round(rr["tflops"], 2),
+        also[name] = {"ms": round(rr["ms"], 5), ("TOP/s" if ww.dtype in ("i8", "w4a8") else "TFLOP/s"): round(rr["tflops"], 2),
                       "frac_mfma_peak": round(rr["tflops"] / PEAK_TFLOPS[ww.dtype], 4),
                       "GB/s": round(rr["gbs"], 1), "frac_hbm_peak": round(rr["gbs"] / PEAK_HBM_GBS, 4),
                       "tile": "%dx%d" % (rr["info"]["tile_m"], rr["info"]["tile_n"]),

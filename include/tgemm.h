@@ -18,6 +18,15 @@
  *              written by gemm_preshuffle_b (see there)
  *   C  M x N    elements of the output type           (ldc = N)
  *
+ * GEMM_LAYOUT_BN stores B as K x N row-major (ldb = N), the layout of the
+ * pages' naive GEMM template (FlyDSL "Kernel Authoring" skill, section 8
+ * "Common Patterns and Recipes", the naive GEMM's (K, N):(N, 1) view of B),
+ * so C = A * B with b(n,k) = B[k][n].  The kernel reads it through the
+ * gfx950 LDS transpose load (ds_read_b64_tr_b16, the 16-lane copy atom of
+ * FlyDSL's "add-target-atom-op" skill, section 1.5.2 "Shape-product
+ * invariants").  bf16 inputs only; K * N * 2 < 2^31; no
+ * pre-shuffled image (gemm_preshuffle_b rejects such plans).
+ *
  * Every pointer passed to gemm_preshuffle_b / gemm_run is a DEVICE pointer
  * owned by the caller.  The library allocates no device memory, never
  * synchronises, and launches asynchronously on the given stream; a plan holds
@@ -61,7 +70,8 @@ typedef enum {
 
 typedef enum {
     GEMM_LAYOUT_BT = 0,               /* B is N x K row-major                        */
-    GEMM_LAYOUT_BT_PRESHUFFLED = 1    /* B is the image written by gemm_preshuffle_b */
+    GEMM_LAYOUT_BT_PRESHUFFLED = 1,   /* B is the image written by gemm_preshuffle_b */
+    GEMM_LAYOUT_BN = 2                /* B is K x N row-major: C = A * B (bf16 only)  */
 } gemm_layout;
 
 typedef struct gemm_plan gemm_plan;   /* opaque, immutable after creation */

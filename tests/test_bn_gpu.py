@@ -1,0 +1,108 @@
+"""Parity of C = A * B with B stored K x N (GEMM_LAYOUT_BN, read through
+the LDS transpose load) with the oracle's gemm_ab.
+
+* Integer-valued bf16 inputs (exact sums): bit-exact on both tile sizes and
+  both outputs, with M and N tails, a half-filled last K step (K % 64 ==
+  32) and the smallest shapes.
+* N(0,1) inputs: within the GEMM bound; the 4096^3 workload on sampled
+  entries; a fused epilogue.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def set_tile(monkeypatch, tile):
+    monkeypatch.delenv("TGEMM_TILE", raising=False)
+    if tile:
+        monkeypatch.setenv("TGEMM_TILE", tile)
+
+
+def int_kn(M, N, K, seed):
+    """Integer-valued bf16 A (M x K) and B stored K x N."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    b = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    return W.to_bf16_bits(a), W.to_bf16_bits(b)
+
+
+def _exact(oracle_mod, bits, out, C):
+    if out == "f32":
+        want = C.astype(np.float32).view(np.uint32)
+    else:
+        want = oracle_mod.round_bf16(C)
+    bad = bits != want
+    assert not bad.any(), "%d mismatches, first at %s: got %r want %r" % (
+        int(bad.sum()), np.argwhere(bad)[0], decode(bits)[tuple(np.argwhere(bad)[0])], C[tuple(np.argwhere(bad)[0])])
+
+
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(300, 272, 1056), (256, 512, 1024), (1, 16, 32), (77, 48, 96)])
+def test_bn_bit_exact(oracle_mod, monkeypatch, tile, out, M, N, K):
+    set_tile(monkeypatch, tile)
+    say("case bn exact", tile, out, M, N, K)
+    A, B = int_kn(M, N, K, seed=M + N + K)
+    bits, info = run_gemm(A, B, M, N, K, "bf16", out, "bn", return_plan_info=True)
+    assert info["tile_m"] == int(tile.split("x")[0])
+    C, _ = oracle_mod.gemm_ab(A, B)
+    _exact(oracle_mod, bits, out, C)
+
+
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+def test_bn_random_within_bound(oracle_mod, monkeypatch, tile):
+    M, N, K = 520, 784, 1504
+    set_tile(monkeypatch, tile)
+    say("case bn random", tile, M, N, K)
+    inp = W.make_inputs(W.WORKLOADS["bf16_4096_bn"], M=M, N=N, K=K, seed=41)
+    assert inp.B.shape == (K, N)
+    bits = run_gemm(inp.A, inp.B, M, N, K, "bf16", "bf16", "bn")
+    C, S = oracle_mod.gemm_ab(inp.A, inp.B)
+    r = assert_within_bound(decode(bits), C, S, "bf16", "bn random " + tile)
+    say("  worst err/bound", r)
+
+
+def test_bn_with_epilogue(oracle_mod, monkeypatch):
+    M, N, K = 300, 272, 1056
+    set_tile(monkeypatch, None)
+    say("case bn epilogue", M, N, K)
+    inp = W.make_inputs(W.WORKLOADS["bf16_4096_bn"], M=M, N=N, K=K, seed=43)
+    rng = np.random.default_rng(44)
+    e = dict(scale_a=rng.uniform(0.05, 0.1, M), scale_b=rng.uniform(0.5, 2.0, N), bias=rng.normal(0, 1, N),
+             kind="bias_gelu")
+    bits = run_gemm(inp.A, inp.B, M, N, K, "bf16", "bf16", "bn", epi=e)
+    acc, S = oracle_mod.gemm_ab(inp.A, inp.B)
+    want = oracle_mod.epilogue(acc, e["scale_a"], e["scale_b"], e["bias"], e["kind"])
+    scale = np.abs(e["scale_a"][:, None] * e["scale_b"][None, :])
+    r = assert_epilogue_within_bound(decode(bits), want, S * scale, np.abs(acc) * scale,
+                                     np.abs(e["bias"])[None, :], "bf16", "bias_gelu", "bn epilogue")
+    say("  worst err/bound", r)
+
+
+def test_bn_full_size_sampled(oracle_mod, monkeypatch):
+    set_tile(monkeypatch, None)
+    w = W.WORKLOADS["bf16_4096_bn"]
+    say("case bn full-size", w.name)
+    inp = W.make_inputs(w)
+    bits = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout)
+    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    C, S = oracle_mod.gemm_ab_entries(inp.A, inp.B, rows, cols)
+    r = assert_within_bound(decode(bits[rows, cols]), C, S, "bf16", w.name)
+    say("  worst err/bound", r)
+    assert np.all(np.isfinite(decode(bits)))

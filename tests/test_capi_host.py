@@ -293,6 +293,24 @@ def test_int_run_guards(lib):
         assert lib.gemm_preshuffle_b(p.handle, B, B + 256 * 128 - 16, None) == tg.GEMM_ERR_INVALID_ARG
 
 
+def test_bn_layout_plans(lib):
+    for dtype in (tg.GEMM_BF16_OUT_BF16, tg.GEMM_BF16_OUT_F32):
+        for M, N, K, tile in [(4096, 4096, 4096, 256), (300, 272, 1056, 128), (8, 16, 32, 128)]:
+            with tg.Plan(M, N, K, dtype, tg.GEMM_LAYOUT_BN) as p:
+                info = p.info()
+                assert info["kernel"] == 0 and info["tile_m"] == tile and info["threads"] == 256
+                assert tg.gemm_preshuffled_b_bytes(p.handle) == 0
+                assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == ((K, 2 * N), (2 * N, 1))
+                assert lib.gemm_preshuffle_b(p.handle, 0x100000, 0x200000, None) == tg.GEMM_ERR_INVALID_ARG
+    for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_I8_OUT_BF16, tg.GEMM_W4A8_OUT_BF16):
+        with pytest.raises(tg.GemmError, match="bf16"):
+            tg.Plan(256, 256, 256, dtype, tg.GEMM_LAYOUT_BN)
+    with pytest.raises(tg.GemmError, match="2\\^31"):
+        tg.Plan(256, 1 << 16, 1 << 14, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)
+    with pytest.raises(tg.GemmError):
+        tg.Plan(256, 256, 256, tg.GEMM_BF16_OUT_BF16, 3)
+
+
 def test_mx_entry_point_guards(lib):
     A, B, C, SA, SB = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
     with tg.Plan(256, 256, 256, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:

@@ -94,6 +94,7 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     int n = 0;
     const tg::TiledVariant *v = tg::tiled_variants(&n);
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
+    const bool bkn = I.layout == GEMM_LAYOUT_BN;
     const int elem = elem_of(I.dtype), out = out_of(I.dtype);
     if (is_mx(I.dtype) || is_int(I.dtype)) {
         // MX and integer operands: only the pipelined 256 x 256 kernel (any
@@ -121,7 +122,7 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     // asks for the generic one.  TGEMM_PIPE_VARIANT=<index> picks a sweep
     // variant of the same element type, output and layout.
     const char *pp = getenv("TGEMM_PIPE");
-    if (want_bm == 256 && want_bn == 256 && !(pp && pp[0] == '0')) {
+    if (want_bm == 256 && want_bn == 256 && !bkn && !(pp && pp[0] == '0')) {
         int nb = 0;
         const tg::TiledVariant *b = tg::pipe_variants(&nb);
         if (const char *e = getenv("TGEMM_PIPE_VARIANT")) {
@@ -139,7 +140,7 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     }
     for (int i = 0; i < n; ++i)
         if (v[i].bm == want_bm && v[i].bn == want_bn && v[i].elem == elem && v[i].out == out &&
-            v[i].preshuffled == pre)
+            v[i].preshuffled == pre && v[i].bkn == bkn)
             return &v[i];
     return nullptr;
 }
@@ -185,6 +186,8 @@ Layout view_of(const gemm_plan &p, int view, bool *okv)
     case GEMM_VIEW_A:
         return make({I.M, p.kbytes}, {p.kbytes, 1});
     case GEMM_VIEW_B:
+        if (I.layout == GEMM_LAYOUT_BN)
+            return make({I.K, I.N * I.elem_bytes}, {I.N * I.elem_bytes, 1});
         return make({I.N, Kb}, {Kb, 1});
     case GEMM_VIEW_B_SHUF:
         return make({I.N / 16, Kb / 64, 4, 16, 16}, {16 * Kb, 1024, 256, 16, 1});
@@ -245,8 +248,12 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
         return nullptr;
     }
-    if (layout != GEMM_LAYOUT_BT && layout != GEMM_LAYOUT_BT_PRESHUFFLED) {
+    if (layout != GEMM_LAYOUT_BT && layout != GEMM_LAYOUT_BT_PRESHUFFLED && layout != GEMM_LAYOUT_BN) {
         fail(GEMM_ERR_INVALID_ARG, "unknown layout %d", layout);
+        return nullptr;
+    }
+    if (layout == GEMM_LAYOUT_BN && dtype != GEMM_BF16_OUT_F32 && dtype != GEMM_BF16_OUT_BF16) {
+        fail(GEMM_ERR_UNSUPPORTED, "B stored K x N is supported for bf16 inputs");
         return nullptr;
     }
     if (M < 0 || N < 0 || K < 0) {
@@ -289,6 +296,10 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     }
     if (N * ob * 256 >= (int64_t(1) << 31)) {
         fail(GEMM_ERR_UNSUPPORTED, "N=%lld too large for 32-bit C tile offsets", (long long)N);
+        return nullptr;
+    }
+    if (layout == GEMM_LAYOUT_BN && K * N * 2 >= (int64_t(1) << 31)) {
+        fail(GEMM_ERR_UNSUPPORTED, "B stored K x N must stay below 2^31 bytes (32-bit offsets)");
         return nullptr;
     }
     if (M * kbytes >= (int64_t(1) << 32) && M <= 64) {
@@ -367,7 +378,7 @@ void gemm_plan_destroy(gemm_plan *plan) { delete plan; }
 
 size_t gemm_preshuffled_b_bytes(const gemm_plan *plan)
 {
-    if (!plan)
+    if (!plan || plan->info.layout == GEMM_LAYOUT_BN)
         return 0;
     return (size_t)plan->info.N * (size_t)plan->kbytes_b;
 }
@@ -468,6 +479,8 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
 {
     if (!plan)
         return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
+    if (plan->info.layout == GEMM_LAYOUT_BN)
+        return fail(GEMM_ERR_INVALID_ARG, "the pre-shuffled image is made from B stored N x K");
     const size_t bytes = gemm_preshuffled_b_bytes(plan);
     if (bytes == 0) {
         ok();
@@ -546,6 +559,8 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.N = (int32_t)I.N;
         a.kbytes = (int32_t)plan->kbytes;
         a.kbytes_b = (int32_t)plan->kbytes_b;
+        a.K = (int32_t)I.K;
+        a.ldb_bytes = (int32_t)(I.N * I.elem_bytes);
         a.k_tiles = plan->k_tiles;
         a.tail_bytes = plan->tail_bytes;
         a.grid = I.grid;

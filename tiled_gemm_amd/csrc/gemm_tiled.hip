@@ -20,12 +20,42 @@
 //   * Epilogue: (acc * s_a) * s_b in fp32, round-to-nearest-even to bf16
 //     (or fp32 as is), buffer stores; rows past M and columns past N are
 //     dropped by the buffer range check.
+//   * B stored K x N (BKN, C = A * B, bf16): a step's 64 K-rows of the
+//     tile's BN columns go to LDS by the same direct loads, rows of BN * 2
+//     bytes with the 16-byte chunks XOR-swizzled by bkn_swz(k).  The MFMA
+//     operand (8 consecutive k of one column per lane) comes out of LDS
+//     through the gfx950 transpose read ds_read_b64_tr_b16 (FlyDSL
+//     "add-target-atom-op" skill, section 1.5.2 "Shape-product invariants":
+//     the copy atom ds_read_tr16_b64 spans 16 lanes; the per-lane layout
+//     below was established with an in-bounds probe): within each 16-lane
+//     block, lane i receives element
+//     i % 4 of the 64 bits fetched by lane 4 e + i / 4, for e = 0..3.  So
+//     lane 4 a + b of block q points at row k0 + a, columns c0 + 4 b .. + 3,
+//     and lane i of the block ends up with rows k0 .. k0 + 3 of column
+//     c0 + i.  Rows past K lie past the end of B and read as zeros.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace tg {
 
-template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT>
+// XOR applied to the 16-byte chunk index of K-row k of a K x N B tile: the 4
+// rows one 16-lane block reads at once (k0 .. k0+3, k0 % 4 == 0) get chunk
+// pairs {c, c+1} ^ 2a, disjoint, and rows 8 apart (the next block) differ in
+// bit 3 as well.  A bijection on every aligned group of 16 chunks.
+__device__ inline int bkn_swz(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 64-bit LDS transpose read (16-bit elements), see the header comment.
+__device__ inline u32x2 lds_read_tr16(const uint8_t *p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT, bool BKN = false>
 struct TiledCfg {
     static constexpr int kWaves = 4;
     static_assert(WGM * WGN == kWaves, "4 waves per workgroup");
@@ -34,7 +64,10 @@ struct TiledCfg {
     static constexpr int FM = WTM / 16;              // 16x16 MFMA tiles per wave (rows)
     static constexpr int FN = WTN / 16;              // (columns)
     static constexpr int A_BYTES = BM * kTileKBytes;
-    static constexpr int B_BYTES = BPRE ? 0 : BN * kTileKBytes;
+    static constexpr int B_BYTES = BPRE ? 0 : BN * kTileKBytes;   // N x K: BN rows; K x N: 64 k-rows of BN * 2
+    static constexpr int KN_ROW = BN * 2;                          // bytes of one K-row of a K x N tile (bf16)
+    static constexpr int KN_CPR = KN_ROW / kChunkBytes;            // its 16-byte chunks
+    static_assert(!BKN || (ELEM == kBf16 && !BPRE && KN_CPR >= 16), "K x N B: bf16, staged in LDS");
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS = 2 * STAGE;
     static constexpr int ROUND_BYTES = kTiledThreads * kChunkBytes;   // one 16B load per thread
@@ -44,10 +77,10 @@ struct TiledCfg {
     static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
 };
 
-template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT>
+template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT, bool BKN>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const TiledArgs p)
 {
-    using Cfg = TiledCfg<BM, BN, WGM, WGN, ELEM, BPRE, OUT>;
+    using Cfg = TiledCfg<BM, BN, WGM, WGN, ELEM, BPRE, OUT, BKN>;
     constexpr int FM = Cfg::FM, FN = Cfg::FN;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
 
@@ -62,7 +95,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
     const int rows_b = min(p.N - n0, BN);
     const uint32_t kb = (uint32_t)p.kbytes;
     const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
-    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
+    // K x N B: the resource starts at column n0 and ends with the matrix, so
+    // rows past K read zeros (columns past N read neighbouring data or zeros
+    // and only feed columns of C that are never stored).
+    const uint32_t ldb = (uint32_t)p.ldb_bytes;
+    const auto rB = BKN ? make_rsrc((const uint8_t *)p.B + (size_t)n0 * 2, (uint32_t)((size_t)p.K * ldb - (size_t)n0 * 2))
+                        : make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
     const int nk = p.k_tiles;
     const uint32_t tail = (uint32_t)p.tail_bytes;
 
@@ -85,10 +123,19 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
 #pragma unroll
     for (int r = 0; r < Cfg::B_ROUNDS; ++r) {
         const int pc = (r * 4 + w) * 64 + l;
-        const int row = pc >> 3;
-        const int c = swz_chunk(row, pc & 7);
-        voffB[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
-        tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+        if constexpr (BKN) {
+            // physical chunk pc % CPR of K-row pc / CPR holds logical chunk
+            // (pc % CPR) ^ bkn_swz(row); K tails need no mask (see rB)
+            const int row = pc / Cfg::KN_CPR;
+            const int c = (pc % Cfg::KN_CPR) ^ bkn_swz(row);
+            voffB[r] = (uint32_t)row * ldb + (uint32_t)c * kChunkBytes;
+            tailB |= 1u << r;
+        } else {
+            const int row = pc >> 3;
+            const int c = swz_chunk(row, pc & 7);
+            voffB[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
+            tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+        }
     }
 
     auto issue_lds = [&](int kt, int stage) {
@@ -102,10 +149,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
         }
         if constexpr (!BPRE) {
             uint8_t *sB = sA + Cfg::A_BYTES;
+            // K x N: a step is 64 K-rows of B
+            const uint32_t soffB = BKN ? (uint32_t)kt * 64u * ldb : soff;
 #pragma unroll
             for (int r = 0; r < Cfg::B_ROUNDS; ++r) {
                 const uint32_t vo = (!part || ((tailB >> r) & 1u)) ? voffB[r] : kOobOffset;
-                buf_load16_to_lds(rB, sB + (r * 4 + w) * 1024, vo, soff);
+                buf_load16_to_lds(rB, sB + (r * 4 + w) * 1024, vo, soffB);
             }
         }
     };
@@ -143,6 +192,20 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
     const int q = l >> 4;       // K slot group of this lane
     const int r16 = l & 15;     // row within a 16-row block
 
+    // K x N B: the operand of column block j for sub-step s (k = 32 s + 8 q
+    // .. + 7 of the step, one column per lane) as two transpose reads.
+    auto bkn_frag = [&](const uint8_t *sB, int s, int j) -> u32x4 {
+        const int col = wn * Cfg::WTN + j * 16 + 4 * (r16 & 3);      // this lane's 4 source columns
+        const int c = (col * 2) >> 4, off = (col * 2) & 15;
+        u32x2 h[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int k = 32 * s + 8 * q + 4 * t + (r16 >> 2);
+            h[t] = lds_read_tr16(sB + k * Cfg::KN_ROW + ((c ^ bkn_swz(k)) << 4) + off);
+        }
+        return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
+    };
+
     auto compute = [&](int stage, const u32x4 (&bq)[FN][2]) {
         const uint8_t *sA = lds + stage * Cfg::STAGE;
         const uint8_t *sB = sA + Cfg::A_BYTES;
@@ -155,6 +218,8 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
                 for (int j = 0; j < FN; ++j) {
                     if constexpr (BPRE)
                         bf[j] = bq[j][s];
+                    else if constexpr (BKN)
+                        bf[j] = bkn_frag(sB, s, j);
                     else
                         bf[j] = lds_load16(lds_chunk(sB, wn * Cfg::WTN + j * 16 + r16, c));
                 }
@@ -248,18 +313,19 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT>
+template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT, bool BKN>
 static hipError_t launch_tiled(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, ELEM, BPRE, OUT>), dim3(a.grid),
+    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, ELEM, BPRE, OUT, BKN>), dim3(a.grid),
                        dim3(kTiledThreads), 0, s, a);
     return hipGetLastError();
 }
 
-#define TG_TILED(BM, BN, WGM, WGN, ELEM, BPRE, OUT)                                        \
+#define TG_TILED_L(BM, BN, WGM, WGN, ELEM, BPRE, OUT, BKN)                                 \
     TiledVariant{BM, BN, WGM, WGN, ELEM, OUT, BPRE,                                         \
-                 TiledCfg<BM, BN, WGM, WGN, ELEM, BPRE, OUT>::LDS, 2,                       \
-                 &launch_tiled<BM, BN, WGM, WGN, ELEM, BPRE, OUT>}
+                 TiledCfg<BM, BN, WGM, WGN, ELEM, BPRE, OUT, BKN>::LDS, 2,                  \
+                 &launch_tiled<BM, BN, WGM, WGN, ELEM, BPRE, OUT, BKN>, BKN}
+#define TG_TILED(BM, BN, WGM, WGN, ELEM, BPRE, OUT) TG_TILED_L(BM, BN, WGM, WGN, ELEM, BPRE, OUT, false)
 
 static const TiledVariant kTiled[] = {
     TG_TILED(256, 256, 2, 2, kBf16, false, kOutBf16),
@@ -274,6 +340,11 @@ static const TiledVariant kTiled[] = {
     TG_TILED(128, 128, 2, 2, kBf16, true, kOutF32),
     TG_TILED(128, 128, 2, 2, kFp8, false, kOutBf16),
     TG_TILED(128, 128, 2, 2, kFp8, true, kOutBf16),
+    // B stored K x N (bf16)
+    TG_TILED_L(256, 256, 2, 2, kBf16, false, kOutBf16, true),
+    TG_TILED_L(256, 256, 2, 2, kBf16, false, kOutF32, true),
+    TG_TILED_L(128, 128, 2, 2, kBf16, false, kOutBf16, true),
+    TG_TILED_L(128, 128, 2, 2, kBf16, false, kOutF32, true),
 };
 
 const TiledVariant *tiled_variants(int *count)

@@ -41,6 +41,8 @@ struct TiledArgs {
     const uint8_t *sb_img;
     int32_t s_groups;
     int32_t kbytes_b;       // bytes of one row of B (kbytes, or kbytes / 2 for int4 B)
+    int32_t K;              // elements along K
+    int32_t ldb_bytes;      // B stored K x N: bytes of one row of B (N * elem_bytes)
 };
 
 // Block-scale image of an MX operand with R rows: the bytes
@@ -88,6 +90,7 @@ struct TiledVariant {
     int lds_bytes;
     int lds_stages;         // K steps the LDS ring holds
     hipError_t (*launch)(const TiledArgs &, hipStream_t);
+    bool bkn = false;       // B stored K x N
 };
 
 struct SkinnyVariant {

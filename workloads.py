@@ -27,7 +27,9 @@ Recipe (every array is raw element bits in row-major order):
   nibble.  The per-row scales are returned as vectors for the epilogue,
   C = (acc * s_a[row]) * s_b[col].
 
-A is M x K, B is N x K (K contiguous in both), C is M x N.
+A is M x K, B is N x K (K contiguous in both), C is M x N.  Layout "bn"
+stores B as K x N (N contiguous): it is drawn N x K as above and stored
+transposed.
 """
 from __future__ import annotations
 
@@ -46,7 +48,7 @@ class Workload:
     K: int
     dtype: str          # "bf16", "e4m3", "mxfp8", "mxfp4", "i8" or "w4a8" (int8 A, int4 B)
     out: str            # "f32" or "bf16"
-    layout: str         # "bt" (B as N x K) or "bt_preshuffled"
+    layout: str         # "bt" (B as N x K), "bt_preshuffled" or "bn" (B as K x N)
     dist_a: tuple
     dist_b: tuple
     seed: int
@@ -104,6 +106,9 @@ WORKLOADS = {
     "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "mxfp4", "bf16", "bt_preshuffled",
                            ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1007,
                            "MX block scales, e2m1 elements"),
+    "bf16_4096_bn": Workload("bf16_4096_bn", 4096, 4096, 4096, "bf16", "bf16", "bn",
+                             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1010,
+                             "B stored K x N (C = A * B)"),
     "i8_8192": Workload("i8_8192", 8192, 8192, 8192, "i8", "bf16", "bt_preshuffled",
                         ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1008,
                         "per-row / per-channel absmax scales"),
@@ -233,6 +238,8 @@ def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
     a = _draw(rng, w.dist_a, (M, K))
     b = _draw(rng, w.dist_b, (N, K))
     if w.dtype == "bf16":
+        if w.layout == "bn":
+            b = np.ascontiguousarray(b.T)
         return Inputs(to_bf16_bits(a), to_bf16_bits(b))
     if w.dtype.startswith("mx"):
         qa, ea = quantize_mx(a, w.dtype)
