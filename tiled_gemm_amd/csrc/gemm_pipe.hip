@@ -446,21 +446,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     if constexpr (ACCA)
         mfma_drain();
 
-    // ---- epilogue: scale, bias, activation, convert, store.
+    // ---- epilogue: scale, bias, activation, convert, store.  Row blocks
+    // outside, column blocks inside: a wave writes its adjacent pieces of
+    // one C row back to back, so the L2 merges them into whole lines before
+    // they go to HBM (the other order measured 1.46x the bytes of C written).
     const EpiView ev = epi_view(p.epi, p.M, p.N);
     constexpr int OB = OUT == kOutF32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)p.N * OB;
     const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+    f32x4 sbv[BP_FN], bzv[BP_FN];
 #pragma unroll
     for (int j = 0; j < BP_FN; ++j) {
         const int col = n0 + wn * BP_WTN + j * 16 + 4 * q;
-        const f32x4 sb = epi_col_scale4(ev, col), bz = epi_bias4(ev, col);
+        sbv[j] = epi_col_scale4(ev, col);
+        bzv[j] = epi_bias4(ev, col);
+    }
 #pragma unroll
-        for (int i = 0; i < BP_FM; ++i) {
-            const int row = wm * BP_WTM + i * 16 + r16;
+    for (int i = 0; i < BP_FM; ++i) {
+        const int row = wm * BP_WTM + i * 16 + r16;
+        const float sa = epi_row_scale(ev, m0 + row);
+#pragma unroll
+        for (int j = 0; j < BP_FN; ++j) {
+            const int col = n0 + wn * BP_WTN + j * 16 + 4 * q;
             const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
             const f32x4 a = INT ? int_acc_to_f32(acc[i][j], W4 ? 0.0625f : 1.f) : acc[i][j];
-            const f32x4 v = epi_apply4(ev, a, epi_row_scale(ev, m0 + row), sb, bz);
+            const f32x4 v = epi_apply4(ev, a, sa, sbv[j], bzv[j]);
             if constexpr (OUT == kOutF32)
                 buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
             else

@@ -295,15 +295,17 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(const Tile
     constexpr int OB = OUT == kOutF32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)p.N * OB;
     const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+    // Row blocks outside, column blocks inside: adjacent pieces of a C row
+    // leave back to back and merge in the L2 into whole lines.
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * Cfg::WTN + j * 16 + 4 * q;
-        const f32x4 sb = epi_col_scale4(ev, col), bz = epi_bias4(ev, col);
+    for (int i = 0; i < FM; ++i) {
+        const int row = wm * Cfg::WTM + i * 16 + r16;
+        const float sa = epi_row_scale(ev, m0 + row);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = wm * Cfg::WTM + i * 16 + r16;
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * Cfg::WTN + j * 16 + 4 * q;
             const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
-            const f32x4 v = epi_apply4(ev, acc[i][j], epi_row_scale(ev, m0 + row), sb, bz);
+            const f32x4 v = epi_apply4(ev, acc[i][j], sa, epi_col_scale4(ev, col), epi_bias4(ev, col));
             if constexpr (OUT == kOutF32) {
                 buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
             } else {
