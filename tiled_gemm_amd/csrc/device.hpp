@@ -217,6 +217,22 @@ __device__ inline f32x4 int_acc_to_f32(f32x4 acc, float unit)
 // 64 wait states: longer than any MFMA's result latency.
 __device__ inline void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }
 
+// The drain for accumulators written by the inline-assembly MFMAs above:
+// wait out the MFMA latency, then pass every accumulator through an empty
+// statement that claims to modify it.  The drain alone orders nothing: it
+// has no register operands, so the compiler may move the epilogue's AGPR
+// reads above it, right behind the MFMA that is still writing them.
+template <int FM, int FN>
+__device__ inline void mfma_drain_acc(f32x4 (&acc)[FM][FN])
+{
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            asm volatile("" : "+a"(acc[i][j]));
+}
+
 // Two fp32 -> two bf16 (round to nearest even), packed low-first.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {

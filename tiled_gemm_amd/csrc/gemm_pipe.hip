@@ -444,7 +444,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if constexpr (ACCA)
-        mfma_drain();
+        mfma_drain_acc(acc);
 
     // ---- epilogue: scale, bias, activation, convert, store.  Row blocks
     // outside, column blocks inside: a wave writes its adjacent pieces of
