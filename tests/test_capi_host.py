@@ -151,7 +151,7 @@ def test_raster_is_a_bijection(lib, M, N, K, dtype, layout):
     p.close()
 
 
-def test_plan_choices(lib):
+def test_plan_choices(lib, monkeypatch):
     def info(*a):
         with tg.Plan(*a) as p:
             return p.info()
@@ -159,12 +159,20 @@ def test_plan_choices(lib):
     assert c["kernel"] == 0 and c["out_bytes"] == 4
     c = info(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert (c["tile_m"], c["tile_n"], c["grid"]) == (256, 256, 256)
+    # B stored N x K: both operands through LDS, two 64 KiB stages, 8 waves
+    assert (c["threads"], c["lds_stages"], c["lds_bytes"]) == (512, 2, 128 * 1024)
+    c = info(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+    assert (c["threads"], c["lds_stages"], c["lds_bytes"]) == (512, 4, 128 * 1024)
     c = info(8192, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
     assert c["lds_bytes"] <= 160 * 1024 and c["grid"] == 1024
     c = info(32, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["kernel"] == 1 and c["grid"] == 256
     c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
+    assert c["lds_stages"] == 4                      # fp8: B in registers
+    monkeypatch.setenv("TGEMM_DMA", "0")
+    c = info(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
+    assert (c["threads"], c["lds_stages"]) == (512, 4)
 
 
 @pytest.mark.parametrize("args,code", [

@@ -17,9 +17,11 @@ from gpu_util import assert_epilogue_within_bound, decode, run_gemm, sample_entr
 
 pytestmark = pytest.mark.gpu
 
-# (tile env, layout, M): "256x256" pipelined 8-wave, "256x256q" pipelined
+# (tile env, layout, M): "256x256" the planner's 256 x 256 kernel (bf16 with
+# B stored N x K: both operands through LDS; fp8: pipelined 8-wave),
+# "256x256p" pipelined 8-wave with B in registers, "256x256q" pipelined
 # 4-wave, "256x256g" generic, "128x128" generic, None with M <= 64 skinny.
-PATHS = [("256x256", "bt", None), ("256x256q", "bt_preshuffled", None), ("256x256g", "bt", None),
+PATHS = [("256x256", "bt", None), ("256x256p", "bt", None), ("256x256q", "bt_preshuffled", None), ("256x256g", "bt", None),
          ("128x128", "bt_preshuffled", None), (None, "bt", 33)]
 DTYPES = [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16")]
 
@@ -36,10 +38,13 @@ def say(*a):
 
 
 def set_path(monkeypatch, tile):
-    for k in ("TGEMM_PIPE", "TGEMM_TILE", "TGEMM_PIPE_WAVES"):
+    for k in ("TGEMM_PIPE", "TGEMM_TILE", "TGEMM_PIPE_WAVES", "TGEMM_DMA"):
         monkeypatch.delenv(k, raising=False)
     if tile is None:
         return
+    if tile.endswith("p"):
+        monkeypatch.setenv("TGEMM_DMA", "0")
+        tile = tile[:-1]
     if tile.endswith("g"):
         monkeypatch.setenv("TGEMM_PIPE", "0")
         tile = tile[:-1]

@@ -19,8 +19,10 @@ from gpu_util import assert_within_bound, decode, run_gemm, sample_entries
 pytestmark = pytest.mark.gpu
 
 # (dtype, out, layout, tile) -- tile None = the planner's own choice; "256x256"
-# is the software-pipelined kernel, "256x256g" the generic tiled kernel,
-# "256x256q" the 4-wave pipelined kernel.
+# is the planner's 256 x 256 kernel (bf16 with B stored N x K: both operands
+# through LDS; otherwise the software-pipelined kernel), "256x256p" the
+# software-pipelined kernel with B in registers, "256x256g" the generic tiled
+# kernel, "256x256q" the 4-wave pipelined kernel.
 PATHS = [
     ("bf16", "f32", "bt", "128x128"), ("bf16", "f32", "bt", "256x256"), ("bf16", "f32", "bt", "256x256g"),
     ("bf16", "bf16", "bt", "128x128"), ("bf16", "bf16", "bt", "256x256"), ("bf16", "bf16", "bt", "256x256g"),
@@ -32,6 +34,7 @@ PATHS = [
     ("bf16", "f32", "bt", "256x256q"), ("bf16", "bf16", "bt", "256x256q"),
     ("bf16", "bf16", "bt_preshuffled", "256x256q"), ("bf16", "f32", "bt_preshuffled", "256x256q"),
     ("e4m3", "bf16", "bt", "256x256q"), ("e4m3", "bf16", "bt_preshuffled", "256x256q"),
+    ("bf16", "f32", "bt", "256x256p"), ("bf16", "bf16", "bt", "256x256p"),
 ]
 
 
@@ -52,6 +55,10 @@ def tile_env(monkeypatch):
     def set_tile(t):
         monkeypatch.delenv("TGEMM_PIPE", raising=False)
         monkeypatch.delenv("TGEMM_PIPE_WAVES", raising=False)
+        monkeypatch.delenv("TGEMM_DMA", raising=False)
+        if t and t.endswith("p"):
+            monkeypatch.setenv("TGEMM_DMA", "0")
+            t = t[:-1]
         if t and t.endswith("q"):
             monkeypatch.setenv("TGEMM_PIPE_WAVES", "4")
             t = t[:-1]
@@ -146,7 +153,7 @@ def test_random_within_bound(oracle_mod, tile_env, dtype, out, layout, tile):
 
 # ------------------------------------------------------------------ full-size workloads, sampled
 
-@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_8192_preshuffled", None),
+@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_4096", "256x256p"), ("bf16_8192_preshuffled", None),
                                        ("bf16_skinny_32x8192x8192", None), ("e4m3_8192", None),
                                        ("bf16_8192_preshuffled", "256x256q"), ("e4m3_8192", "256x256q"),
                                        ("bf16_4096", "256x256q")])

@@ -123,6 +123,26 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     // variant of the same element type, output and layout.
     const char *pp = getenv("TGEMM_PIPE");
     if (want_bm == 256 && want_bn == 256 && !bkn && !(pp && pp[0] == '0')) {
+        // bf16 with B stored N x K: both operands staged through LDS by the
+        // loads' own LDS writes (full 128-byte lines of B, where the
+        // register-staged kernel's MFMA lane order can only load half lines).
+        // TGEMM_DMA=0, or a forced pipelined variant or wave count, selects
+        // the register-staged kernel; TGEMM_DMA_VARIANT=<index> picks a sweep
+        // variant of either element type.
+        int nd = 0;
+        const tg::TiledVariant *d = tg::dma_variants(&nd);
+        if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
+            const int k = atoi(e);
+            if (k >= 0 && k < nd && d[k].elem == elem && d[k].out == out && d[k].preshuffled == pre)
+                return &d[k];
+        }
+        const char *dm = getenv("TGEMM_DMA");
+        if (elem == tg::kBf16 && !pre && !(dm && dm[0] == '0') && !getenv("TGEMM_PIPE_VARIANT") &&
+            !getenv("TGEMM_PIPE_WAVES")) {
+            for (int i = 0; i < nd; ++i)
+                if (d[i].elem == elem && d[i].out == out && !d[i].preshuffled)
+                    return &d[i];
+        }
         int nb = 0;
         const tg::TiledVariant *b = tg::pipe_variants(&nb);
         if (const char *e = getenv("TGEMM_PIPE_VARIANT")) {

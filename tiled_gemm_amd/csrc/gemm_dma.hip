@@ -1,0 +1,319 @@
+// GEMM C = A * B^T for 256 x 256 tiles with BOTH operands staged through LDS
+// by the buffer loads' own LDS writes (FlyDSL "Kernel Authoring" skill,
+// section 6 "GEMM Pattern (Preshuffle)": 64-byte K micro-steps, LDS
+// ping-pong, XOR-swizzled tiles, B in MFMA operand order; section 3 "Runtime
+// Loops with Loop-Carried Values" for the load-next / compute-current loop).
+//
+// Why both operands go through LDS on gfx950: a 16-byte load whose data
+// returns to VGPRs costs the MFMA loop about three times what the same bytes
+// cost when the load writes LDS directly (work-skipping measurements of the
+// register-staged B kernel: dropping its B loads gained 22-33%, dropping the
+// same number of LDS-writing A loads 8%).  The pages' preshuffle kernel keeps
+// B out of LDS; here the pre-shuffled image still pays off, because a wave's
+// 1 KiB operand block is contiguous both in HBM and in LDS, so B needs no
+// swizzle and its fragment reads are linear.
+//
+// Workgroup: WGM x WGN waves over a 256 x 256 output tile (2 x 4: each wave
+// 128 rows x 64 columns, 128 fp32 accumulators per lane).  Main-loop step:
+// 128 bytes of K (two 16x16x32 bf16 MFMAs per 16 x 16 block).
+//
+//   LDS     two stages of 64 KiB: A (256 rows x 128 B, chunk-swizzled) and B
+//           (pre-shuffled: 32 operand blocks of 1 KiB; plain: 256 rows x
+//           128 B, chunk-swizzled like A).
+//   DMA     step k+2 is issued right after barrier(k) into the stage step k
+//           has just finished reading, spread over the last PD groups.
+//   Reads   one ordered stream per step: for each half h of the step, the FN
+//           B fragments, then the A fragments of the FM row blocks; each
+//           read runs PD groups ahead of its MFMAs, across the step boundary.
+//   Sync    one barrier per step, PD groups before its end, after
+//           vmcnt(0) (step k+1 has landed) and lgkmcnt(0) (every read of the
+//           stage about to be overwritten has returned).
+//   Epilogue (acc * s_a) * s_b (+ bias, activation) in fp32, RNE to bf16,
+//           buffer stores (rows past M and columns past N dropped).
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace tg {
+
+namespace {
+
+constexpr int DM_BM = 256;
+constexpr int DM_BN = 256;
+constexpr int DM_A = DM_BM * kTileKBytes;      // 32 KiB of A per stage
+constexpr int DM_B = DM_BN * kTileKBytes;      // 32 KiB of B per stage
+constexpr int DM_STAGE = DM_A + DM_B;
+constexpr int DM_LDS = 2 * DM_STAGE;           // 128 KiB
+
+template <int N>
+using dic = std::integral_constant<int, N>;
+
+}  // namespace
+
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const TiledArgs p)
+{
+    static_assert(ELEM == kBf16 || ELEM == kFp8, "bf16 or fp8 e4m3 operands");
+    // fp8: one 128-byte K slice per step and MFMA (16x16x128, 32 bytes per
+    // lane: chunks q and q + 4 of the slice); bf16: two 64-byte halves.
+    constexpr bool F8 = ELEM == kFp8;
+    constexpr int WAVES = WGM * WGN;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int WTM = DM_BM / WGM, WTN = DM_BN / WGN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int AR = DM_A / (THREADS * kChunkBytes);     // A loads per lane and step
+    constexpr int BR = DM_B / (THREADS * kChunkBytes);     // B loads per lane and step
+    constexpr int NL = AR + BR;
+    constexpr int NG = F8 ? FM : 2 * FM;                   // groups per step: half h = g / FM (bf16)
+    static_assert(WAVES == 8, "two waves per SIMD: 128 accumulators per lane in VGPRs");
+    // bf16: next-step B fragments of half 0 reuse the dead registers of
+    // half 0; fp8: B fragments are double-buffered by step parity.
+    static_assert(PD >= 1 && (F8 ? PD < FM : PD <= FM), "prefetch distance");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[DM_LDS];
+
+    const int w = wave_id();
+    const int l = lane_id();
+    const int q = l >> 4, r16 = l & 15;
+    const int wm = w / WGN, wn = w % WGN;
+
+    int tm, tn;
+    tile_of_wg(blockIdx.x, p.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const int m0 = tm * DM_BM, n0 = tn * DM_BN;
+    const int rows_a = min(p.M - m0, DM_BM);
+    const int rows_b = min(p.N - n0, DM_BN);
+    const uint32_t kb = (uint32_t)p.kbytes;
+    const uint32_t kbB = (uint32_t)p.kbytes_b;
+    const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
+    const int nk = p.k_tiles;
+    const uint32_t tail = (uint32_t)p.tail_bytes;
+
+    // ---- load sources.  Load r of a step lands at byte (r * WAVES + w) *
+    // 1024 + 16 l of its operand's half of the stage.  Row-major operands:
+    // that is row pc / 8, physical chunk pc % 8, so the lane fetches logical
+    // chunk swz_chunk(row, pc % 8).  Pre-shuffled B: operand block u = (n
+    // block u / 2, K half u % 2), 1 KiB contiguous in the image.
+    uint32_t voffA[AR], voffB[BR];
+    uint32_t tailA = 0, tailB = 0;
+#pragma unroll
+    for (int r = 0; r < AR; ++r) {
+        const int pc = (r * WAVES + w) * 64 + l;
+        const int row = pc >> 3;
+        const int c = swz_chunk(row, pc & 7);
+        voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
+        tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+    }
+#pragma unroll
+    for (int r = 0; r < BR; ++r) {
+        const int u = r * WAVES + w;
+        if constexpr (BPRE) {
+            voffB[r] = (uint32_t)(u >> 1) * 16u * kbB + (uint32_t)(u & 1) * 1024u + (uint32_t)l * 16u;
+            tailB |= ((uint32_t)((u & 1) * 64) < tail ? 1u : 0u) << r;
+        } else {
+            const int pc = u * 64 + l;
+            const int row = pc >> 3;
+            const int c = swz_chunk(row, pc & 7);
+            voffB[r] = (uint32_t)row * kbB + (uint32_t)c * kChunkBytes;
+            tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+        }
+    }
+    constexpr uint32_t kBStep = BPRE ? 2048u : (uint32_t)kTileKBytes;   // image bytes per step and block row
+    // Load idx (A rounds first, then B) of step kt into stage S.  Loads past
+    // the last step, and the missing half of a half-filled last step, read
+    // out of range and land zeros.
+    // MASK == false: the caller guarantees step kt is whole and in range, so
+    // the offsets need no per-lane selection (no VALU work beside the load).
+    auto issue_one = [&](int kt, auto s_c, int idx, auto mask_c) {
+        constexpr int S = decltype(s_c)::value;
+        if constexpr (!decltype(mask_c)::value) {
+            if (idx < AR)
+                buf_load16_to_lds(rA, lds + S * DM_STAGE + (idx * WAVES + w) * 1024, voffA[idx],
+                                  (uint32_t)kt * kTileKBytes);
+            else
+                buf_load16_to_lds(rB, lds + S * DM_STAGE + DM_A + ((idx - AR) * WAVES + w) * 1024, voffB[idx - AR],
+                                  (uint32_t)kt * kBStep);
+            issue_fence();
+            return;
+        }
+        const bool beyond = kt >= nk;
+        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+        if (idx < AR) {
+            const bool keep = !beyond & (!part | (((tailA >> idx) & 1u) != 0));
+            buf_load16_to_lds(rA, lds + S * DM_STAGE + (idx * WAVES + w) * 1024, keep_or_oob(keep, voffA[idx]),
+                              (uint32_t)kt * kTileKBytes);
+        } else {
+            const int r = idx - AR;
+            const bool keep = !beyond & (!part | (((tailB >> r) & 1u) != 0));
+            buf_load16_to_lds(rB, lds + S * DM_STAGE + DM_A + (r * WAVES + w) * 1024, keep_or_oob(keep, voffB[r]),
+                              (uint32_t)kt * kBStep);
+        }
+        issue_fence();
+    };
+
+    // ---- fragments.  A: row block i, half h -> logical chunk 4 h + q of row
+    // wm * WTM + 16 i + r16 (fp8: chunks q and q + 4).  B: block j of the
+    // wave, half h.
+    auto a_addr = [&](int s, int g, int h) -> const uint8_t * {
+        const int i = g % FM;
+        const int row = wm * WTM + i * 16 + r16;
+        return lds + s * DM_STAGE + row * kTileKBytes + swz_chunk(row, h * 4 + q) * kChunkBytes;
+    };
+    auto b_addr = [&](int s, int h, int j) -> const uint8_t * {
+        const int nb = wn * FN + j;
+        if constexpr (BPRE)
+            return lds + s * DM_STAGE + DM_A + (nb * 2 + h) * 1024 + l * 16;
+        const int row = nb * 16 + r16;
+        return lds + s * DM_STAGE + DM_A + row * kTileKBytes + swz_chunk(row, h * 4 + q) * kChunkBytes;
+    };
+    using FragT = typename std::conditional<F8, i32x8, u32x4>::type;
+    FragT fa[NG];
+    FragT fb[2][FN];        // bf16: [half][block]; fp8: [step parity][block]
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Reads for group t of the step held in stage s: the half's B fragments
+    // first when t opens a half, then t's A fragment.
+    auto load_group = [&](int s, int t) {
+        if constexpr (F8) {
+            if (t == 0) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    fb[s][j] = join32(lds_load16(b_addr(s, 0, j)), lds_load16(b_addr(s, 1, j)));
+            }
+            fa[t] = join32(lds_load16(a_addr(s, t, 0)), lds_load16(a_addr(s, t, 1)));
+        } else {
+            if (t % FM == 0) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    fb[t / FM][j] = lds_load16(b_addr(s, t / FM, j));
+            }
+            fa[t] = lds_load16(a_addr(s, t, t / FM));
+        }
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto step = [&](int kt, auto s_c, auto mask_c) {
+        constexpr int S = decltype(s_c)::value;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g == NG - PD) {
+                // Every read of stage S has been issued: wait for them and for
+                // step kt+1's loads, meet, then refill stage S with step kt+2.
+                __builtin_amdgcn_s_waitcnt(0);
+                barrier();
+            }
+            if (g >= NG - PD) {
+                const int go = g - (NG - PD);
+#pragma unroll
+                for (int idx = go * NL / PD; idx < (go + 1) * NL / PD; ++idx)
+                    issue_one(kt + 2, s_c, idx, mask_c);
+            }
+            if (g + PD < NG)
+                load_group(S, g + PD);
+            else
+                load_group(S ^ 1, g + PD - NG);
+            const int i = g % FM, h = g / FM;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (F8)
+                    acc[i][j] = mfma_fp8x8(fb[S][j], fa[g], acc[i][j]);
+                else
+                    acc[i][j] = mfma_bf16(fb[h][j], fa[g], acc[i][j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- prologue: steps 0 and 1 into stages 0 and 1, the first fragments.
+#pragma unroll
+    for (int idx = 0; idx < NL; ++idx)
+        issue_one(0, dic<0>{}, idx, std::true_type{});
+#pragma unroll
+    for (int idx = 0; idx < NL; ++idx)
+        issue_one(1, dic<1>{}, idx, std::true_type{});
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier();
+#pragma unroll
+    for (int t = 0; t < PD; ++t)
+        load_group(0, t);
+    // Steps run in pairs; a step past nk is a phantom whose operands are all
+    // zeros (its loads read out of range), so it adds exact zeros.
+    // Steps kt < nfull - 2 load whole, in-range steps (kt + 2 < nfull) and
+    // run without masks; the last few steps run the masked form.
+    const int nfull = tail == (uint32_t)kTileKBytes ? nk : nk - 1;
+    int kt = 0;
+    for (; kt + 1 < nfull - 2; kt += 2) {
+        step(kt, dic<0>{}, std::false_type{});
+        step(kt + 1, dic<1>{}, std::false_type{});
+    }
+    for (; kt < nk; kt += 2) {
+        step(kt, dic<0>{}, std::true_type{});
+        step(kt + 1, dic<1>{}, std::true_type{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- epilogue: row blocks outside, column blocks inside, so a wave
+    // writes its adjacent pieces of one C row back to back.
+    const EpiView ev = epi_view(p.epi, p.M, p.N);
+    constexpr int OB = OUT == kOutF32 ? 4 : 2;
+    const uint32_t ldc = (uint32_t)p.N * OB;
+    const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+    f32x4 sbv[FN], bzv[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + 4 * q;
+        sbv[j] = epi_col_scale4(ev, col);
+        bzv[j] = epi_bias4(ev, col);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = wm * WTM + i * 16 + r16;
+        const float sa = epi_row_scale(ev, m0 + row);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + 4 * q;
+            const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
+            const f32x4 v = epi_apply4(ev, acc[i][j], sa, sbv[j], bzv[j]);
+            if constexpr (OUT == kOutF32)
+                buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
+            else
+                buf_store8(rC, u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)}, voff);
+        }
+    }
+}
+
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD>
+static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_dma_kernel<ELEM, OUT, BPRE, WGM, WGN, PD>), dim3(a.grid), dim3(64 * WGM * WGN), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+#define TG_DMA(ELEM, OUT, BPRE, WGM, WGN, PD) \
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, OUT, BPRE, DM_LDS, 2, &launch_dma<ELEM, OUT, BPRE, WGM, WGN, PD>}
+
+static const TiledVariant kDma[] = {
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 4),   // 1
+    TG_DMA(kBf16, kOutF32, false, 2, 4, 4),    // 2
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // 3
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 2),    // 4
+    TG_DMA(kFp8, kOutBf16, true, 1, 8, 3),     // 5
+    TG_DMA(kBf16, kOutBf16, true, 2, 4, 6),    // 6
+};
+
+const TiledVariant *dma_variants(int *count)
+{
+    *count = (int)(sizeof(kDma) / sizeof(kDma[0]));
+    return kDma;
+}
+
+}  // namespace tg

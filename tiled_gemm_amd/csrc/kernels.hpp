@@ -107,6 +107,7 @@ constexpr int kTiledThreads = 256;
 
 const TiledVariant *tiled_variants(int *count);
 const TiledVariant *pipe_variants(int *count);
+const TiledVariant *dma_variants(int *count);
 const SkinnyVariant *skinny_variants(int *count);
 hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
 hipError_t launch_bscale_image(const BscaleArgs &, hipStream_t);
