@@ -301,15 +301,22 @@ def test_int_run_guards(lib):
         assert lib.gemm_preshuffle_b(p.handle, B, B + 256 * 128 - 16, None) == tg.GEMM_ERR_INVALID_ARG
 
 
-def test_bn_layout_plans(lib):
+def test_bn_layout_plans(lib, monkeypatch):
     for dtype in (tg.GEMM_BF16_OUT_BF16, tg.GEMM_BF16_OUT_F32):
-        for M, N, K, tile in [(4096, 4096, 4096, 256), (300, 272, 1056, 128), (8, 16, 32, 128)]:
+        # 256 x 256 tiles: 8 waves, both operands staged in LDS (2 stages);
+        # 128 x 128: the generic 4-wave tiled kernel
+        for M, N, K, tile, threads in [(4096, 4096, 4096, 256, 512), (300, 272, 1056, 128, 256),
+                                       (8, 16, 32, 128, 256)]:
             with tg.Plan(M, N, K, dtype, tg.GEMM_LAYOUT_BN) as p:
                 info = p.info()
-                assert info["kernel"] == 0 and info["tile_m"] == tile and info["threads"] == 256
+                assert info["kernel"] == 0 and info["tile_m"] == tile and info["threads"] == threads
                 assert tg.gemm_preshuffled_b_bytes(p.handle) == 0
                 assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == ((K, 2 * N), (2 * N, 1))
                 assert lib.gemm_preshuffle_b(p.handle, 0x100000, 0x200000, None) == tg.GEMM_ERR_INVALID_ARG
+        monkeypatch.setenv("TGEMM_DMA", "0")
+        with tg.Plan(4096, 4096, 4096, dtype, tg.GEMM_LAYOUT_BN) as p:
+            assert p.info()["threads"] == 256                # the generic tiled kernel
+        monkeypatch.delenv("TGEMM_DMA")
     for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_I8_OUT_BF16, tg.GEMM_W4A8_OUT_BF16):
         with pytest.raises(tg.GemmError, match="bf16"):
             tg.Plan(256, 256, 256, dtype, tg.GEMM_LAYOUT_BN)

@@ -118,31 +118,35 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
         const int64_t big = ((I.M + 255) / 256) * ((I.N + 255) / 256);
         want_bm = want_bn = big >= 128 ? 256 : 128;
     }
-    // 256 x 256 tiles: the software-pipelined kernel, unless TGEMM_PIPE=0
-    // asks for the generic one.  TGEMM_PIPE_VARIANT=<index> picks a sweep
-    // variant of the same element type, output and layout.
+    // 256 x 256 tiles.  bf16 with B stored N x K or K x N: both operands
+    // staged through LDS by the loads' own LDS writes (gemm_dma.hip: whole
+    // 128-byte lines of B, where the register-staged kernel's MFMA lane order
+    // can only load half lines; K x N through the transpose read).
+    // TGEMM_DMA=0, or a forced pipelined variant or wave count, selects the
+    // other kernels; TGEMM_DMA_VARIANT=<index> picks a sweep variant.
     const char *pp = getenv("TGEMM_PIPE");
-    if (want_bm == 256 && want_bn == 256 && !bkn && !(pp && pp[0] == '0')) {
-        // bf16 with B stored N x K: both operands staged through LDS by the
-        // loads' own LDS writes (full 128-byte lines of B, where the
-        // register-staged kernel's MFMA lane order can only load half lines).
-        // TGEMM_DMA=0, or a forced pipelined variant or wave count, selects
-        // the register-staged kernel; TGEMM_DMA_VARIANT=<index> picks a sweep
-        // variant of either element type.
+    if (want_bm == 256 && want_bn == 256 && !(pp && pp[0] == '0')) {
         int nd = 0;
         const tg::TiledVariant *d = tg::dma_variants(&nd);
         if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
             const int k = atoi(e);
-            if (k >= 0 && k < nd && d[k].elem == elem && d[k].out == out && d[k].preshuffled == pre)
+            if (k >= 0 && k < nd && d[k].elem == elem && d[k].out == out && d[k].preshuffled == pre &&
+                d[k].bkn == bkn)
                 return &d[k];
         }
         const char *dm = getenv("TGEMM_DMA");
         if (elem == tg::kBf16 && !pre && !(dm && dm[0] == '0') && !getenv("TGEMM_PIPE_VARIANT") &&
             !getenv("TGEMM_PIPE_WAVES")) {
             for (int i = 0; i < nd; ++i)
-                if (d[i].elem == elem && d[i].out == out && !d[i].preshuffled)
+                if (d[i].elem == elem && d[i].out == out && !d[i].preshuffled && d[i].bkn == bkn)
                     return &d[i];
         }
+    }
+    // Otherwise 256 x 256 tiles run the software-pipelined kernel (B N x K or
+    // pre-shuffled), unless TGEMM_PIPE=0 asks for the generic one.
+    // TGEMM_PIPE_VARIANT=<index> picks a sweep variant of the same element
+    // type, output and layout.
+    if (want_bm == 256 && want_bn == 256 && !bkn && !(pp && pp[0] == '0')) {
         int nb = 0;
         const tg::TiledVariant *b = tg::pipe_variants(&nb);
         if (const char *e = getenv("TGEMM_PIPE_VARIANT")) {

@@ -348,6 +348,30 @@ __device__ inline f32x4 epi_apply4(const EpiView &v, f32x4 acc, float sa, f32x4 
                  epi_apply1(v, acc.z, sa, sb.z, bz.z), epi_apply1(v, acc.w, sa, sb.w, bz.w)};
 }
 
+// ---------------------------------------------------------------------------
+// B stored K x N (bf16): K-rows of a tile in LDS and the gfx950 transpose read.
+// ---------------------------------------------------------------------------
+// XOR applied to the 16-byte chunk index of K-row k of a K x N B tile: the 4
+// rows one 16-lane block reads at once (k0 .. k0+3, k0 % 4 == 0) get chunk
+// pairs {c, c+1} ^ 2a, disjoint, and rows 8 apart (the next block) differ in
+// bit 3 as well.  A bijection on every aligned group of 16 chunks.
+__device__ inline int bkn_swz(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 64-bit LDS transpose read of 16-bit elements (ds_read_b64_tr_b16).  Within
+// each 16-lane block, lane i receives element i % 4 of the 64 bits addressed
+// by lane 4 e + i / 4, e = 0..3 (established with an in-bounds probe).  So if
+// lane 4 a + b of a block points at K-row k0 + a, columns c0 + 4 b .. + 3,
+// lane i of the block ends up with K-rows k0 .. k0 + 3 of column c0 + i.
+__device__ inline u32x2 lds_read_tr16(const uint8_t *p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 

@@ -49,10 +49,14 @@ using dic = std::integral_constant<int, N>;
 
 }  // namespace
 
-template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD>
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const TiledArgs p)
 {
     static_assert(ELEM == kBf16 || ELEM == kFp8, "bf16 or fp8 e4m3 operands");
+    // BKN: B stored K x N (C = A * B): a step's 64 K-rows of the tile's 256
+    // columns are the B stage (rows of 512 bytes, 16-byte chunks XOR-swizzled
+    // by bkn_swz), and each bf16 operand is two transpose reads.
+    static_assert(!BKN || (ELEM == kBf16 && !BPRE), "K x N B: bf16");
     // fp8: one 128-byte K slice per step and MFMA (16x16x128, 32 bytes per
     // lane: chunks q and q + 4 of the slice); bf16: two 64-byte halves.
     constexpr bool F8 = ELEM == kFp8;
@@ -83,7 +87,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     const uint32_t kb = (uint32_t)p.kbytes;
     const uint32_t kbB = (uint32_t)p.kbytes_b;
     const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
-    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
+    // K x N B: the resource starts at column n0 and ends with the matrix, so
+    // K-rows past K read zeros; columns past N read neighbouring data or
+    // zeros and only feed columns of C that are never stored.
+    const uint32_t ldb = (uint32_t)p.ldb_bytes;
+    const auto rB = BKN ? make_rsrc((const uint8_t *)p.B + (size_t)n0 * 2,
+                                    (uint32_t)((size_t)p.K * ldb - (size_t)n0 * 2))
+                        : make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
     const int nk = p.k_tiles;
     const uint32_t tail = (uint32_t)p.tail_bytes;
 
@@ -105,7 +115,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
 #pragma unroll
     for (int r = 0; r < BR; ++r) {
         const int u = r * WAVES + w;
-        if constexpr (BPRE) {
+        if constexpr (BKN) {
+            const int pc = u * 64 + l;
+            const int row = pc >> 5;                    // 32 chunks per K-row
+            const int c = (pc & 31) ^ bkn_swz(row);
+            voffB[r] = (uint32_t)row * ldb + (uint32_t)c * kChunkBytes;
+            tailB |= 1u << r;                           // rows past K are out of range
+        } else if constexpr (BPRE) {
             voffB[r] = (uint32_t)(u >> 1) * 16u * kbB + (uint32_t)(u & 1) * 1024u + (uint32_t)l * 16u;
             tailB |= ((uint32_t)((u & 1) * 64) < tail ? 1u : 0u) << r;
         } else {
@@ -116,7 +132,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
             tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
         }
     }
-    constexpr uint32_t kBStep = BPRE ? 2048u : (uint32_t)kTileKBytes;   // image bytes per step and block row
+    // bytes of B per step: pre-shuffled image 2 KiB per block row, N x K 128
+    // per row, K x N 64 K-rows
+    const uint32_t kBStep = BKN ? 64u * ldb : (BPRE ? 2048u : (uint32_t)kTileKBytes);
     // Load idx (A rounds first, then B) of step kt into stage S.  Loads past
     // the last step, and the missing half of a half-filled last step, read
     // out of range and land zeros.
@@ -157,6 +175,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         const int row = wm * WTM + i * 16 + r16;
         return lds + s * DM_STAGE + row * kTileKBytes + swz_chunk(row, h * 4 + q) * kChunkBytes;
     };
+    // K x N: the operand of column block j for half h (k = 32 h + 8 q .. + 7
+    // of the step, one column per lane) as two transpose reads.
+    auto bkn_frag = [&](int s, int h, int j) -> u32x4 {
+        const uint8_t *sB = lds + s * DM_STAGE + DM_A;
+        const int col = wn * WTN + j * 16 + 4 * (r16 & 3);    // this lane's 4 source columns
+        const int c = (col * 2) >> 4, off = (col * 2) & 15;
+        u32x2 t2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int k = 32 * h + 8 * q + 4 * t + (r16 >> 2);
+            t2[t] = lds_read_tr16(sB + k * 512 + ((c ^ bkn_swz(k)) << 4) + off);
+        }
+        return u32x4{t2[0].x, t2[0].y, t2[1].x, t2[1].y};
+    };
     auto b_addr = [&](int s, int h, int j) -> const uint8_t * {
         const int nb = wn * FN + j;
         if constexpr (BPRE)
@@ -187,8 +219,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         } else {
             if (t % FM == 0) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    fb[t / FM][j] = lds_load16(b_addr(s, t / FM, j));
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (BKN)
+                        fb[t / FM][j] = bkn_frag(s, t / FM, j);
+                    else
+                        fb[t / FM][j] = lds_load16(b_addr(s, t / FM, j));
+                }
             }
             fa[t] = lds_load16(a_addr(s, t, t / FM));
         }
@@ -289,16 +325,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     }
 }
 
-template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD>
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN>
 static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_dma_kernel<ELEM, OUT, BPRE, WGM, WGN, PD>), dim3(a.grid), dim3(64 * WGM * WGN), 0, s,
-                       a);
+    hipLaunchKernelGGL((gemm_dma_kernel<ELEM, OUT, BPRE, WGM, WGN, PD, BKN>), dim3(a.grid), dim3(64 * WGM * WGN), 0,
+                       s, a);
     return hipGetLastError();
 }
 
 #define TG_DMA(ELEM, OUT, BPRE, WGM, WGN, PD) \
-    TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, OUT, BPRE, DM_LDS, 2, &launch_dma<ELEM, OUT, BPRE, WGM, WGN, PD>}
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, OUT, BPRE, DM_LDS, 2, &launch_dma<ELEM, OUT, BPRE, WGM, WGN, PD, false>}
+#define TG_DMA_KN(OUT, WGM, WGN, PD)                                                                              \
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, kBf16, OUT, false, DM_LDS, 2, &launch_dma<kBf16, OUT, false, WGM, WGN, PD, true>, \
+                 true}
 
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
@@ -308,6 +347,9 @@ static const TiledVariant kDma[] = {
     TG_DMA(kFp8, kOutBf16, false, 1, 8, 2),    // 4
     TG_DMA(kFp8, kOutBf16, true, 1, 8, 3),     // 5
     TG_DMA(kBf16, kOutBf16, true, 2, 4, 6),    // 6
+    TG_DMA_KN(kOutBf16, 2, 4, 4),              // 7: B stored K x N
+    TG_DMA_KN(kOutF32, 2, 4, 4),
+    TG_DMA_KN(kOutBf16, 2, 4, 6),
 };
 
 const TiledVariant *dma_variants(int *count)

@@ -38,23 +38,6 @@
 
 namespace tg {
 
-// XOR applied to the 16-byte chunk index of K-row k of a K x N B tile: the 4
-// rows one 16-lane block reads at once (k0 .. k0+3, k0 % 4 == 0) get chunk
-// pairs {c, c+1} ^ 2a, disjoint, and rows 8 apart (the next block) differ in
-// bit 3 as well.  A bijection on every aligned group of 16 chunks.
-__device__ inline int bkn_swz(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// 64-bit LDS transpose read (16-bit elements), see the header comment.
-__device__ inline u32x2 lds_read_tr16(const uint8_t *p)
-{
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4 *)(__attribute__((address_space(3))) uint8_t *)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
-
 template <int BM, int BN, int WGM, int WGN, int ELEM, bool BPRE, int OUT, bool BKN = false>
 struct TiledCfg {
     static constexpr int kWaves = 4;
