@@ -16,6 +16,8 @@ Contents
 * ``gemm_ab`` / ``gemm_ab_entries`` -- C = A * B with B stored K x N (the
   naive template's layout): b(n, k) is B[k][n], i.e. the same sum with the
   stored B read column-wise.
+* ``gemm_at`` / ``gemm_at_entries`` -- the same sum with A stored K x M:
+  a(m, k) is A[k][m] (and, with ``b_kn``, B stored K x N as well).
 * ``gemm_bt_int`` / ``gemm_bt_int_entries`` -- exact integer sums (int64)
   for an int8 A and an int8 or packed int4 B (W4A8).
 * ``round_bf16`` -- the oracle's own round-to-nearest-even to bf16.
@@ -387,3 +389,21 @@ def gemm_ab_entries(A: np.ndarray, B_kn: np.ndarray, rows, cols, dtype: str = "b
     """gemm_ab at the (rows[t], cols[t]) entries only."""
     B_kn = _operand(B_kn, dtype)
     return gemm_bt_entries(A, np.ascontiguousarray(B_kn.T), rows, cols, dtype=dtype, sigma=sigma)
+
+
+def gemm_at(A_km: np.ndarray, B: np.ndarray, dtype: str = "bf16", sigma: float = 1.0, want_s: bool = True,
+            b_kn: bool = False):
+    """C_ref[m][n] = sigma * sum_k A_km[k][m] * b(n,k) for A stored K x M: the
+    element A_km[k][m] is a(m,k) of the M x K form; B is N x K, or K x N with
+    b_kn (b(n,k) = B[k][n]).  gemm_bt on the transposed copies."""
+    A = np.ascontiguousarray(_operand(A_km, dtype).T)
+    Bt = np.ascontiguousarray(_operand(B, dtype).T) if b_kn else B
+    return gemm_bt(A, Bt, dtype=dtype, sigma=sigma, want_s=want_s)
+
+
+def gemm_at_entries(A_km: np.ndarray, B: np.ndarray, rows, cols, dtype: str = "bf16", sigma: float = 1.0,
+                    b_kn: bool = False):
+    """gemm_at at the (rows[t], cols[t]) entries only."""
+    A = np.ascontiguousarray(_operand(A_km, dtype).T)
+    Bt = np.ascontiguousarray(_operand(B, dtype).T) if b_kn else B
+    return gemm_bt_entries(A, Bt, rows, cols, dtype=dtype, sigma=sigma)

@@ -530,3 +530,41 @@ def test_gemm_ab_unit_vectors(oracle_mod):
     b = np.arange(K * N, dtype=np.float32).reshape(K, N)
     C, _ = oracle_mod.gemm_ab(bf16(a), bf16(b))
     assert np.array_equal(C[0], b[1].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# A stored K x M
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("b_kn", [False, True])
+def test_gemm_at_is_the_plain_matrix_product(oracle_mod, b_kn):
+    # integer values: every sum exact; numpy's int64 matmul of the stored
+    # arrays is an independent definition: C = A_km^T @ B^T (B N x K) or
+    # A_km^T @ B (B K x N).  Non-square, so a wrongly oriented operand would
+    # not even have the right shape.
+    rng = np.random.default_rng(23)
+    M, N, K = 5, 7, 24
+    a_km = rng.integers(-9, 10, (K, M))
+    b = rng.integers(-9, 10, (K, N) if b_kn else (N, K))
+    want = a_km.T @ (b if b_kn else b.T)
+    C, S = oracle_mod.gemm_at(bf16(a_km.astype(np.float32)), bf16(b.astype(np.float32)), b_kn=b_kn)
+    assert C.shape == (M, N)
+    assert np.array_equal(C, want.astype(np.float64))
+    assert np.array_equal(S, (np.abs(a_km.T) @ np.abs(b if b_kn else b.T)).astype(np.float64))
+    rows, cols = np.array([0, 4, 2]), np.array([6, 0, 3])
+    Ce, Se = oracle_mod.gemm_at_entries(bf16(a_km.astype(np.float32)), bf16(b.astype(np.float32)), rows, cols,
+                                        b_kn=b_kn)
+    assert np.array_equal(Ce, C[rows, cols]) and np.array_equal(Se, S[rows, cols])
+
+
+def test_gemm_at_unit_vectors(oracle_mod):
+    # A stored K x M with column m holding e_{sel[m]}: row m of C is column
+    # sel[m] of B^T, i.e. C[m][n] = B[n][sel[m]]
+    K, M, N = 6, 3, 5
+    sel = [4, 0, 2]
+    a_km = np.zeros((K, M), np.float32)
+    for m, k in enumerate(sel):
+        a_km[k, m] = 1.0
+    b = np.arange(N * K, dtype=np.float32).reshape(N, K)
+    C, _ = oracle_mod.gemm_at(bf16(a_km), bf16(b))
+    for m, k in enumerate(sel):
+        assert np.array_equal(C[m], b[:, k].astype(np.float64))
