@@ -27,6 +27,14 @@
  * invariants").  bf16 inputs only; K * N * 2 < 2^31; no
  * pre-shuffled image (gemm_preshuffle_b rejects such plans).
  *
+ * GEMM_LAYOUT_AT and GEMM_LAYOUT_AT_BN store A as K x M row-major (lda = M),
+ * so a(m,k) = A[k][m]; B is N x K (AT) or K x N (AT_BN, b(n,k) = B[k][n]).
+ * The other operand layout the same skill's naive template and transpose
+ * atom describe, read through the same LDS transpose load.  bf16 inputs
+ * only; M % 8 == 0 (16-byte pieces of A's K-rows); K * M * 2 < 2^31; such
+ * plans always use 256 x 256 tiles.  B is read as stored; only
+ * GEMM_LAYOUT_BT_PRESHUFFLED plans read the pre-shuffled image.
+ *
  * Every pointer passed to gemm_preshuffle_b / gemm_run is a DEVICE pointer
  * owned by the caller.  The library allocates no device memory, never
  * synchronises, and launches asynchronously on the given stream; a plan holds
@@ -71,7 +79,9 @@ typedef enum {
 typedef enum {
     GEMM_LAYOUT_BT = 0,               /* B is N x K row-major                        */
     GEMM_LAYOUT_BT_PRESHUFFLED = 1,   /* B is the image written by gemm_preshuffle_b */
-    GEMM_LAYOUT_BN = 2                /* B is K x N row-major: C = A * B (bf16 only)  */
+    GEMM_LAYOUT_BN = 2,               /* B is K x N row-major: C = A * B (bf16 only)  */
+    GEMM_LAYOUT_AT = 3,               /* A is K x M row-major, B N x K (bf16 only)   */
+    GEMM_LAYOUT_AT_BN = 4             /* A is K x M, B K x N row-major (bf16 only)   */
 } gemm_layout;
 
 typedef struct gemm_plan gemm_plan;   /* opaque, immutable after creation */
@@ -121,9 +131,11 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
 
 /*
  * gemm_run -- C = cvt((A * B^T) * s_a * s_b) on `stream`.
- *   A      device pointer, 16-byte aligned, M x K input elements.
- *   B      device pointer, 16-byte aligned: N x K (GEMM_LAYOUT_BT) or the
- *          pre-shuffled image (GEMM_LAYOUT_BT_PRESHUFFLED).
+ *   A      device pointer, 16-byte aligned, M x K input elements (K x M
+ *          for GEMM_LAYOUT_AT and GEMM_LAYOUT_AT_BN).
+ *   B      device pointer, 16-byte aligned: N x K (GEMM_LAYOUT_BT,
+ *          GEMM_LAYOUT_AT), the pre-shuffled image (GEMM_LAYOUT_BT_PRESHUFFLED)
+ *          or K x N (GEMM_LAYOUT_BN, GEMM_LAYOUT_AT_BN).
  *   C      device pointer, 16-byte aligned, M x N output elements; overwritten.
  *   scale  device pointer to two floats {s_a, s_b}, or NULL for 1, 1.  Read
  *          on the device, so fp8 scales never force a host synchronisation.
@@ -291,7 +303,8 @@ typedef struct {
 int gemm_plan_query(const gemm_plan *plan, gemm_plan_info *info);
 
 typedef enum {
-    GEMM_VIEW_A = 0,          /* A bytes:       (M, Ka):(Ka, 1), Ka = K * elem_bits / 8      */
+    GEMM_VIEW_A = 0,          /* A bytes:       (M, Ka):(Ka, 1), Ka = K * elem_bits / 8;
+                                 A stored K x M: (K, 2M):(2M, 1)                            */
     GEMM_VIEW_B = 1,          /* B bytes:       (N, Kb):(Kb, 1), Kb = K * b_elem_bits / 8    */
     GEMM_VIEW_B_SHUF = 2,     /* pre-shuffled:  (N/16, Kb/64, 4, 16, 16):(16Kb, 1024, 256, 16, 1) */
     GEMM_VIEW_B_SRC = 3,      /* B bytes seen through the same 5 coordinates:

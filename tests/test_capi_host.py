@@ -323,7 +323,31 @@ def test_bn_layout_plans(lib, monkeypatch):
     with pytest.raises(tg.GemmError, match="2\\^31"):
         tg.Plan(256, 1 << 16, 1 << 14, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)
     with pytest.raises(tg.GemmError):
-        tg.Plan(256, 256, 256, tg.GEMM_BF16_OUT_BF16, 3)
+        tg.Plan(256, 256, 256, tg.GEMM_BF16_OUT_BF16, -1)
+
+
+def test_at_layout_plans(lib):
+    # A stored K x M (B N x K or K x N): always the 8-wave LDS-staged kernel
+    # on 256 x 256 tiles, whatever the size
+    for layout, b_kn in ((tg.GEMM_LAYOUT_AT, False), (tg.GEMM_LAYOUT_AT_BN, True)):
+        for dtype in (tg.GEMM_BF16_OUT_BF16, tg.GEMM_BF16_OUT_F32):
+            for M, N, K in [(4096, 4096, 4096), (296, 272, 1056), (8, 16, 32)]:
+                with tg.Plan(M, N, K, dtype, layout) as p:
+                    info = p.info()
+                    assert (info["kernel"], info["tile_m"], info["threads"], info["lds_stages"]) == (0, 256, 512, 2)
+                    assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_A) == ((K, 2 * M), (2 * M, 1))
+                    want_b = ((K, 2 * N), (2 * N, 1)) if b_kn else ((N, 2 * K), (2 * K, 1))
+                    assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == want_b
+                    assert tg.gemm_preshuffled_b_bytes(p.handle) == (0 if b_kn else N * K * 2)
+        for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_I8_OUT_BF16):
+            with pytest.raises(tg.GemmError, match="bf16"):
+                tg.Plan(256, 256, 256, dtype, layout)
+        with pytest.raises(tg.GemmError, match="multiple of 8"):
+            tg.Plan(300, 256, 256, tg.GEMM_BF16_OUT_BF16, layout)        # M % 8
+        with pytest.raises(tg.GemmError, match="2\\^31"):
+            tg.Plan(1 << 16, 256, 1 << 14, tg.GEMM_BF16_OUT_BF16, layout)
+    with pytest.raises(tg.GemmError):
+        tg.Plan(256, 256, 256, tg.GEMM_BF16_OUT_BF16, 5)
 
 
 def test_mx_entry_point_guards(lib):

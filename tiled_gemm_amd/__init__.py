@@ -33,6 +33,8 @@ GEMM_W4A8_OUT_BF16 = 6         # int8 A, packed int4 B (two per byte, even eleme
 GEMM_LAYOUT_BT = 0
 GEMM_LAYOUT_BT_PRESHUFFLED = 1
 GEMM_LAYOUT_BN = 2             # B stored K x N row-major: C = A * B
+GEMM_LAYOUT_AT = 3             # A stored K x M row-major, B N x K
+GEMM_LAYOUT_AT_BN = 4          # A stored K x M, B stored K x N
 
 GEMM_EPI_NONE, GEMM_EPI_BIAS, GEMM_EPI_BIAS_RELU, GEMM_EPI_BIAS_SILU, GEMM_EPI_BIAS_GELU = range(5)
 EPILOGUES = {"none": GEMM_EPI_NONE, "bias": GEMM_EPI_BIAS, "bias_relu": GEMM_EPI_BIAS_RELU,
@@ -225,7 +227,8 @@ def gemm_tile_of_workgroup(plan: int, wg: int):
 DTYPES = {"bf16_f32": GEMM_BF16_OUT_F32, "bf16": GEMM_BF16_OUT_BF16, "e4m3": GEMM_E4M3_OUT_BF16,
           "mxfp8": GEMM_MXFP8_OUT_BF16, "mxfp4": GEMM_MXFP4_OUT_BF16, "i8": GEMM_I8_OUT_BF16,
           "w4a8": GEMM_W4A8_OUT_BF16}
-LAYOUTS = {"bt": GEMM_LAYOUT_BT, "bt_preshuffled": GEMM_LAYOUT_BT_PRESHUFFLED, "bn": GEMM_LAYOUT_BN}
+LAYOUTS = {"bt": GEMM_LAYOUT_BT, "bt_preshuffled": GEMM_LAYOUT_BT_PRESHUFFLED, "bn": GEMM_LAYOUT_BN,
+           "at": GEMM_LAYOUT_AT, "at_bn": GEMM_LAYOUT_AT_BN}
 
 
 class Plan:

@@ -94,7 +94,8 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
     int n = 0;
     const tg::TiledVariant *v = tg::tiled_variants(&n);
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
-    const bool bkn = I.layout == GEMM_LAYOUT_BN;
+    const bool bkn = I.layout == GEMM_LAYOUT_BN || I.layout == GEMM_LAYOUT_AT_BN;
+    const bool akm = I.layout == GEMM_LAYOUT_AT || I.layout == GEMM_LAYOUT_AT_BN;
     const int elem = elem_of(I.dtype), out = out_of(I.dtype);
     if (is_mx(I.dtype) || is_int(I.dtype)) {
         // MX and integer operands: only the pipelined 256 x 256 kernel (any
@@ -108,6 +109,20 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
             if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre &&
                 (waves == 0 || b[i].wgm * b[i].wgn == waves))
                 return &b[i];
+        return nullptr;
+    }
+    // A stored K x M: only the LDS-staged 256 x 256 kernel reads it.
+    if (akm) {
+        int nd = 0;
+        const tg::TiledVariant *d = tg::dma_variants(&nd);
+        if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
+            const int k = atoi(e);
+            if (k >= 0 && k < nd && d[k].akm && d[k].elem == elem && d[k].out == out && d[k].bkn == bkn)
+                return &d[k];
+        }
+        for (int i = 0; i < nd; ++i)
+            if (d[i].akm && d[i].elem == elem && d[i].out == out && d[i].bkn == bkn)
+                return &d[i];
         return nullptr;
     }
     int want_bm = 0, want_bn = 0;
@@ -131,14 +146,14 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
         if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
             const int k = atoi(e);
             if (k >= 0 && k < nd && d[k].elem == elem && d[k].out == out && d[k].preshuffled == pre &&
-                d[k].bkn == bkn)
+                d[k].bkn == bkn && !d[k].akm)
                 return &d[k];
         }
         const char *dm = getenv("TGEMM_DMA");
         if (elem == tg::kBf16 && !pre && !(dm && dm[0] == '0') && !getenv("TGEMM_PIPE_VARIANT") &&
             !getenv("TGEMM_PIPE_WAVES")) {
             for (int i = 0; i < nd; ++i)
-                if (d[i].elem == elem && d[i].out == out && !d[i].preshuffled && d[i].bkn == bkn)
+                if (d[i].elem == elem && d[i].out == out && !d[i].preshuffled && d[i].bkn == bkn && !d[i].akm)
                     return &d[i];
         }
     }
@@ -208,9 +223,11 @@ Layout view_of(const gemm_plan &p, int view, bool *okv)
     *okv = true;
     switch (view) {
     case GEMM_VIEW_A:
+        if (I.layout == GEMM_LAYOUT_AT || I.layout == GEMM_LAYOUT_AT_BN)
+            return make({I.K, I.M * I.elem_bytes}, {I.M * I.elem_bytes, 1});
         return make({I.M, p.kbytes}, {p.kbytes, 1});
     case GEMM_VIEW_B:
-        if (I.layout == GEMM_LAYOUT_BN)
+        if (I.layout == GEMM_LAYOUT_BN || I.layout == GEMM_LAYOUT_AT_BN)
             return make({I.K, I.N * I.elem_bytes}, {I.N * I.elem_bytes, 1});
         return make({I.N, Kb}, {Kb, 1});
     case GEMM_VIEW_B_SHUF:
@@ -272,12 +289,15 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
         return nullptr;
     }
-    if (layout != GEMM_LAYOUT_BT && layout != GEMM_LAYOUT_BT_PRESHUFFLED && layout != GEMM_LAYOUT_BN) {
+    if (layout < GEMM_LAYOUT_BT || layout > GEMM_LAYOUT_AT_BN) {
         fail(GEMM_ERR_INVALID_ARG, "unknown layout %d", layout);
         return nullptr;
     }
-    if (layout == GEMM_LAYOUT_BN && dtype != GEMM_BF16_OUT_F32 && dtype != GEMM_BF16_OUT_BF16) {
-        fail(GEMM_ERR_UNSUPPORTED, "B stored K x N is supported for bf16 inputs");
+    const bool b_kn = layout == GEMM_LAYOUT_BN || layout == GEMM_LAYOUT_AT_BN;
+    const bool a_km = layout == GEMM_LAYOUT_AT || layout == GEMM_LAYOUT_AT_BN;
+    if ((b_kn || a_km) && dtype != GEMM_BF16_OUT_F32 && dtype != GEMM_BF16_OUT_BF16) {
+        fail(GEMM_ERR_UNSUPPORTED, "%s stored %s is supported for bf16 inputs", a_km ? "A" : "B",
+             a_km ? "K x M" : "K x N");
         return nullptr;
     }
     if (M < 0 || N < 0 || K < 0) {
@@ -322,8 +342,16 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "N=%lld too large for 32-bit C tile offsets", (long long)N);
         return nullptr;
     }
-    if (layout == GEMM_LAYOUT_BN && K * N * 2 >= (int64_t(1) << 31)) {
+    if (b_kn && K * N * 2 >= (int64_t(1) << 31)) {
         fail(GEMM_ERR_UNSUPPORTED, "B stored K x N must stay below 2^31 bytes (32-bit offsets)");
+        return nullptr;
+    }
+    if (a_km && K * M * 2 >= (int64_t(1) << 31)) {
+        fail(GEMM_ERR_UNSUPPORTED, "A stored K x M must stay below 2^31 bytes (32-bit offsets)");
+        return nullptr;
+    }
+    if (a_km && M % 8 != 0) {
+        fail(GEMM_ERR_UNSUPPORTED, "M=%lld must be a multiple of 8 for A stored K x M", (long long)M);
         return nullptr;
     }
     if (M * kbytes >= (int64_t(1) << 32) && M <= 64) {
@@ -402,7 +430,7 @@ void gemm_plan_destroy(gemm_plan *plan) { delete plan; }
 
 size_t gemm_preshuffled_b_bytes(const gemm_plan *plan)
 {
-    if (!plan || plan->info.layout == GEMM_LAYOUT_BN)
+    if (!plan || plan->info.layout == GEMM_LAYOUT_BN || plan->info.layout == GEMM_LAYOUT_AT_BN)
         return 0;
     return (size_t)plan->info.N * (size_t)plan->kbytes_b;
 }
@@ -503,7 +531,7 @@ int gemm_preshuffle_b(const gemm_plan *plan, const void *B, void *B_shuf, hipStr
 {
     if (!plan)
         return fail(GEMM_ERR_INVALID_ARG, "NULL plan");
-    if (plan->info.layout == GEMM_LAYOUT_BN)
+    if (plan->info.layout == GEMM_LAYOUT_BN || plan->info.layout == GEMM_LAYOUT_AT_BN)
         return fail(GEMM_ERR_INVALID_ARG, "the pre-shuffled image is made from B stored N x K");
     const size_t bytes = gemm_preshuffled_b_bytes(plan);
     if (bytes == 0) {
@@ -585,6 +613,7 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.kbytes_b = (int32_t)plan->kbytes_b;
         a.K = (int32_t)I.K;
         a.ldb_bytes = (int32_t)(I.N * I.elem_bytes);
+        a.lda_bytes = (int32_t)(I.M * I.elem_bytes);
         a.k_tiles = plan->k_tiles;
         a.tail_bytes = plan->tail_bytes;
         a.grid = I.grid;

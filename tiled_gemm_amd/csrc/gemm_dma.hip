@@ -49,7 +49,7 @@ using dic = std::integral_constant<int, N>;
 
 }  // namespace
 
-template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN>
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN, bool AKM>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const TiledArgs p)
 {
     static_assert(ELEM == kBf16 || ELEM == kFp8, "bf16 or fp8 e4m3 operands");
@@ -57,6 +57,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     // columns are the B stage (rows of 512 bytes, 16-byte chunks XOR-swizzled
     // by bkn_swz), and each bf16 operand is two transpose reads.
     static_assert(!BKN || (ELEM == kBf16 && !BPRE), "K x N B: bf16");
+    // AKM: A stored K x M, staged and read the same way (64 K-rows of the
+    // tile's 256 rows of C per step).
+    static_assert(!AKM || (ELEM == kBf16 && !BPRE), "K x M A: bf16");
     // fp8: one 128-byte K slice per step and MFMA (16x16x128, 32 bytes per
     // lane: chunks q and q + 4 of the slice); bf16: two 64-byte halves.
     constexpr bool F8 = ELEM == kFp8;
@@ -86,7 +89,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     const int rows_b = min(p.N - n0, DM_BN);
     const uint32_t kb = (uint32_t)p.kbytes;
     const uint32_t kbB = (uint32_t)p.kbytes_b;
-    const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
+    const uint32_t lda = (uint32_t)p.lda_bytes;
+    const auto rA = AKM ? make_rsrc((const uint8_t *)p.A + (size_t)m0 * 2,
+                                    (uint32_t)((size_t)p.K * lda - (size_t)m0 * 2))
+                        : make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
     // K x N B: the resource starts at column n0 and ends with the matrix, so
     // K-rows past K read zeros; columns past N read neighbouring data or
     // zeros and only feed columns of C that are never stored.
@@ -107,10 +113,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
 #pragma unroll
     for (int r = 0; r < AR; ++r) {
         const int pc = (r * WAVES + w) * 64 + l;
-        const int row = pc >> 3;
-        const int c = swz_chunk(row, pc & 7);
-        voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
-        tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+        if constexpr (AKM) {
+            const int row = pc >> 5;                    // 32 chunks per K-row
+            const int c = (pc & 31) ^ bkn_swz(row);
+            voffA[r] = (uint32_t)row * lda + (uint32_t)c * kChunkBytes;
+            tailA |= 1u << r;                           // rows past K are out of range
+        } else {
+            const int row = pc >> 3;
+            const int c = swz_chunk(row, pc & 7);
+            voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
+            tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+        }
     }
 #pragma unroll
     for (int r = 0; r < BR; ++r) {
@@ -132,6 +145,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
             tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
         }
     }
+    const uint32_t kAStep = AKM ? 64u * lda : (uint32_t)kTileKBytes;   // bytes of A per step
     // bytes of B per step: pre-shuffled image 2 KiB per block row, N x K 128
     // per row, K x N 64 K-rows
     const uint32_t kBStep = BKN ? 64u * ldb : (BPRE ? 2048u : (uint32_t)kTileKBytes);
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         if constexpr (!decltype(mask_c)::value) {
             if (idx < AR)
                 buf_load16_to_lds(rA, lds + S * DM_STAGE + (idx * WAVES + w) * 1024, voffA[idx],
-                                  (uint32_t)kt * kTileKBytes);
+                                  (uint32_t)kt * kAStep);
             else
                 buf_load16_to_lds(rB, lds + S * DM_STAGE + DM_A + ((idx - AR) * WAVES + w) * 1024, voffB[idx - AR],
                                   (uint32_t)kt * kBStep);
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         if (idx < AR) {
             const bool keep = !beyond & (!part | (((tailA >> idx) & 1u) != 0));
             buf_load16_to_lds(rA, lds + S * DM_STAGE + (idx * WAVES + w) * 1024, keep_or_oob(keep, voffA[idx]),
-                              (uint32_t)kt * kTileKBytes);
+                              (uint32_t)kt * kAStep);
         } else {
             const int r = idx - AR;
             const bool keep = !beyond & (!part | (((tailB >> r) & 1u) != 0));
@@ -170,6 +184,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     // ---- fragments.  A: row block i, half h -> logical chunk 4 h + q of row
     // wm * WTM + 16 i + r16 (fp8: chunks q and q + 4).  B: block j of the
     // wave, half h.
+    // K x M A: the operand of row block i for half h, two transpose reads.
+    auto akm_frag = [&](int s, int g, int h) -> u32x4 {
+        const uint8_t *sA = lds + s * DM_STAGE;
+        const int col = wm * WTM + (g % FM) * 16 + 4 * (r16 & 3);   // this lane's 4 source rows of C
+        const int c = (col * 2) >> 4, off = (col * 2) & 15;
+        u32x2 t2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int k = 32 * h + 8 * q + 4 * t + (r16 >> 2);
+            t2[t] = lds_read_tr16(sA + k * 512 + ((c ^ bkn_swz(k)) << 4) + off);
+        }
+        return u32x4{t2[0].x, t2[0].y, t2[1].x, t2[1].y};
+    };
     auto a_addr = [&](int s, int g, int h) -> const uint8_t * {
         const int i = g % FM;
         const int row = wm * WTM + i * 16 + r16;
@@ -226,7 +253,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
                         fb[t / FM][j] = lds_load16(b_addr(s, t / FM, j));
                 }
             }
-            fa[t] = lds_load16(a_addr(s, t, t / FM));
+            if constexpr (AKM)
+                fa[t] = akm_frag(s, t, t / FM);
+            else
+                fa[t] = lds_load16(a_addr(s, t, t / FM));
         }
     };
     auto barrier = [&]() {
@@ -325,19 +355,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     }
 }
 
-template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN>
+template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN, bool AKM>
 static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_dma_kernel<ELEM, OUT, BPRE, WGM, WGN, PD, BKN>), dim3(a.grid), dim3(64 * WGM * WGN), 0,
-                       s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<ELEM, OUT, BPRE, WGM, WGN, PD, BKN, AKM>), dim3(a.grid),
+                       dim3(64 * WGM * WGN), 0, s, a);
     return hipGetLastError();
 }
 
-#define TG_DMA(ELEM, OUT, BPRE, WGM, WGN, PD) \
-    TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, OUT, BPRE, DM_LDS, 2, &launch_dma<ELEM, OUT, BPRE, WGM, WGN, PD, false>}
-#define TG_DMA_KN(OUT, WGM, WGN, PD)                                                                              \
-    TiledVariant{DM_BM, DM_BN, WGM, WGN, kBf16, OUT, false, DM_LDS, 2, &launch_dma<kBf16, OUT, false, WGM, WGN, PD, true>, \
-                 true}
+#define TG_DMA(ELEM, OUT, BPRE, WGM, WGN, PD)                                                       \
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, OUT, BPRE, DM_LDS, 2,                                    \
+                 &launch_dma<ELEM, OUT, BPRE, WGM, WGN, PD, false, false>}
+#define TG_DMA_L(OUT, WGM, WGN, PD, BKN, AKM)                                                        \
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, kBf16, OUT, false, DM_LDS, 2,                                  \
+                 &launch_dma<kBf16, OUT, false, WGM, WGN, PD, BKN, AKM>, BKN, AKM}
+#define TG_DMA_KN(OUT, WGM, WGN, PD) TG_DMA_L(OUT, WGM, WGN, PD, true, false)
 
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
@@ -350,6 +382,10 @@ static const TiledVariant kDma[] = {
     TG_DMA_KN(kOutBf16, 2, 4, 4),              // 7: B stored K x N
     TG_DMA_KN(kOutF32, 2, 4, 4),
     TG_DMA_KN(kOutBf16, 2, 4, 6),
+    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 10: A stored K x M, B N x K
+    TG_DMA_L(kOutF32, 2, 4, 4, false, true),
+    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 12: A stored K x M, B K x N
+    TG_DMA_L(kOutF32, 2, 4, 4, true, true),
 };
 
 const TiledVariant *dma_variants(int *count)

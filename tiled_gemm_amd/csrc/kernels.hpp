@@ -43,6 +43,7 @@ struct TiledArgs {
     int32_t kbytes_b;       // bytes of one row of B (kbytes, or kbytes / 2 for int4 B)
     int32_t K;              // elements along K
     int32_t ldb_bytes;      // B stored K x N: bytes of one row of B (N * elem_bytes)
+    int32_t lda_bytes;      // A stored K x M: bytes of one row of A (M * elem_bytes)
 };
 
 // Block-scale image of an MX operand with R rows: the bytes
@@ -91,6 +92,7 @@ struct TiledVariant {
     int lds_stages;         // K steps the LDS ring holds
     hipError_t (*launch)(const TiledArgs &, hipStream_t);
     bool bkn = false;       // B stored K x N
+    bool akm = false;       // A stored K x M
 };
 
 struct SkinnyVariant {

@@ -29,7 +29,8 @@ Recipe (every array is raw element bits in row-major order):
 
 A is M x K, B is N x K (K contiguous in both), C is M x N.  Layout "bn"
 stores B as K x N (N contiguous): it is drawn N x K as above and stored
-transposed.
+transposed.  Layouts "at" and "at_bn" store A as K x M the same way (and
+"at_bn" B as K x N).
 """
 from __future__ import annotations
 
@@ -48,7 +49,8 @@ class Workload:
     K: int
     dtype: str          # "bf16", "e4m3", "mxfp8", "mxfp4", "i8" or "w4a8" (int8 A, int4 B)
     out: str            # "f32" or "bf16"
-    layout: str         # "bt" (B as N x K), "bt_preshuffled" or "bn" (B as K x N)
+    layout: str         # "bt" (B as N x K), "bt_preshuffled", "bn" (B as K x N), "at" (A as
+                        # K x M, B N x K) or "at_bn" (A as K x M, B K x N)
     dist_a: tuple
     dist_b: tuple
     seed: int
@@ -109,6 +111,12 @@ WORKLOADS = {
     "bf16_4096_bn": Workload("bf16_4096_bn", 4096, 4096, 4096, "bf16", "bf16", "bn",
                              ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1010,
                              "B stored K x N (C = A * B)"),
+    "bf16_4096_at": Workload("bf16_4096_at", 4096, 4096, 4096, "bf16", "bf16", "at",
+                             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1011,
+                             "A stored K x M"),
+    "bf16_4096_at_bn": Workload("bf16_4096_at_bn", 4096, 4096, 4096, "bf16", "bf16", "at_bn",
+                                ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1012,
+                                "A stored K x M, B stored K x N"),
     "i8_8192": Workload("i8_8192", 8192, 8192, 8192, "i8", "bf16", "bt_preshuffled",
                         ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1008,
                         "per-row / per-channel absmax scales"),
@@ -238,8 +246,11 @@ def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
     a = _draw(rng, w.dist_a, (M, K))
     b = _draw(rng, w.dist_b, (N, K))
     if w.dtype == "bf16":
-        if w.layout == "bn":
+        # drawn as M x K and N x K, then stored as the layout says
+        if w.layout in ("bn", "at_bn"):
             b = np.ascontiguousarray(b.T)
+        if w.layout in ("at", "at_bn"):
+            a = np.ascontiguousarray(a.T)
         return Inputs(to_bf16_bits(a), to_bf16_bits(b))
     if w.dtype.startswith("mx"):
         qa, ea = quantize_mx(a, w.dtype)
