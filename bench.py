@@ -190,7 +190,7 @@ def main():
         log("bench: copy calibration %d MiB x 3" % args.calibrate_copy)
         del src, dst
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
-        "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192", "e4m3_8192", "mxfp8_8192", "mxfp4_8192",
+        "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192",
         "i8_8192", "w4a8_8192"])
     results = {}
     inputs = {}

@@ -24,8 +24,9 @@
  * so C = A * B with b(n,k) = B[k][n].  The kernel reads it through the
  * gfx950 LDS transpose load (ds_read_b64_tr_b16, the 16-lane copy atom of
  * FlyDSL's "add-target-atom-op" skill, section 1.5.2 "Shape-product
- * invariants").  bf16 inputs only; K * N * 2 < 2^31; no
- * pre-shuffled image (gemm_preshuffle_b rejects such plans).
+ * invariants"; for fp8 its 8-bit form ds_read_b64_tr_b8).  bf16 or fp8
+ * e4m3 inputs; K * N * elem_bytes < 2^31; no pre-shuffled image
+ * (gemm_preshuffle_b rejects such plans); fp8 plans use 256 x 256 tiles.
  *
  * GEMM_LAYOUT_AT and GEMM_LAYOUT_AT_BN store A as K x M row-major (lda = M),
  * so a(m,k) = A[k][m]; B is N x K (AT) or K x N (AT_BN, b(n,k) = B[k][n]).
@@ -79,7 +80,7 @@ typedef enum {
 typedef enum {
     GEMM_LAYOUT_BT = 0,               /* B is N x K row-major                        */
     GEMM_LAYOUT_BT_PRESHUFFLED = 1,   /* B is the image written by gemm_preshuffle_b */
-    GEMM_LAYOUT_BN = 2,               /* B is K x N row-major: C = A * B (bf16 only)  */
+    GEMM_LAYOUT_BN = 2,               /* B is K x N row-major: C = A * B (bf16, e4m3) */
     GEMM_LAYOUT_AT = 3,               /* A is K x M row-major, B N x K (bf16 only)   */
     GEMM_LAYOUT_AT_BN = 4             /* A is K x M, B K x N row-major (bf16 only)   */
 } gemm_layout;

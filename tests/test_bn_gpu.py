@@ -1,5 +1,5 @@
 """Parity of C = A * B with B stored K x N (GEMM_LAYOUT_BN, read through
-the LDS transpose load) with the oracle's gemm_ab.
+the LDS transpose load) with the oracle's gemm_ab, for bf16 and fp8 e4m3.
 
 * Integer-valued bf16 inputs (exact sums): bit-exact on both tile sizes and
   both outputs, with M and N tails, a half-filled last K step (K % 64 ==
@@ -112,3 +112,40 @@ def test_bn_full_size_sampled(oracle_mod, monkeypatch):
     r = assert_within_bound(decode(bits[rows, cols]), C, S, "bf16", w.name)
     say("  worst err/bound", r)
     assert np.all(np.isfinite(decode(bits)))
+
+
+# ------------------------------------------------------------------ fp8 e4m3 (8-bit transpose read)
+
+@pytest.mark.parametrize("M,N,K", [(300, 272, 1088), (256, 512, 1024), (1, 16, 64), (77, 48, 192)])
+def test_bn_fp8_bit_exact(oracle_mod, monkeypatch, M, N, K):
+    # integer values in [-4, 4] are exact in e4m3; power-of-two scales keep
+    # the sums and the scaled result exact, so the bf16 output is the single
+    # RNE of an exact value on both sides
+    set_tile(monkeypatch, None)
+    say("case bn fp8 exact", M, N, K)
+    inp = W.int_inputs(M, N, K, "e4m3", seed=M + 3 * N + K)
+    B_kn = np.ascontiguousarray(inp.B.T)
+    bits, info = run_gemm(inp.A, B_kn, M, N, K, "e4m3", "bf16", "bn", scale=(0.5, 0.25), return_plan_info=True)
+    assert info["tile_m"] == 256
+    C, _ = oracle_mod.gemm_ab(inp.A, B_kn, dtype="e4m3", sigma=oracle_mod.sigma_of(0.5, 0.25))
+    _exact(oracle_mod, bits, "bf16", C)
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 784, 1536), (4096, 4096, 4096)])
+def test_bn_fp8_random_within_bound(oracle_mod, monkeypatch, M, N, K):
+    set_tile(monkeypatch, None)
+    say("case bn fp8 random", M, N, K)
+    inp = W.make_inputs(W.WORKLOADS["e4m3_8192"], M=M, N=N, K=K, seed=53)
+    B_kn = np.ascontiguousarray(inp.B.T)
+    bits = run_gemm(inp.A, B_kn, M, N, K, "e4m3", "bf16", "bn", scale=(inp.scale_a, inp.scale_b))
+    sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+    if M * N <= 1 << 20:
+        C, S = oracle_mod.gemm_ab(inp.A, B_kn, dtype="e4m3", sigma=sigma)
+        got = decode(bits)
+    else:
+        rows, cols = sample_entries(M, N, 8192, seed=54)
+        C, S = oracle_mod.gemm_ab_entries(inp.A, B_kn, rows, cols, dtype="e4m3", sigma=sigma)
+        got = decode(bits[rows, cols])
+        assert np.all(np.isfinite(decode(bits)))
+    r = assert_within_bound(got, C, S, "e4m3", "bn fp8 random %dx%dx%d" % (M, N, K))
+    say("  worst err/bound", r)

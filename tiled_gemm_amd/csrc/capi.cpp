@@ -111,17 +111,18 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
                 return &b[i];
         return nullptr;
     }
-    // A stored K x M: only the LDS-staged 256 x 256 kernel reads it.
-    if (akm) {
+    // A stored K x M, and fp8 B stored K x N: only the LDS-staged 256 x 256
+    // kernel reads them.
+    if (akm || (bkn && elem == tg::kFp8)) {
         int nd = 0;
         const tg::TiledVariant *d = tg::dma_variants(&nd);
         if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
             const int k = atoi(e);
-            if (k >= 0 && k < nd && d[k].akm && d[k].elem == elem && d[k].out == out && d[k].bkn == bkn)
+            if (k >= 0 && k < nd && d[k].akm == akm && d[k].elem == elem && d[k].out == out && d[k].bkn == bkn)
                 return &d[k];
         }
         for (int i = 0; i < nd; ++i)
-            if (d[i].akm && d[i].elem == elem && d[i].out == out && d[i].bkn == bkn)
+            if (d[i].akm == akm && d[i].elem == elem && d[i].out == out && d[i].bkn == bkn)
                 return &d[i];
         return nullptr;
     }
@@ -295,9 +296,13 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     }
     const bool b_kn = layout == GEMM_LAYOUT_BN || layout == GEMM_LAYOUT_AT_BN;
     const bool a_km = layout == GEMM_LAYOUT_AT || layout == GEMM_LAYOUT_AT_BN;
-    if ((b_kn || a_km) && dtype != GEMM_BF16_OUT_F32 && dtype != GEMM_BF16_OUT_BF16) {
-        fail(GEMM_ERR_UNSUPPORTED, "%s stored %s is supported for bf16 inputs", a_km ? "A" : "B",
-             a_km ? "K x M" : "K x N");
+    const bool bf16_in = dtype == GEMM_BF16_OUT_F32 || dtype == GEMM_BF16_OUT_BF16;
+    if (a_km && !bf16_in) {
+        fail(GEMM_ERR_UNSUPPORTED, "A stored K x M is supported for bf16 inputs");
+        return nullptr;
+    }
+    if (b_kn && !bf16_in && dtype != GEMM_E4M3_OUT_BF16) {
+        fail(GEMM_ERR_UNSUPPORTED, "B stored K x N is supported for bf16 and fp8 e4m3 inputs");
         return nullptr;
     }
     if (M < 0 || N < 0 || K < 0) {
@@ -342,7 +347,7 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "N=%lld too large for 32-bit C tile offsets", (long long)N);
         return nullptr;
     }
-    if (b_kn && K * N * 2 >= (int64_t(1) << 31)) {
+    if (b_kn && K * N * (ebits / 8) >= (int64_t(1) << 31)) {
         fail(GEMM_ERR_UNSUPPORTED, "B stored K x N must stay below 2^31 bytes (32-bit offsets)");
         return nullptr;
     }

@@ -372,6 +372,25 @@ __device__ inline u32x2 lds_read_tr16(const uint8_t *p)
     return __builtin_bit_cast(u32x2, v);
 }
 
+// 64-bit LDS transpose read of 8-bit elements (ds_read_b64_tr_b8).  Within
+// each 16-lane block, lane i receives, as its byte e (e = 0..7), byte i % 8 of
+// the 64 bits addressed by lane 2 e + i / 8 (established with an in-bounds
+// probe).  So if lane 2 e + b of a block points at K-row k0 + e, columns
+// c0 + 8 b .. + 7, lane i ends up with K-rows k0 .. k0 + 7 of column c0 + i.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
+__device__ inline u32x2 lds_read_tr8(const uint8_t *p)
+{
+    const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2 *)(__attribute__((address_space(3))) uint8_t *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Chunk swizzle of the K-rows of an 8-bit K x N tile (rows of 256 bytes, one
+// full 64-bank line each): chunk c of K-row k sits at c ^ (k & 7), so the 8
+// rows one transpose read takes from a 16-lane block hit 8 different chunks.
+__device__ inline int bkn8_swz(int k) { return k & 7; }
+
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 

@@ -53,16 +53,22 @@ template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN, bool
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const TiledArgs p)
 {
     static_assert(ELEM == kBf16 || ELEM == kFp8, "bf16 or fp8 e4m3 operands");
-    // BKN: B stored K x N (C = A * B): a step's 64 K-rows of the tile's 256
-    // columns are the B stage (rows of 512 bytes, 16-byte chunks XOR-swizzled
-    // by bkn_swz), and each bf16 operand is two transpose reads.
-    static_assert(!BKN || (ELEM == kBf16 && !BPRE), "K x N B: bf16");
+    // BKN: B stored K x N (C = A * B): a step's K-rows of the tile's 256
+    // columns are the B stage (bf16: 64 rows of 512 bytes, chunks swizzled by
+    // bkn_swz, two 16-bit transpose reads per operand; fp8: 128 rows of 256
+    // bytes, bkn8_swz, four 8-bit transpose reads per operand).
+    static_assert(!BKN || !BPRE, "K x N B is not pre-shuffled");
     // AKM: A stored K x M, staged and read the same way (64 K-rows of the
     // tile's 256 rows of C per step).
     static_assert(!AKM || (ELEM == kBf16 && !BPRE), "K x M A: bf16");
     // fp8: one 128-byte K slice per step and MFMA (16x16x128, 32 bytes per
     // lane: chunks q and q + 4 of the slice); bf16: two 64-byte halves.
     constexpr bool F8 = ELEM == kFp8;
+    // K x N B geometry per step: bf16 64 K-rows of 512 bytes (swizzle
+    // bkn_swz), fp8 128 K-rows of 256 bytes (swizzle bkn8_swz).
+    constexpr int KN_ROWS = F8 ? 128 : 64;
+    constexpr int KN_CPR = (F8 ? 256 : 512) / kChunkBytes;
+    auto kn_swz = [](int k) { return F8 ? bkn8_swz(k) : bkn_swz(k); };
     constexpr int WAVES = WGM * WGN;
     constexpr int THREADS = 64 * WAVES;
     constexpr int WTM = DM_BM / WGM, WTN = DM_BN / WGN;
@@ -97,8 +103,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     // K-rows past K read zeros; columns past N read neighbouring data or
     // zeros and only feed columns of C that are never stored.
     const uint32_t ldb = (uint32_t)p.ldb_bytes;
-    const auto rB = BKN ? make_rsrc((const uint8_t *)p.B + (size_t)n0 * 2,
-                                    (uint32_t)((size_t)p.K * ldb - (size_t)n0 * 2))
+    constexpr int EB = F8 ? 1 : 2;                       // bytes per element
+    const auto rB = BKN ? make_rsrc((const uint8_t *)p.B + (size_t)n0 * EB,
+                                    (uint32_t)((size_t)p.K * ldb - (size_t)n0 * EB))
                         : make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
     const int nk = p.k_tiles;
     const uint32_t tail = (uint32_t)p.tail_bytes;
@@ -130,8 +137,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         const int u = r * WAVES + w;
         if constexpr (BKN) {
             const int pc = u * 64 + l;
-            const int row = pc >> 5;                    // 32 chunks per K-row
-            const int c = (pc & 31) ^ bkn_swz(row);
+            const int row = pc / KN_CPR;
+            const int c = (pc % KN_CPR) ^ kn_swz(row);
             voffB[r] = (uint32_t)row * ldb + (uint32_t)c * kChunkBytes;
             tailB |= 1u << r;                           // rows past K are out of range
         } else if constexpr (BPRE) {
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     const uint32_t kAStep = AKM ? 64u * lda : (uint32_t)kTileKBytes;   // bytes of A per step
     // bytes of B per step: pre-shuffled image 2 KiB per block row, N x K 128
     // per row, K x N 64 K-rows
-    const uint32_t kBStep = BKN ? 64u * ldb : (BPRE ? 2048u : (uint32_t)kTileKBytes);
+    const uint32_t kBStep = BKN ? (uint32_t)KN_ROWS * ldb : (BPRE ? 2048u : (uint32_t)kTileKBytes);
     // Load idx (A rounds first, then B) of step kt into stage S.  Loads past
     // the last step, and the missing half of a half-filled last step, read
     // out of range and land zeros.
@@ -216,6 +223,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         }
         return u32x4{t2[0].x, t2[0].y, t2[1].x, t2[1].y};
     };
+    // fp8 K x N: the 32-byte operand of column block j (this lane's column,
+    // K positions 16 q .. 16 q + 15 and 64 + 16 q .. + 15 of the step, the
+    // order A's two chunks give) as four 8-row transpose reads.
+    auto bkn8_frag = [&](int s, int j) -> i32x8 {
+        const uint8_t *sB = lds + s * DM_STAGE + DM_A;
+        const int e = r16 >> 1, b = r16 & 1;
+        const int cb = wn * WTN + j * 16 + 8 * b;                // this lane's 8 source columns
+        const int c = cb >> 4, off = cb & 15;
+        u32x2 t4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = (t >> 1) * 64 + 16 * q + 8 * (t & 1) + e;
+            t4[t] = lds_read_tr8(sB + k * 256 + ((c ^ bkn8_swz(k)) << 4) + off);
+        }
+        return i32x8{(int)t4[0].x, (int)t4[0].y, (int)t4[1].x, (int)t4[1].y,
+                     (int)t4[2].x, (int)t4[2].y, (int)t4[3].x, (int)t4[3].y};
+    };
     auto b_addr = [&](int s, int h, int j) -> const uint8_t * {
         const int nb = wn * FN + j;
         if constexpr (BPRE)
@@ -239,8 +263,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         if constexpr (F8) {
             if (t == 0) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    fb[s][j] = join32(lds_load16(b_addr(s, 0, j)), lds_load16(b_addr(s, 1, j)));
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (BKN)
+                        fb[s][j] = bkn8_frag(s, j);
+                    else
+                        fb[s][j] = join32(lds_load16(b_addr(s, 0, j)), lds_load16(b_addr(s, 1, j)));
+                }
             }
             fa[t] = join32(lds_load16(a_addr(s, t, 0)), lds_load16(a_addr(s, t, 1)));
         } else {
@@ -370,6 +398,9 @@ static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
     TiledVariant{DM_BM, DM_BN, WGM, WGN, kBf16, OUT, false, DM_LDS, 2,                                  \
                  &launch_dma<kBf16, OUT, false, WGM, WGN, PD, BKN, AKM>, BKN, AKM}
 #define TG_DMA_KN(OUT, WGM, WGN, PD) TG_DMA_L(OUT, WGM, WGN, PD, true, false)
+#define TG_DMA_KN8(WGM, WGN, PD)                                                                   \
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, kFp8, kOutBf16, false, DM_LDS, 2,                              \
+                 &launch_dma<kFp8, kOutBf16, false, WGM, WGN, PD, true, false>, true, false}
 
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
@@ -386,6 +417,8 @@ static const TiledVariant kDma[] = {
     TG_DMA_L(kOutF32, 2, 4, 4, false, true),
     TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 12: A stored K x M, B K x N
     TG_DMA_L(kOutF32, 2, 4, 4, true, true),
+    TG_DMA_KN8(1, 8, 3),                       // 14: fp8, B stored K x N
+    TG_DMA_KN8(1, 8, 2),
 };
 
 const TiledVariant *dma_variants(int *count)

@@ -111,6 +111,9 @@ WORKLOADS = {
     "bf16_4096_bn": Workload("bf16_4096_bn", 4096, 4096, 4096, "bf16", "bf16", "bn",
                              ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1010,
                              "B stored K x N (C = A * B)"),
+    "e4m3_8192_bn": Workload("e4m3_8192_bn", 8192, 8192, 8192, "e4m3", "bf16", "bn",
+                             ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1013,
+                             "per-tensor scales amax/448, B stored K x N"),
     "bf16_4096_at": Workload("bf16_4096_at", 4096, 4096, 4096, "bf16", "bf16", "at",
                              ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1011,
                              "A stored K x M"),
@@ -267,6 +270,8 @@ def make_inputs(w: Workload, M: int | None = None, N: int | None = None,
         return Inputs(qa.view(np.uint8), qb, sa_rows=sa, sb_cols=sb)
     qa, sa = quantize_e4m3(a)
     qb, sb = quantize_e4m3(b)
+    if w.layout == "bn":
+        qb = np.ascontiguousarray(qb.T)
     return Inputs(qa, qb, sa, sb)
 
 
