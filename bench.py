@@ -190,7 +190,8 @@ def main():
         log("bench: copy calibration %d MiB x 3" % args.calibrate_copy)
         del src, dst
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
-        "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192",
+        "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
+        "bf16_skinny_32x8192x8192_preshuffled", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192",
         "i8_8192", "w4a8_8192"])
     results = {}
     inputs = {}
@@ -198,7 +199,7 @@ def main():
         w = W.WORKLOADS[name]
         log("bench: generating", name)
         inp = W.make_inputs(w)
-        rotate = 3 if name == "bf16_skinny_32x8192x8192" else 1
+        rotate = 3 if name.startswith("bf16_skinny_32x8192x8192") else 1
         steps = args.steps if name == (args.only or HEADLINE) else max(10, args.steps // 2)
         ms, wall, info, shuf_ms = time_gemm(torch, tg, w, inp, steps, args.warmup, rotate)
         tflops = w.flops / (ms * 1e-3) / 1e12
@@ -223,7 +224,7 @@ def main():
     head = args.only or HEADLINE
     w = W.WORKLOADS[head]
     r = results[head]
-    bound = "hbm" if head == "bf16_skinny_32x8192x8192" else "mfma"
+    bound = "hbm" if head.startswith("bf16_skinny_32x8192x8192") else "mfma"
     traffic = None
     if head == HEADLINE:
         from profile_summary import read_traffic

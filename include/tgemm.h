@@ -285,7 +285,7 @@ typedef struct {
     int64_t M, N, K;
     int32_t dtype, layout;
     int32_t elem_bytes, out_bytes;
-    int32_t kernel;          /* 0 tiled, 1 skinny                                     */
+    int32_t kernel;          /* 0 tiled, 1 skinny (M <= 64, B N x K or pre-shuffled)  */
     int32_t tile_m, tile_n;  /* output tile of one workgroup                          */
     int32_t tile_k_bytes;    /* K bytes consumed per main-loop step (multiple of 64)  */
     int32_t threads;         /* threads per workgroup                                 */

@@ -167,6 +167,14 @@ def test_plan_choices(lib, monkeypatch):
     assert c["lds_bytes"] <= 160 * 1024 and c["grid"] == 1024
     c = info(32, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["kernel"] == 1 and c["grid"] == 256
+    # pre-shuffled B at decode shapes: the skinny kernel with B in registers
+    # (2 register stages, LDS for A's ring only)
+    for M, dt in ((1, tg.GEMM_BF16_OUT_BF16), (32, tg.GEMM_BF16_OUT_F32), (64, tg.GEMM_E4M3_OUT_BF16)):
+        c = info(M, 8192, 8192, dt, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+        assert (c["kernel"], c["grid"], c["tile_n"], c["lds_stages"]) == (1, 256, 32, 2)
+        assert c["tile_m"] >= M
+    c = info(65, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+    assert c["kernel"] == 0
     c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
     assert c["lds_stages"] == 4                      # fp8: B in registers

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 # "256x256p" pipelined 8-wave with B in registers, "256x256q" pipelined
 # 4-wave, "256x256g" generic, "128x128" generic, None with M <= 64 skinny.
 PATHS = [("256x256", "bt", None), ("256x256p", "bt", None), ("256x256q", "bt_preshuffled", None), ("256x256g", "bt", None),
-         ("128x128", "bt_preshuffled", None), (None, "bt", 33)]
+         ("128x128", "bt_preshuffled", None), (None, "bt", 33), (None, "bt_preshuffled", 33)]
 DTYPES = [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16")]
 
 

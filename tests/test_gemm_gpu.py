@@ -117,17 +117,39 @@ def test_integer_exact_every_path(oracle_mod, tile_env, dtype, out, layout, tile
     exact_check(oracle_mod, inp, M, N, K, dtype, out, layout, scale)
 
 
+@pytest.mark.parametrize("layout", ["bt", "bt_preshuffled"])
 @pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("e4m3", "bf16")])
 @pytest.mark.parametrize("M", [1, 17, 32, 33, 64])
-def test_integer_exact_skinny(oracle_mod, tile_env, dtype, out, M):
+@pytest.mark.parametrize("N,kpad", [(544, 0), (528, 64)])
+def test_integer_exact_skinny(oracle_mod, tile_env, dtype, out, M, layout, N, kpad):
+    # kpad = 64: K * elem_bytes is an odd multiple of 64, so the last 128-byte
+    # K step is half full; N = 528 leaves the last workgroup one 16-column block.
     tile_env(None)
-    N, K = 544, 1024 + 64 * (dtype == "bf16")      # bf16: 2176 bytes -> ragged last 128-byte step
-    say("case skinny int-exact", dtype, out, M, N, K)
-    inp = W.int_inputs(M, N, K, dtype, seed=M + 99)
-    with tg.Plan(M, N, K, gpu_dtype(dtype, out), tg.GEMM_LAYOUT_BT) as p:
+    K = (1024 + kpad) // (2 if dtype == "bf16" else 1)
+    say("case skinny int-exact", dtype, out, layout, M, N, K)
+    inp = W.int_inputs(M, N, K, dtype, seed=M + N + 99)
+    with tg.Plan(M, N, K, gpu_dtype(dtype, out), tg.LAYOUTS[layout]) as p:
         assert p.info()["kernel"] == 1
     scale = (2.0, 0.125) if dtype == "e4m3" else (1.0, 1.0)
-    exact_check(oracle_mod, inp, M, N, K, dtype, out, "bt", scale)
+    exact_check(oracle_mod, inp, M, N, K, dtype, out, layout, scale)
+
+
+@pytest.mark.parametrize("layout", ["bt", "bt_preshuffled"])
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("e4m3", "bf16")])
+@pytest.mark.parametrize("M", [1, 32, 64])
+def test_random_skinny(oracle_mod, tile_env, dtype, out, M, layout):
+    N, K = 784, 2080 if dtype == "bf16" else 4160
+    tile_env(None)
+    say("case skinny random", dtype, out, layout, M, N, K)
+    w = W.WORKLOADS["e4m3_8192" if dtype == "e4m3" else "bf16_skinny_32x8192x8192"]
+    inp = W.make_inputs(w, M=M, N=N, K=K, seed=777 + M)
+    C_bits, info = run_gemm(inp.A, inp.B, M, N, K, dtype, out, layout, scale=(inp.scale_a, inp.scale_b),
+                            return_plan_info=True)
+    assert info["kernel"] == 1
+    sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+    C_ref, S = oracle_mod.gemm_bt(inp.A, inp.B, dtype=dtype, sigma=sigma)
+    r = assert_within_bound(decode(C_bits), C_ref, S, dtype, "skinny random %s %s M=%d" % (dtype, layout, M))
+    say("  worst err/bound", r)
 
 
 def gpu_dtype(dtype, out):
@@ -154,7 +176,8 @@ def test_random_within_bound(oracle_mod, tile_env, dtype, out, layout, tile):
 # ------------------------------------------------------------------ full-size workloads, sampled
 
 @pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_4096", "256x256p"), ("bf16_8192_preshuffled", None),
-                                       ("bf16_skinny_32x8192x8192", None), ("e4m3_8192", None),
+                                       ("bf16_skinny_32x8192x8192", None),
+                                       ("bf16_skinny_32x8192x8192_preshuffled", None), ("e4m3_8192", None),
                                        ("bf16_8192_preshuffled", "256x256q"), ("e4m3_8192", "256x256q"),
                                        ("bf16_4096", "256x256q")])
 def test_full_size_sampled(oracle_mod, tile_env, name, tile):

@@ -187,19 +187,22 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
 
 const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
 {
-    if (I.layout != GEMM_LAYOUT_BT || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") || is_mx(I.dtype) ||
-        is_int(I.dtype))
+    if ((I.layout != GEMM_LAYOUT_BT && I.layout != GEMM_LAYOUT_BT_PRESHUFFLED) || I.M < 1 || I.M > 64 ||
+        getenv("TGEMM_TILE") || is_mx(I.dtype) || is_int(I.dtype))
         return nullptr;
+    const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
     const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
     int n = 0;
     const tg::SkinnyVariant *v = tg::skinny_variants(&n);
     if (const char *e = getenv("TGEMM_SKINNY_VARIANT")) {
         const int k = atoi(e);
-        if (k >= 0 && k < n && v[k].mblocks == mb && v[k].elem == elem_of(I.dtype) && v[k].out == out_of(I.dtype))
+        if (k >= 0 && k < n && v[k].mblocks == mb && v[k].elem == elem_of(I.dtype) && v[k].out == out_of(I.dtype) &&
+            v[k].preshuffled == pre)
             return &v[k];
     }
     for (int i = 0; i < n; ++i)
-        if (v[i].mblocks == mb && v[i].elem == elem_of(I.dtype) && v[i].out == out_of(I.dtype))
+        if (v[i].mblocks == mb && v[i].elem == elem_of(I.dtype) && v[i].out == out_of(I.dtype) &&
+            v[i].preshuffled == pre)
             return &v[i];
     return nullptr;
 }

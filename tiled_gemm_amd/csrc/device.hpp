@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "kernels.hpp"
 #include "layout.hpp"
@@ -392,6 +393,19 @@ __device__ inline u32x2 lds_read_tr8(const uint8_t *p)
 __device__ inline int bkn8_swz(int k) { return k & 7; }
 
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled,
+// so that register arrays indexed by the constant stay in registers.
+template <typename F, int... I>
+__device__ inline void static_for_seq(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F &&f)
+{
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
 }  // namespace tg

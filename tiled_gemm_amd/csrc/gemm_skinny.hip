@@ -29,6 +29,58 @@ namespace tg {
 
 constexpr int kRedPitch = kSkinnyTileN + 1;   // padded reduction row (bank spread)
 
+// Sums the waves' partial 16 x 16 tiles through LDS in a fixed wave order
+// (deterministic), then applies the epilogue and stores C.  The caller has
+// drained every load that writes LDS and synchronised the workgroup.
+template <int MB, int OUT, int WAVES>
+__device__ inline void skinny_finish(const SkinnyArgs &p, const f32x4 (&acc)[MB][kSkinnyTileN / 16], uint8_t *lds,
+                                     int n0)
+{
+    constexpr int NB = kSkinnyTileN / 16;
+    constexpr int ROWS_A = MB * 16;
+    const int w = wave_id();
+    const int l = lane_id();
+    const int q = l >> 4, r16 = l & 15;
+    using RedRows = float[ROWS_A][kRedPitch];
+    RedRows *red = reinterpret_cast<RedRows *>(lds);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[w][i * 16 + r16][j * 16 + 4 * q + v] = acc[i][j][v];
+    __syncthreads();
+
+    const EpiView ev = epi_view(p.epi, p.M, p.N);
+    constexpr int OB = OUT == kOutF32 ? 4 : 2;
+    const uint32_t ldc = (uint32_t)p.N * OB;
+    const auto rC = make_rsrc(p.C, (uint32_t)p.M * ldc);
+    // Each thread finishes pairs of adjacent outputs.
+    for (int o = threadIdx.x * 2; o < ROWS_A * kSkinnyTileN; o += 64 * WAVES * 2) {
+        const int row = o / kSkinnyTileN, col = o % kSkinnyTileN;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < WAVES; ++ww) {
+            s0 += red[ww][row][col];
+            s1 += red[ww][row][col + 1];
+        }
+        const int n = n0 + col;
+        float sb[2], bz[2];
+        epi_col2(ev, n, sb, bz);
+        const float sa = epi_row_scale(ev, row);
+        s0 = epi_apply1(ev, s0, sa, sb[0], bz[0]);
+        s1 = epi_apply1(ev, s1, sa, sb[1], bz[1]);
+        const uint32_t voffc = (row < p.M && n < p.N) ? (uint32_t)row * ldc + (uint32_t)n * OB : kOobOffset;
+        if constexpr (OUT == kOutF32)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, s0),
+                                                        __builtin_bit_cast(uint32_t, s1)},
+                                                  rC, voffc, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(s0, s1), rC, voffc, 0, 0);
+    }
+}
+
 template <int MB, int WAVES, int DEPTH>
 struct SkinnyCfg {
     static constexpr int ROWS_A = MB * 16;
@@ -157,45 +209,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_kernel(const Skinny
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);
     __syncthreads();
 
-    // ---- cross-wave reduction in a fixed order, then the epilogue.
-    using RedRows = float[Cfg::ROWS_A][kRedPitch];
-    RedRows *red = reinterpret_cast<RedRows *>(lds);
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                red[w][i * 16 + r16][j * 16 + 4 * q + v] = acc[i][j][v];
-    __syncthreads();
-
-    const EpiView ev = epi_view(p.epi, p.M, p.N);
-    constexpr int OB = OUT == kOutF32 ? 4 : 2;
-    const uint32_t ldc = (uint32_t)p.N * OB;
-    const auto rC = make_rsrc(p.C, (uint32_t)p.M * ldc);
-    // Each thread finishes pairs of adjacent outputs.
-    for (int o = threadIdx.x * 2; o < Cfg::ROWS_A * kSkinnyTileN; o += 64 * WAVES * 2) {
-        const int row = o / kSkinnyTileN, col = o % kSkinnyTileN;
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < WAVES; ++ww) {
-            s0 += red[ww][row][col];
-            s1 += red[ww][row][col + 1];
-        }
-        const int n = n0 + col;
-        float sb[2], bz[2];
-        epi_col2(ev, n, sb, bz);
-        const float sa = epi_row_scale(ev, row);
-        s0 = epi_apply1(ev, s0, sa, sb[0], bz[0]);
-        s1 = epi_apply1(ev, s1, sa, sb[1], bz[1]);
-        const uint32_t voffc = (row < p.M && n < p.N) ? (uint32_t)row * ldc + (uint32_t)n * OB : kOobOffset;
-        if constexpr (OUT == kOutF32)
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, s0),
-                                                        __builtin_bit_cast(uint32_t, s1)},
-                                                  rC, voffc, 0, 0);
-        else
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(s0, s1), rC, voffc, 0, 0);
-    }
+    skinny_finish<MB, OUT, WAVES>(p, acc, lds, n0);
 }
 
 template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool ROTATE>
@@ -206,11 +220,186 @@ static hipError_t launch_skinny(const SkinnyArgs &a, int grid, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Skinny GEMM with B pre-shuffled.  The pre-shuffled image stores each
+// 16-column block's operand for 64 bytes of K as one contiguous 1 KiB, in
+// the MFMA lane order (lane l: column l % 16, K bytes 16 (l / 16) .. +15), so
+// B goes straight from HBM into VGPRs with whole-line, fully contiguous wave
+// loads and never touches LDS.  Only A, which every workgroup re-reads from
+// L2, is staged: whole-line LDS-writing loads into a per-wave ring, read back
+// in the MFMA order like the tiled kernels' A.  The step, the K split over
+// the waves, the rotation and the reduction are those of the kernel above.
+// ---------------------------------------------------------------------------
+template <int MB, int WAVES, int DEPTH, bool BLDS>
+struct SkinnyPreCfg {
+    static constexpr int ROWS_A = MB * 16;
+    static constexpr int ASTAGE = ROWS_A * kTileKBytes;     // A bytes per stage
+    static constexpr int BL = 2 * (kSkinnyTileN / 16);      // 1 KiB B loads per stage
+    static constexpr int STAGE = ASTAGE + (BLDS ? BL * 1024 : 0);
+    static constexpr int RING = DEPTH * STAGE;              // bytes per wave
+    static constexpr int AL = ROWS_A / 8;                   // 1 KiB A loads per stage
+    static constexpr int LOADS = AL + BL;
+    static constexpr int RED = WAVES * ROWS_A * kRedPitch * 4;
+    static constexpr int LDS = WAVES * RING > RED ? WAVES * RING : RED;
+    static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+    static_assert((DEPTH - 1) * LOADS < 64, "vmcnt holds 6 bits");
+};
+
+template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool BLDS, int ORD>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const SkinnyArgs p)
+{
+    using Cfg = SkinnyPreCfg<MB, WAVES, DEPTH, BLDS>;
+    constexpr int NB = kSkinnyTileN / 16;
+    constexpr int AL = Cfg::AL;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
+
+    const int w = wave_id();
+    const int l = lane_id();
+    const int q = l >> 4, r16 = l & 15;
+    const int n0 = blockIdx.x * kSkinnyTileN;
+    const uint32_t kb = (uint32_t)p.kbytes;
+    const int rows_b = min(p.N - n0, kSkinnyTileN);
+    const auto rA = make_rsrc(p.A, (uint32_t)p.M * kb);
+    // The workgroup's 16-column blocks are contiguous in the image (16 * kb
+    // bytes each); a block past N lies past the record count (zeros).
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
+    const int nk = p.k_tiles;
+    const uint32_t tail = (uint32_t)p.tail_bytes;
+    uint8_t *const ring = lds + w * Cfg::RING;
+
+    // A: wave load j covers rows 8j .. 8j + 7 of the stage, as above.
+    uint32_t voffA[AL];
+    uint32_t half_keep = 0;
+#pragma unroll
+    for (int j = 0; j < AL; ++j) {
+        const int row = 8 * j + (l >> 3);
+        const int c = swz_chunk(row, l & 7);
+        voffA[j] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
+        half_keep |= (c < kChunksPerRow / 2 ? 1u : 0u) << j;
+    }
+
+    // ORD: 0 runs of steps, rotated start; 1 runs; 2 steps w, w + WAVES, ...,
+    // rotated start; 3 the same without rotation
+    constexpr bool INTER = ORD >= 2;
+    const int per = (nk + WAVES - 1) / WAVES;
+    const int first = INTER ? w : w * per;
+    const int nt = INTER ? (w < nk ? (nk - w + WAVES - 1) / WAVES : 0) : max(0, min(per, nk - first));
+    const int rot = (ORD == 0 || ORD == 2) ? (int)((blockIdx.x * 37u) % (uint32_t)max(nk, 1)) : 0;
+
+    // B of one step: 64-byte K blocks 2 kt + h of 16-column block j.
+    u32x4 bq[DEPTH][NB][2];
+
+    // Step t of this wave into stage s.  Every load is issued; those past the
+    // run, or past K in a half-filled last step, are out of range (zeros).
+    auto issue = [&](int t, auto s_c) {
+        constexpr int S = decltype(s_c)::value;
+        int kt = first + (INTER ? WAVES * t : t) + rot;
+        kt = kt >= nk ? kt - nk : kt;
+        const bool in = t < nt;
+        const bool part = (kt == nk - 1) & (tail != (uint32_t)kTileKBytes);
+        const uint32_t soffA = in ? (uint32_t)kt * kTileKBytes : 0u;
+        uint8_t *const dst = ring + S * Cfg::STAGE;
+#pragma unroll
+        for (int j = 0; j < AL; ++j) {
+            const bool keep = in & (!part | (((half_keep >> j) & 1u) != 0));
+            buf_load16_to_lds(rA, dst + j * 1024, keep_or_oob(keep, voffA[j]), soffA);
+        }
+        const uint32_t soffB = in ? (uint32_t)kt * 2048u : 0u;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool keep = in & (!part | (h == 0));
+                const uint32_t voffB = keep_or_oob(keep, (uint32_t)j * 16u * kb + (uint32_t)h * 1024u + (uint32_t)l * 16u);
+                if constexpr (BLDS)
+                    buf_load16_to_lds(rB, dst + Cfg::ASTAGE + (2 * j + h) * 1024, voffB, soffB);
+                else
+                    bq[S][j][h] = buf_load16(rB, voffB, soffB);
+            }
+        issue_fence();
+    };
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // A operands: lane l takes row l % 16 of each 16-row block and chunks
+    // l / 16 (paired with K block 2 kt) and 4 + l / 16 (block 2 kt + 1).
+    auto compute = [&](auto s_c) {
+        constexpr int S = decltype(s_c)::value;
+        const uint8_t *const st = ring + S * Cfg::STAGE;
+        u32x4 a[MB][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int row = i * 16 + r16;
+                a[i][h] = lds_load16(st + row * kTileKBytes + swz_chunk(row, h * 4 + q) * kChunkBytes);
+            }
+        if constexpr (BLDS) {
+            // the staged operand blocks are in lane order already
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    bq[S][j][h] = lds_load16(st + Cfg::ASTAGE + (2 * j + h) * 1024 + l * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if constexpr (ELEM == kBf16) {
+                    acc[i][j] = mfma_bf16(bq[S][j][0], a[i][0], acc[i][j]);
+                    acc[i][j] = mfma_bf16(bq[S][j][1], a[i][1], acc[i][j]);
+                } else {
+                    acc[i][j] = mfma_fp8x8(join32(bq[S][j][0], bq[S][j][1]), join32(a[i][0], a[i][1]), acc[i][j]);
+                }
+            }
+    };
+
+    // Waiting for the oldest stage leaves the DEPTH - 1 younger ones in
+    // flight.  The run is rounded up to whole rings; the extra steps load and
+    // multiply zeros.
+    constexpr int kVm = (DEPTH - 1) * Cfg::LOADS;
+    constexpr int kWaitOldest = (kWaitVmcnt0 & ~0xC00F) | (kVm & 0xF) | ((kVm >> 4) << 14);
+    constexpr int kWaitLds = 0xC07F;
+    const int ntr = (nt + DEPTH - 1) / DEPTH * DEPTH;
+    static_for<DEPTH>([&](auto s_c) { issue(decltype(s_c)::value, s_c); });
+    for (int t0 = 0; t0 < ntr; t0 += DEPTH) {
+        static_for<DEPTH>([&](auto s_c) {
+            __builtin_amdgcn_s_waitcnt(kWaitOldest);
+            compute(s_c);
+            __builtin_amdgcn_s_waitcnt(kWaitLds);     // the stage's A reads are done before its refill
+            issue(t0 + decltype(s_c)::value + DEPTH, s_c);
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);
+    __syncthreads();
+    skinny_finish<MB, OUT, WAVES>(p, acc, lds, n0);
+}
+
+template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool BLDS, int ORD>
+static hipError_t launch_skinny_pre(const SkinnyArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_skinny_pre_kernel<MB, ELEM, OUT, WAVES, DEPTH, BLDS, ORD>), dim3(grid), dim3(64 * WAVES), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
 #define TG_SKINNY(MB, ELEM, OUT, WAVES, DEPTH, ROTATE)                                                       \
     SkinnyVariant{MB, ELEM, OUT, WAVES, DEPTH, SkinnyCfg<MB, WAVES, DEPTH>::LDS,                             \
                   &launch_skinny<MB, ELEM, OUT, WAVES, DEPTH, ROTATE>}
 
-// The first variant of each (rows, elem, out) is the planner's choice; the
+#define TG_SKINNY_PRE_O(MB, ELEM, OUT, WAVES, DEPTH, BLDS, ORD)                                              \
+    SkinnyVariant{MB, ELEM, OUT, WAVES, DEPTH, SkinnyPreCfg<MB, WAVES, DEPTH, BLDS>::LDS,                    \
+                  &launch_skinny_pre<MB, ELEM, OUT, WAVES, DEPTH, BLDS, ORD>, true}
+#define TG_SKINNY_PRE_L(MB, ELEM, OUT, WAVES, DEPTH, BLDS) TG_SKINNY_PRE_O(MB, ELEM, OUT, WAVES, DEPTH, BLDS, 1)
+#define TG_SKINNY_PRE(MB, ELEM, OUT, WAVES, DEPTH) TG_SKINNY_PRE_L(MB, ELEM, OUT, WAVES, DEPTH, false)
+
+// The first variant of each (rows, elem, out, B layout) is the planner's choice; the
 // rest are alternatives selectable by index with TGEMM_SKINNY_VARIANT.
 static const SkinnyVariant kSkinny[] = {
     TG_SKINNY(1, kBf16, kOutBf16, 8, 3, true), TG_SKINNY(2, kBf16, kOutBf16, 8, 2, true),
@@ -221,6 +410,19 @@ static const SkinnyVariant kSkinny[] = {
     // alternatives for the 32-row bf16 shape
     TG_SKINNY(2, kBf16, kOutBf16, 8, 2, false), TG_SKINNY(2, kBf16, kOutBf16, 4, 4, true),
     TG_SKINNY(2, kBf16, kOutBf16, 2, 8, true),
+    // B pre-shuffled (register-staged B, steps in runs, no rotation)
+    TG_SKINNY_PRE(1, kBf16, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kBf16, kOutBf16, 12, 2),     // 12
+    TG_SKINNY_PRE(4, kBf16, kOutBf16, 8, 2),  TG_SKINNY_PRE(1, kBf16, kOutF32, 12, 2),
+    TG_SKINNY_PRE(2, kBf16, kOutF32, 12, 2),  TG_SKINNY_PRE(4, kBf16, kOutF32, 8, 2),
+    TG_SKINNY_PRE(1, kFp8, kOutBf16, 12, 2),  TG_SKINNY_PRE(2, kFp8, kOutBf16, 12, 2),      // 18
+    TG_SKINNY_PRE(4, kFp8, kOutBf16, 8, 2),
+    // alternatives for the 32-row bf16 shape: (waves, stages, B via LDS, order)
+    TG_SKINNY_PRE_O(2, kBf16, kOutBf16, 8, 4, false, 0), TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 4),   // 21
+    TG_SKINNY_PRE(2, kBf16, kOutBf16, 16, 2), TG_SKINNY_PRE(2, kBf16, kOutBf16, 12, 3),
+    TG_SKINNY_PRE_L(2, kBf16, kOutBf16, 8, 2, true), TG_SKINNY_PRE_O(2, kBf16, kOutBf16, 12, 2, false, 3), // 25
+    TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 3), TG_SKINNY_PRE(2, kBf16, kOutBf16, 10, 2),
+    // alternative for the 64-row shape
+    TG_SKINNY_PRE(4, kBf16, kOutBf16, 4, 4),                                                    // 29
 };
 
 const SkinnyVariant *skinny_variants(int *count)

@@ -102,6 +102,7 @@ struct SkinnyVariant {
     int stages;             // LDS stages per wave
     int lds_bytes;
     hipError_t (*launch)(const SkinnyArgs &, int grid, hipStream_t);
+    bool preshuffled = false;   // B is the pre-shuffled image (register-staged B)
 };
 
 constexpr int kSkinnyTileN = 32;

@@ -99,6 +99,10 @@ WORKLOADS = {
                                          "bf16", "bt", ("normal", 0.0, 1.0),
                                          ("normal", 0.0, 0.02), 1004,
                                          "decode-like, HBM-bound"),
+    "bf16_skinny_32x8192x8192_preshuffled": Workload("bf16_skinny_32x8192x8192_preshuffled", 32, 8192, 8192,
+                                                     "bf16", "bf16", "bt_preshuffled", ("normal", 0.0, 1.0),
+                                                     ("normal", 0.0, 0.02), 1014,
+                                                     "decode-like with a pre-shuffled weight, HBM-bound"),
     "e4m3_8192": Workload("e4m3_8192", 8192, 8192, 8192, "e4m3", "bf16", "bt",
                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1005,
                           "per-tensor scales amax/448"),
