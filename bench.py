@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "i8": 5000.0, "w4a8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_preshuffled"
+# Workloads with fewer 256 x 256 tiles than CUs: timed through gemm_run_ws
+# (split K with a workspace), plain gemm_run reported beside.
+SPLIT_K_WORKLOADS = ("bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192")
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE scaled by a copy of known size (see the file for the commands).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_pipe_bf16_8192_preshuffled.txt")
@@ -39,14 +42,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
+def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None, ws=False):
     """Time `steps` gemm_run launches (after `warmup`) with HIP events on the
     launch stream.  With rotate > 1, that many independent input/output sets
     are cycled so the operands are not served from the last-level cache.
     With epi (an epilogue name), gemm_run_ex is timed instead, with per-row
     and per-column scale vectors and a bias vector.  Integer workloads run
     through gemm_run_ex with their per-row / per-channel dequantisation
-    scales."""
+    scales.  With ws, gemm_run_ws with a workspace of gemm_workspace_bytes
+    (split K where the plan splits)."""
     code = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
             ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16, ("mxfp8", "bf16"): tg.GEMM_MXFP8_OUT_BF16,
             ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16, ("i8", "bf16"): tg.GEMM_I8_OUT_BF16,
@@ -96,6 +100,12 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None):
         def launch(A, B, C):
             plan.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream=s, scale_a=qa.data_ptr(),
                         scale_a_per_row=True, scale_b=qb.data_ptr(), scale_b_per_col=True)
+    elif ws:
+        wsb = plan.workspace_bytes()
+        Wk = torch.empty(max(16, wsb), dtype=torch.uint8, device="cuda")
+
+        def launch(A, B, C):
+            plan.run_ws(A.data_ptr(), B.data_ptr(), C.data_ptr(), Wk.data_ptr(), wsb, stream=s)
     elif epi is None:
         def launch(A, B, C):
             plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
@@ -191,8 +201,8 @@ def main():
         del src, dst
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
         "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
-        "bf16_skinny_32x8192x8192_preshuffled", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192",
-        "i8_8192", "w4a8_8192"])
+        "bf16_skinny_32x8192x8192_preshuffled", "bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192",
+        "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "i8_8192", "w4a8_8192"])
     results = {}
     inputs = {}
     for name in names:
@@ -201,11 +211,17 @@ def main():
         inp = W.make_inputs(w)
         rotate = 3 if name.startswith("bf16_skinny_32x8192x8192") else 1
         steps = args.steps if name == (args.only or HEADLINE) else max(10, args.steps // 2)
-        ms, wall, info, shuf_ms = time_gemm(torch, tg, w, inp, steps, args.warmup, rotate)
+        split = name in SPLIT_K_WORKLOADS
+        if split:
+            # split K through gemm_run_ws; the plain gemm_run figure beside it
+            ms1, _, _, _ = time_gemm(torch, tg, w, inp, steps, args.warmup, rotate)
+        ms, wall, info, shuf_ms = time_gemm(torch, tg, w, inp, steps, args.warmup, rotate, ws=split)
         tflops = w.flops / (ms * 1e-3) / 1e12
         gbs = w.min_bytes / (ms * 1e-3) / 1e9
         results[name] = dict(ms=ms, wall=wall, steps=steps, tflops=tflops, gbs=gbs, info=info,
                              shuf_ms=shuf_ms, rotate=rotate)
+        if split:
+            results[name]["ms_gemm_run"] = ms1
         log("bench: %-26s %.4f ms  %.1f TFLOP/s  %.0f GB/s  tile %dx%d grid %d" % (
             name, ms, tflops, gbs, info["tile_m"], info["tile_n"], info["grid"]))
         if name == HEADLINE:
@@ -268,6 +284,12 @@ def main():
                       "GB/s": round(rr["gbs"], 1), "frac_hbm_peak": round(rr["gbs"] / PEAK_HBM_GBS, 4),
                       "tile": "%dx%d" % (rr["info"]["tile_m"], rr["info"]["tile_n"]),
                       "input_sets_rotated": rr["rotate"]}
+        if "ms_gemm_run" in rr:
+            also[name]["split_k"] = rr["info"]["ws_splits"]
+            also[name]["ms_gemm_run"] = round(rr["ms_gemm_run"], 5)
+    if head in SPLIT_K_WORKLOADS:
+        line["config"]["split_k"] = r["info"]["ws_splits"]
+        line["config"]["ms_gemm_run"] = round(r["ms_gemm_run"], 5)
     if also:
         line["also"] = also
     if not args.no_cpu_baseline and head in inputs:

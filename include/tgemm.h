@@ -197,6 +197,42 @@ int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C,
                 const gemm_epilogue_args *epi, hipStream_t stream);
 
 /*
+ * Split K with a caller-provided workspace.  When a problem has fewer
+ * 256 x 256 output tiles than the chip has compute units (a few hundred rows
+ * of A against a large B: batched decode, small prefill), each tile is
+ * computed by s workgroups that take one K slice each and write fp32 partial
+ * tiles to the workspace; a second kernel sums the s partials of every
+ * element in slice order (deterministic) and applies the epilogue of
+ * gemm_run_ex.  The plan decides s (gemm_plan_info.ws_splits); plans with
+ * s == 1 need no workspace.  bf16 plans with GEMM_LAYOUT_BT or
+ * GEMM_LAYOUT_BT_PRESHUFFLED split; the others never do.  (The pages' GEMM
+ * has no split K: this is this library's answer to shapes whose tile grid
+ * leaves most of the chip idle.)
+ *
+ * gemm_workspace_bytes -- bytes gemm_run_ws needs to split K:
+ *   ws_splits * M * N * 4, or 0 when the plan does not split (or NULL).
+ */
+size_t gemm_workspace_bytes(const gemm_plan *plan);
+
+/*
+ * gemm_run_ws -- gemm_run_ex, split over K when the workspace allows it.
+ *   A, B, C, epi, stream  as for gemm_run_ex.
+ *   workspace        device pointer, 16-byte aligned, not overlapping A, B
+ *                    or C; owned by the caller, contents need not be
+ *                    initialised and are undefined afterwards.
+ *   workspace_bytes  its size.  With a NULL workspace or fewer than
+ *                    gemm_workspace_bytes(plan) bytes the call is exactly
+ *                    gemm_run_ex (no split).
+ * Two launches on `stream` (tile kernel, then the reduction); asynchronous;
+ * allocates nothing.  Calls that share one workspace must not overlap in time
+ * (issue them on one stream).  Errors as gemm_run_ex, plus
+ * GEMM_ERR_INVALID_ARG for a misaligned or overlapping workspace.
+ */
+int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *C,
+                const gemm_epilogue_args *epi, void *workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
  * MX block-scaled operands (GEMM_MXFP8_OUT_BF16, GEMM_MXFP4_OUT_BF16).  The
  * pages' gfx950 scaled MFMA (FlyDSL "Kernel authoring guide", section 4.3
  * "ROCm intrinsics", MFMA instructions: mfma_scale_f32_16x16x128_f8f6f4)
@@ -298,6 +334,9 @@ typedef struct {
     int32_t elem_bits;       /* bits per input element of A (16, 8 or 4); elem_bytes
                                 is elem_bits / 8, so 0 for MXFP4                       */
     int32_t b_elem_bits;     /* bits per input element of B (4 for W4A8, else elem_bits) */
+    int32_t ws_splits;       /* K slices gemm_run_ws uses with a large enough
+                                workspace (1: it runs as gemm_run_ex)                 */
+    int32_t ws_grid;         /* workgroups of gemm_run_ws's tile launch               */
 } gemm_plan_info;
 
 /* gemm_plan_query -- copy the plan's decisions into *info. */

@@ -39,14 +39,16 @@ def _dev_f32(x):
 
 def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
              scale=(1.0, 1.0), use_scale=True, stream=None, plan=None, return_plan_info=False, epi=None,
-             sa_blocks=None, sb_blocks=None):
+             sa_blocks=None, sb_blocks=None, workspace=None):
     """One C = A * B^T through gemm_plan_create / [gemm_preshuffle_b] /
     gemm_run, or gemm_run_ex when ``epi`` is given: a dict with optional
     scale_a (scalar or M values), scale_b (scalar or N values), bias (N
     values) and kind (a name in tg.EPILOGUES).  MX dtypes take the E8M0 block
     scales sa_blocks (M x K/32) and sb_blocks (N x K/32) and run through
     gemm_preshuffle_bscale + gemm_run_mx.  Returns the raw bits of C as a
-    numpy array (M x N)."""
+    numpy array (M x N).  ``workspace`` runs gemm_run_ws: True gives it
+    gemm_workspace_bytes(plan) bytes, an int that many (0: a NULL workspace);
+    per-tensor ``scale`` then goes in as the epilogue's two scalars."""
     code = DTYPE_CODE[(dtype, out)]
     lay = tg.LAYOUTS[layout]
     own = plan is None
@@ -72,6 +74,19 @@ def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
             imgs.append((src, img))
         plan.run_mx(A.data_ptr(), imgs[0][1].data_ptr(), Bx.data_ptr(), imgs[1][1].data_ptr(), C.data_ptr(),
                     stream=s, scale_a=keep["scale_a"].data_ptr() if "scale_a" in keep else None,
+                    scale_a_per_row=np.ndim(e.get("scale_a")) > 0,
+                    scale_b=keep["scale_b"].data_ptr() if "scale_b" in keep else None,
+                    scale_b_per_col=np.ndim(e.get("scale_b")) > 0,
+                    bias=keep["bias"].data_ptr() if "bias" in keep else None,
+                    epilogue=tg.EPILOGUES[e.get("kind", "none")])
+    elif workspace is not None and workspace is not False:
+        e = dict(epi) if epi is not None else (
+            dict(scale_a=scale[0], scale_b=scale[1], kind="none") if use_scale else dict(kind="none"))
+        keep = {k: _dev_f32(e[k]) for k in ("scale_a", "scale_b", "bias") if e.get(k) is not None}
+        wsb = plan.workspace_bytes() if workspace is True else int(workspace)
+        W = torch.full((max(16, wsb),), 0x7F, dtype=torch.uint8, device="cuda")   # garbage: never read unwritten
+        plan.run_ws(A.data_ptr(), Bx.data_ptr(), C.data_ptr(), W.data_ptr() if wsb else None, wsb, stream=s,
+                    scale_a=keep["scale_a"].data_ptr() if "scale_a" in keep else None,
                     scale_a_per_row=np.ndim(e.get("scale_a")) > 0,
                     scale_b=keep["scale_b"].data_ptr() if "scale_b" in keep else None,
                     scale_b_per_col=np.ndim(e.get("scale_b")) > 0,

@@ -383,3 +383,53 @@ def test_mx_entry_point_guards(lib):
         assert p.bscale_image_bytes(0) == 0
     with tg.Plan(0, 256, 256, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
         assert lib.gemm_run_mx(p.handle, None, None, None, None, None, None, None) == tg.GEMM_OK
+
+
+def test_split_k_plans(lib, monkeypatch):
+    """Split K (gemm_run_ws): slices while 256 x 256 tiles x slices <= 256 and
+    each slice keeps >= 8 K steps; every slice non-empty; workspace bytes."""
+    monkeypatch.delenv("TGEMM_SPLIT", raising=False)
+
+    def plan(M, N, K, dt=tg.GEMM_BF16_OUT_BF16, lay=tg.GEMM_LAYOUT_BT_PRESHUFFLED):
+        with tg.Plan(M, N, K, dt, lay) as p:
+            return p.info(), p.workspace_bytes()
+    for M, want in ((65, 8), (256, 8), (257, 4), (512, 4), (768, 2), (1024, 2), (1025, 1), (8192, 1)):
+        info, ws = plan(M, 8192, 8192)
+        assert info["ws_splits"] == want, (M, info["ws_splits"])
+        assert ws == (want * M * 8192 * 4 if want > 1 else 0)
+        tiles = -(-M // 256) * 32
+        assert info["ws_grid"] == (tiles * want if want > 1 else info["grid"])
+    # K bounds the slices: 8 steps (1 KiB of K) each at least
+    assert plan(256, 8192, 2048)[0]["ws_splits"] == 4            # 32 steps of 128 bytes
+    assert plan(256, 8192, 512)[0]["ws_splits"] == 1
+    # skinny, fp8, MX, integer and K-major layouts never split
+    assert plan(64, 8192, 8192)[0]["ws_splits"] == 1
+    assert plan(256, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)[0]["ws_splits"] == 1
+    assert plan(256, 8192, 8192, tg.GEMM_I8_OUT_BF16)[0]["ws_splits"] == 1
+    assert plan(256, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)[0]["ws_splits"] == 1
+    # a forced count, uneven slices; an impossible one is refused (no split)
+    monkeypatch.setenv("TGEMM_SPLIT", "3")
+    assert plan(136, 528, 4160)[0]["ws_splits"] == 3
+    monkeypatch.setenv("TGEMM_SPLIT", "64")
+    assert plan(136, 528, 4160)[0]["ws_splits"] == 1                # 65 steps: slices would be empty
+    # the generic tiled kernel does not read the split fields: never split on it
+    monkeypatch.setenv("TGEMM_SPLIT", "4")
+    monkeypatch.setenv("TGEMM_PIPE", "0")
+    assert plan(256, 8192, 8192)[0]["ws_splits"] == 1
+
+
+def test_run_ws_argument_errors(lib):
+    M, N, K = 256, 8192, 8192
+    with tg.Plan(M, N, K, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        need = p.workspace_bytes()
+        A, B, C, Wk = 1 << 32, 2 << 32, 3 << 32, 4 << 32          # never dereferenced: validation fails first
+        with pytest.raises(tg.GemmError) as e:
+            p.run_ws(A, B, C, Wk + 8, need)
+        assert e.value.code == tg.GEMM_ERR_INVALID_ARG and "aligned" in tg.gemm_last_error()
+        with pytest.raises(tg.GemmError) as e:
+            p.run_ws(A, B, C, C, need)                             # workspace over C
+        assert "overlaps" in tg.gemm_last_error()
+        with pytest.raises(tg.GemmError) as e:
+            p.run_ws(A, B, C, Wk, need, epilogue=tg.GEMM_EPI_BIAS)  # bias epilogue without a bias
+        assert e.value.code == tg.GEMM_ERR_INVALID_ARG
+    assert tg.gemm_workspace_bytes(None) == 0

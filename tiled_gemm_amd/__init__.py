@@ -47,7 +47,8 @@ EXPORTS = (
     "gemm_plan_create", "gemm_plan_destroy", "gemm_preshuffled_b_bytes", "gemm_preshuffle_b",
     "gemm_run", "gemm_run_ex", "gemm_bscale_image_bytes", "gemm_preshuffle_bscale", "gemm_run_mx",
     "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
-    "gemm_layout_idx2crd", "gemm_lds_swizzle", "gemm_tile_of_workgroup",
+    "gemm_layout_idx2crd", "gemm_lds_swizzle", "gemm_tile_of_workgroup", "gemm_workspace_bytes",
+    "gemm_run_ws",
 )
 
 
@@ -68,7 +69,7 @@ class gemm_plan_info(ctypes.Structure):
         (f, ctypes.c_int32) for f in (
             "dtype", "layout", "elem_bytes", "out_bytes", "kernel", "tile_m", "tile_n",
             "tile_k_bytes", "threads", "lds_stages", "lds_bytes", "grid", "tiles_m", "tiles_n",
-            "group_m", "split_k", "elem_bits", "b_elem_bits")]
+            "group_m", "split_k", "elem_bits", "b_elem_bits", "ws_splits", "ws_grid")]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -99,6 +100,8 @@ def load() -> ctypes.CDLL:
         "gemm_bscale_image_bytes": (ctypes.c_size_t, [vp, c_int]),
         "gemm_preshuffle_bscale": (c_int, [vp, c_int, vp, vp, vp]),
         "gemm_run_mx": (c_int, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp]),
+        "gemm_workspace_bytes": (ctypes.c_size_t, [vp]),
+        "gemm_run_ws": (c_int, [vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp, ctypes.c_size_t, vp]),
         "gemm_last_error": (ctypes.c_char_p, []),
         "gemm_plan_query": (c_int, [vp, ctypes.POINTER(gemm_plan_info)]),
         "gemm_plan_layout": (c_int, [vp, c_int, p32, p64, p64]),
@@ -161,6 +164,20 @@ def gemm_run_ex(plan: int, A: int, B: int, C: int, scale_a: int | None = None, s
     epi = gemm_epilogue_args(scale_a or None, scale_b or None, bias or None, int(scale_a_per_row),
                              int(scale_b_per_col), epilogue)
     _check(load().gemm_run_ex(plan, A, B, C, ctypes.byref(epi), stream), "gemm_run_ex")
+
+
+def gemm_workspace_bytes(plan: int) -> int:
+    return int(load().gemm_workspace_bytes(plan))
+
+
+def gemm_run_ws(plan: int, A: int, B: int, C: int, workspace: int | None, workspace_bytes: int,
+                scale_a: int | None = None, scale_a_per_row: bool = False, scale_b: int | None = None,
+                scale_b_per_col: bool = False, bias: int | None = None, epilogue: int = GEMM_EPI_NONE,
+                stream: int = 0) -> None:
+    epi = gemm_epilogue_args(scale_a or None, scale_b or None, bias or None, int(scale_a_per_row),
+                             int(scale_b_per_col), epilogue)
+    _check(load().gemm_run_ws(plan, A, B, C, ctypes.byref(epi), workspace or None, workspace_bytes, stream),
+           "gemm_run_ws")
 
 
 def gemm_bscale_image_bytes(plan: int, operand: int) -> int:
@@ -274,3 +291,11 @@ class Plan:
     def run_ex(self, A: int, B: int, C: int, stream: int = 0, **epi) -> None:
         """gemm_run_ex; keyword arguments as for the module-level gemm_run_ex."""
         gemm_run_ex(self.handle, A, B, C, stream=stream, **epi)
+
+    def workspace_bytes(self) -> int:
+        return gemm_workspace_bytes(self.handle)
+
+    def run_ws(self, A: int, B: int, C: int, workspace: int | None, workspace_bytes: int, stream: int = 0,
+               **epi) -> None:
+        """gemm_run_ws; keyword arguments as for the module-level gemm_run_ex."""
+        gemm_run_ws(self.handle, A, B, C, workspace, workspace_bytes, stream=stream, **epi)

@@ -24,6 +24,11 @@ struct gemm_plan {
     int32_t k_tiles, tail_bytes;
     const tg::TiledVariant *tiled;     // kernel == 0
     const tg::SkinnyVariant *skinny;   // kernel == 1
+    // Split K with a workspace (gemm_run_ws): the 256 x 256 fp32-output
+    // variant, the number of K slices and the steps per slice; splits == 1
+    // when splitting does not pay.
+    const tg::TiledVariant *split_v;
+    int32_t splits, split_steps, split_grid, split_tiles_m, split_tiles_n, split_group_m;
 };
 
 namespace {
@@ -89,7 +94,7 @@ int out_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? tg::kOutF32 : tg::kO
 
 // Static tile table: the first entry whose predicate holds.  An optional
 // TGEMM_TILE=<bm>x<bn> in the environment forces a tiled variant (sweeps).
-const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
+const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = false)
 {
     int n = 0;
     const tg::TiledVariant *v = tg::tiled_variants(&n);
@@ -127,7 +132,9 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I)
         return nullptr;
     }
     int want_bm = 0, want_bn = 0;
-    if (const char *e = getenv("TGEMM_TILE"))
+    if (force256)
+        want_bm = want_bn = 256;
+    else if (const char *e = getenv("TGEMM_TILE"))
         if (sscanf(e, "%dx%d", &want_bm, &want_bn) != 2)
             want_bm = want_bn = 0;
     if (!want_bm) {
@@ -205,6 +212,55 @@ const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
             v[i].preshuffled == pre)
             return &v[i];
     return nullptr;
+}
+
+// Split K for the workspace entry point.  A problem whose 256 x 256 tiles
+// number fewer than the 256 CUs (a few hundred rows against a large B) is
+// bound by how fast each CU streams its tile's operands, so K is divided into
+// s slices: tiles * s workgroups each write an fp32 partial tile, and a
+// reduction kernel sums the slices in order and applies the epilogue.  s is
+// the largest power of two with tiles * s <= 256 and at least 8 K steps
+// (1 KiB of K) per slice; TGEMM_SPLIT=<s> forces it (sweeps; 1 disables).
+void plan_split(gemm_plan *p)
+{
+    const gemm_plan_info &I = p->info;
+    p->splits = 1;
+    p->split_steps = p->k_tiles;
+    if (I.kernel != 0 || I.M == 0 || I.N == 0 || I.K == 0 || elem_of(I.dtype) != tg::kBf16 || is_mx(I.dtype) ||
+        is_int(I.dtype) || (I.layout != GEMM_LAYOUT_BT && I.layout != GEMM_LAYOUT_BT_PRESHUFFLED) ||
+        I.N * 4 * 256 >= (int64_t(1) << 31))
+        return;
+    const int64_t tm = (I.M + 255) / 256, tn = (I.N + 255) / 256;
+    const int64_t tiles = tm * tn;
+    int s = 1;
+    const char *e = getenv("TGEMM_SPLIT");
+    if (e) {
+        s = atoi(e);
+    } else {
+        while (tiles * s * 2 <= 256 && p->k_tiles / (s * 2) >= 8)
+            s *= 2;
+    }
+    if (s < 2 || s > 64)
+        return;
+    const int per = (p->k_tiles + s - 1) / s;
+    if ((int64_t)(s - 1) * per >= p->k_tiles)           // every slice non-empty
+        return;
+    gemm_plan_info J = I;
+    J.dtype = GEMM_BF16_OUT_F32;
+    const tg::TiledVariant *v = pick_tiled(J, true);
+    // Only the pipelined and the LDS-staged kernels read the split fields.
+    int np = 0, nd = 0;
+    const tg::TiledVariant *pv = tg::pipe_variants(&np), *dv = tg::dma_variants(&nd);
+    const bool splittable = v && ((v >= pv && v < pv + np) || (v >= dv && v < dv + nd));
+    if (!splittable || v->bm != 256 || v->bn != 256 || v->lds_bytes > kLdsLimit)
+        return;
+    p->split_v = v;
+    p->splits = s;
+    p->split_steps = per;
+    p->split_tiles_m = (int32_t)tm;
+    p->split_tiles_n = (int32_t)tn;
+    p->split_group_m = (int32_t)(tm < 4 ? tm : 4);
+    p->split_grid = (int32_t)(tiles * s);
 }
 
 Layout make(std::initializer_list<int64_t> shape, std::initializer_list<int64_t> stride)
@@ -430,6 +486,9 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "tile needs %d bytes of LDS (> 160 KiB)", I.lds_bytes);
         return nullptr;
     }
+    plan_split(p);
+    I.ws_splits = p->splits;
+    I.ws_grid = p->splits > 1 ? p->split_grid : I.grid;
     ok();
     return p;
 }
@@ -641,6 +700,58 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+size_t workspace_bytes(const gemm_plan *plan)
+{
+    if (!plan || plan->splits < 2)
+        return 0;
+    return (size_t)plan->splits * (size_t)plan->info.M * (size_t)plan->info.N * 4u;
+}
+
+// Split-K run: the slices' fp32 partials into W, then the ordered sum and
+// the epilogue into C.  The caller has validated A, B, C and W.
+int run_split(const gemm_plan *plan, const void *A, const void *B, void *C, void *W, const tg::EpiArgs &epi,
+              hipStream_t stream)
+{
+    const gemm_plan_info &I = plan->info;
+    tg::TiledArgs a{};
+    a.A = A;
+    a.B = B;
+    a.C = W;
+    a.epi = tg::EpiArgs{};                 // partials: no scaling, no bias, no activation
+    a.epi.act = tg::kActNone;
+    a.M = (int32_t)I.M;
+    a.N = (int32_t)I.N;
+    a.kbytes = (int32_t)plan->kbytes;
+    a.kbytes_b = (int32_t)plan->kbytes_b;
+    a.K = (int32_t)I.K;
+    a.ldb_bytes = (int32_t)(I.N * I.elem_bytes);
+    a.lda_bytes = (int32_t)(I.M * I.elem_bytes);
+    a.k_tiles = plan->k_tiles;
+    a.tail_bytes = plan->tail_bytes;
+    a.grid = plan->split_grid;
+    a.tiles_m = plan->split_tiles_m;
+    a.tiles_n = plan->split_tiles_n;
+    a.group_m = plan->split_group_m;
+    a.splits = plan->splits;
+    a.split_steps = plan->split_steps;
+    hipError_t e = plan->split_v->launch(a, stream);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "split-K launch: %s", hipGetErrorString(e));
+    tg::SplitReduceArgs r{};
+    r.W = (const float *)W;
+    r.C = C;
+    r.epi = epi;
+    r.M = (int32_t)I.M;
+    r.N = (int32_t)I.N;
+    r.splits = plan->splits;
+    r.out = out_of(I.dtype);
+    e = tg::launch_split_reduce(r, stream);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "split-K reduction launch: %s", hipGetErrorString(e));
+    ok();
+    return GEMM_OK;
+}
+
 // The epilogue description -> kernel arguments (GEMM_OK or an error).
 int epi_from(const gemm_epilogue_args *epi, tg::EpiArgs *e)
 {
@@ -706,6 +817,36 @@ int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C, co
     if (int rc = epi_from(epi, &e))
         return rc;
     return run_impl(plan, A, B, C, e, stream);
+}
+
+size_t gemm_workspace_bytes(const gemm_plan *plan) { return workspace_bytes(plan); }
+
+int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *C, const gemm_epilogue_args *epi,
+                void *workspace, size_t workspace_bytes_given, hipStream_t stream)
+{
+    if (int rc = reject_mx(plan))
+        return rc;
+    tg::EpiArgs e;
+    if (int rc = epi_from(epi, &e))
+        return rc;
+    const size_t need = workspace_bytes(plan);
+    if (need == 0 || !workspace || workspace_bytes_given < need)
+        return run_impl(plan, A, B, C, e, stream);
+    const gemm_plan_info &I = plan->info;
+    if (!A || !B || !C)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL A, B or C");
+    if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(workspace))
+        return fail(GEMM_ERR_INVALID_ARG, "A, B, C and the workspace must be 16-byte aligned");
+    const size_t cbytes = (size_t)I.M * I.N * I.out_bytes;
+    const size_t abytes = (size_t)I.M * plan->kbytes, bbytes = (size_t)I.N * plan->kbytes_b;
+    if (overlap(C, cbytes, A, abytes) || overlap(C, cbytes, B, bbytes))
+        return fail(GEMM_ERR_INVALID_ARG, "C overlaps A or B");
+    if (overlap(workspace, need, A, abytes) || overlap(workspace, need, B, bbytes) ||
+        overlap(workspace, need, C, cbytes))
+        return fail(GEMM_ERR_INVALID_ARG, "the workspace overlaps A, B or C");
+    if (int rc = check_device())
+        return rc;
+    return run_split(plan, A, B, C, workspace, e, stream);
 }
 
 size_t gemm_bscale_image_bytes(const gemm_plan *plan, int operand)

@@ -394,6 +394,32 @@ __device__ inline int bkn8_swz(int k) { return k & 7; }
 
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Split K (TiledArgs::splits): this workgroup's place in the tile raster,
+// its K steps [kt0, kt0 + nk) with the valid bytes of the last one, and its
+// output (C, or its fp32 partial in the workspace).
+struct SplitK {
+    int wg, grid;
+    int kt0, nk;
+    uint32_t tail;
+    void *C;
+};
+__device__ inline SplitK split_k_of(const TiledArgs &p)
+{
+    SplitK s{(int)blockIdx.x, p.grid, 0, p.k_tiles, (uint32_t)p.tail_bytes, p.C};
+    if (p.splits > 1) {
+        const int tiles = p.grid / p.splits;
+        const int sp = (int)blockIdx.x / tiles;
+        s.wg = (int)blockIdx.x - sp * tiles;
+        s.grid = tiles;
+        s.kt0 = sp * p.split_steps;
+        s.nk = min(p.split_steps, p.k_tiles - s.kt0);
+        if (s.kt0 + s.nk < p.k_tiles)
+            s.tail = kTileKBytes;
+        s.C = (uint8_t *)p.C + (size_t)sp * (size_t)p.M * (size_t)p.N * 4u;
+    }
+    return s;
+}
+
 // f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled,
 // so that register arrays indexed by the constant stay in registers.
 template <typename F, int... I>

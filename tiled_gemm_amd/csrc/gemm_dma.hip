@@ -88,27 +88,32 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     const int q = l >> 4, r16 = l & 15;
     const int wm = w / WGN, wn = w % WGN;
 
+    const SplitK sk = split_k_of(p);
     int tm, tn;
-    tile_of_wg(blockIdx.x, p.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    tile_of_wg(sk.wg, sk.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m0 = tm * DM_BM, n0 = tn * DM_BN;
     const int rows_a = min(p.M - m0, DM_BM);
     const int rows_b = min(p.N - n0, DM_BN);
     const uint32_t kb = (uint32_t)p.kbytes;
     const uint32_t kbB = (uint32_t)p.kbytes_b;
     const uint32_t lda = (uint32_t)p.lda_bytes;
-    const auto rA = AKM ? make_rsrc((const uint8_t *)p.A + (size_t)m0 * 2,
-                                    (uint32_t)((size_t)p.K * lda - (size_t)m0 * 2))
-                        : make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
+    // A split starts its operands' resources at its first K step (kAStep /
+    // kBStep bytes per step, below), so every step index is split-relative.
+    const uint32_t shA = (uint32_t)sk.kt0 * (AKM ? 64u * lda : (uint32_t)kTileKBytes);
+    const auto rA = AKM ? make_rsrc((const uint8_t *)p.A + (size_t)m0 * 2 + shA,
+                                    (uint32_t)((size_t)p.K * lda - (size_t)m0 * 2 - shA))
+                        : make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb + shA, (uint32_t)rows_a * kb - shA);
     // K x N B: the resource starts at column n0 and ends with the matrix, so
     // K-rows past K read zeros; columns past N read neighbouring data or
     // zeros and only feed columns of C that are never stored.
     const uint32_t ldb = (uint32_t)p.ldb_bytes;
     constexpr int EB = F8 ? 1 : 2;                       // bytes per element
-    const auto rB = BKN ? make_rsrc((const uint8_t *)p.B + (size_t)n0 * EB,
-                                    (uint32_t)((size_t)p.K * ldb - (size_t)n0 * EB))
-                        : make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
-    const int nk = p.k_tiles;
-    const uint32_t tail = (uint32_t)p.tail_bytes;
+    const uint32_t shB = (uint32_t)sk.kt0 * (BKN ? (uint32_t)KN_ROWS * ldb : (BPRE ? 2048u : (uint32_t)kTileKBytes));
+    const auto rB = BKN ? make_rsrc((const uint8_t *)p.B + (size_t)n0 * EB + shB,
+                                    (uint32_t)((size_t)p.K * ldb - (size_t)n0 * EB - shB))
+                        : make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB + shB, (uint32_t)rows_b * kbB - shB);
+    const int nk = sk.nk;
+    const uint32_t tail = sk.tail;
 
     // ---- load sources.  Load r of a step lands at byte (r * WAVES + w) *
     // 1024 + 16 l of its operand's half of the stage.  Row-major operands:
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     const EpiView ev = epi_view(p.epi, p.M, p.N);
     constexpr int OB = OUT == kOutF32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)p.N * OB;
-    const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+    const auto rC = make_rsrc((uint8_t *)sk.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
     f32x4 sbv[FN], bzv[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {

@@ -104,17 +104,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     const int q = l >> 4, r16 = l & 15;
     const int wm = w / WGN, wn = w % WGN;
 
+    const SplitK sk = split_k_of(p);
     int tm, tn;
-    tile_of_wg(blockIdx.x, p.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    tile_of_wg(sk.wg, sk.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m0 = tm * BP_BM, n0 = tn * BP_BN;
     const int rows_a = min(p.M - m0, BP_BM);
     const int rows_b = min(p.N - n0, BP_BN);
     const uint32_t kb = (uint32_t)p.kbytes;
     const uint32_t kbB = (uint32_t)p.kbytes_b;
-    const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
-    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
-    const int nk = p.k_tiles;
-    const uint32_t tail = (uint32_t)p.tail_bytes;
+    // A split starts its operands' resources at its first K step (bytes of
+    // that step: A 128 per row; B as kBStep below), so every step index below
+    // is split-relative.  Only bf16 and fp8 plans split K: the MX scale
+    // images are indexed by the absolute step.
+    const uint32_t shA = (uint32_t)sk.kt0 * (uint32_t)kTileKBytes;
+    const uint32_t shB =
+        (uint32_t)sk.kt0 * (W4 ? (BPRE ? 1024u : 64u) : (BPRE ? 2048u : (uint32_t)kTileKBytes));
+    const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb + shA, (uint32_t)rows_a * kb - shA);
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB + shB, (uint32_t)rows_b * kbB - shB);
+    const int nk = sk.nk;
+    const uint32_t tail = sk.tail;
 
     // ---- A: global -> LDS source offsets, as in the generic kernel.
     uint32_t voffA[BP_AR];
@@ -453,7 +461,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     const EpiView ev = epi_view(p.epi, p.M, p.N);
     constexpr int OB = OUT == kOutF32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)p.N * OB;
-    const auto rC = make_rsrc((uint8_t *)p.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+    const auto rC = make_rsrc((uint8_t *)sk.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
     f32x4 sbv[BP_FN], bzv[BP_FN];
 #pragma unroll
     for (int j = 0; j < BP_FN; ++j) {

@@ -44,6 +44,24 @@ struct TiledArgs {
     int32_t K;              // elements along K
     int32_t ldb_bytes;      // B stored K x N: bytes of one row of B (N * elem_bytes)
     int32_t lda_bytes;      // A stored K x M: bytes of one row of A (M * elem_bytes)
+    // Split K: with splits > 1 the launch has grid = tiles * splits
+    // workgroups; workgroup g takes tile g % tiles and the split_steps K steps
+    // starting at step (g / tiles) * split_steps (the last split: the rest),
+    // and writes its fp32 partial tile to C + (g / tiles) * M * N * 4 bytes
+    // with the identity epilogue.  splits == 1: the whole K, C as given.
+    int32_t splits;
+    int32_t split_steps;
+};
+
+// Sum of the split-K partials and the epilogue: C[m][n] = cvt(epi(sum over
+// s in order of W[s][m][n])), W holding `splits` fp32 M x N matrices.
+struct SplitReduceArgs {
+    const float *W;
+    void *C;
+    EpiArgs epi;
+    int32_t M, N;
+    int32_t splits;
+    int32_t out;            // kOutF32 or kOutBf16
 };
 
 // Block-scale image of an MX operand with R rows: the bytes
@@ -109,6 +127,7 @@ constexpr int kSkinnyTileN = 32;
 constexpr int kTiledThreads = 256;
 
 const TiledVariant *tiled_variants(int *count);
+hipError_t launch_split_reduce(const SplitReduceArgs &a, hipStream_t s);
 const TiledVariant *pipe_variants(int *count);
 const TiledVariant *dma_variants(int *count);
 const SkinnyVariant *skinny_variants(int *count);

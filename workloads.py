@@ -103,6 +103,13 @@ WORKLOADS = {
                                                      "bf16", "bf16", "bt_preshuffled", ("normal", 0.0, 1.0),
                                                      ("normal", 0.0, 0.02), 1014,
                                                      "decode-like with a pre-shuffled weight, HBM-bound"),
+    "bf16_256x8192x8192_preshuffled": Workload("bf16_256x8192x8192_preshuffled", 256, 8192, 8192, "bf16",
+                                               "bf16", "bt_preshuffled", ("normal", 0.0, 1.0),
+                                               ("normal", 0.0, 0.02), 1015,
+                                               "batched decode / small prefill, pre-shuffled weight"),
+    "bf16_1024x8192x8192": Workload("bf16_1024x8192x8192", 1024, 8192, 8192, "bf16", "bf16", "bt",
+                                    ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), 1016,
+                                    "prefill chunk: 128 output tiles"),
     "e4m3_8192": Workload("e4m3_8192", 8192, 8192, 8192, "e4m3", "bf16", "bt",
                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1005,
                           "per-tensor scales amax/448"),
