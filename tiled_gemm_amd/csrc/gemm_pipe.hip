@@ -138,12 +138,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     u32x4 stA[BP_AR];                           // staging (ADMA == false)
     int stA_tile = 0;
     // One A load (round r of tile kt), for the spread schedule below.
-    auto issue_a_one = [&](int kt, int r) {
-        const bool beyond = kt >= nk;
-        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
-        const bool keep = !beyond & (!part | (((tailA >> r) & 1u) != 0));
-        buf_load16_to_lds(rA, lds + (kt % NS) * BP_STAGE + (r * WAVES + w) * 1024, keep_or_oob(keep, voffA[r]),
-                          (uint32_t)kt * kTileKBytes);
+    // MASK false: the caller guarantees tile kt is whole and in range, so
+    // the offsets need no per-lane selection.
+    auto issue_a_one = [&](int kt, int r, auto mask_c) {
+        uint32_t vo = voffA[r];
+        if constexpr (decltype(mask_c)::value) {
+            const bool beyond = kt >= nk;
+            const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+            const bool keep = !beyond & (!part | (((tailA >> r) & 1u) != 0));
+            vo = keep_or_oob(keep, vo);
+        }
+        buf_load16_to_lds(rA, lds + (kt % NS) * BP_STAGE + (r * WAVES + w) * 1024, vo, (uint32_t)kt * kTileKBytes);
         issue_fence();
     };
     auto issue_a = [&](int kt) {
@@ -186,12 +191,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     // A half-filled last step (K bytes 0..63 valid): half 1 is the missing part.
     auto b_keep = [&](bool beyond, bool part, int h) { return !beyond & ((h == 0) | !part); };
     u32x4 bq[2][BP_FN][BH];
-    auto issue_b_one = [&](int kt, auto set_c, int j, int h) {
+    auto issue_b_one = [&](int kt, auto set_c, int j, int h, auto mask_c) {
         constexpr int S = decltype(set_c)::value;
-        const bool beyond = kt >= nk;
-        const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
-        bq[S][j][h] = buf_load16(rB, keep_or_oob(b_keep(beyond, part, h), voffB[j] + (uint32_t)h * kBHalf),
-                                 (uint32_t)kt * kBStep);
+        uint32_t vo = voffB[j] + (uint32_t)h * kBHalf;
+        if constexpr (decltype(mask_c)::value) {
+            const bool beyond = kt >= nk;
+            const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+            vo = keep_or_oob(b_keep(beyond, part, h), vo);
+        }
+        bq[S][j][h] = buf_load16(rB, vo, (uint32_t)kt * kBStep);
         issue_fence();
     };
     auto issue_b = [&](int kt, auto set_c) {
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
 
     // One step.  Set CUR holds B(kt); set 1-CUR receives B(kt+1).  GP: the
     // step's position in its scale group (MX).
-    auto step = [&](int kt, auto cur_c, auto gp_c) {
+    auto step = [&](int kt, auto cur_c, auto gp_c, auto mask_c) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int GP = decltype(gp_c)::value;
         constexpr int kVmBar = kVmBarrier0 + SL * scale_starts(GP);
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                 if (g < NG - PD) {
 #pragma unroll
                     for (int b = g * BP_BR / (NG - PD); b < (g + 1) * BP_BR / (NG - PD); ++b)
-                        issue_b_one(kt + 1, ic<1 - CUR>{}, b / BH, b % BH);
+                        issue_b_one(kt + 1, ic<1 - CUR>{}, b / BH, b % BH, mask_c);
                 } else {
                     const int go = g - (NG - PD);
                     if (go == 0) {
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
                     }
 #pragma unroll
                     for (int r = go * BP_AR / PD; r < (go + 1) * BP_AR / PD; ++r)
-                        issue_a_one(kt + NS - 1, r);
+                        issue_a_one(kt + NS - 1, r, mask_c);
                 }
             } else if (g == NG - PD) {
                 if constexpr (ADMA) {
@@ -437,17 +445,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     // Steps run in pairs (MX e4m3: in fours, one scale group); steps past nk
     // are phantom steps whose operands are all out of range, i.e. zeros, and
     // add exact zeros.
+    // With the spread schedule, a pair of steps whose loads (B up to kt + 2,
+    // A up to kt + NS) all cover whole, in-range tiles runs without per-lane
+    // masks; the remaining pairs run the masked copy.
+    using masked = std::true_type;
+    using unmasked = std::false_type;
     if constexpr (ELEM == kMx8) {
         for (int kt = 0; kt < nk; kt += 4) {
-            step(kt, ic<0>{}, ic<0>{});
-            step(kt + 1, ic<1>{}, ic<1>{});
-            step(kt + 2, ic<0>{}, ic<2>{});
-            step(kt + 3, ic<1>{}, ic<3>{});
+            step(kt, ic<0>{}, ic<0>{}, masked{});
+            step(kt + 1, ic<1>{}, ic<1>{}, masked{});
+            step(kt + 2, ic<0>{}, ic<2>{}, masked{});
+            step(kt + 3, ic<1>{}, ic<3>{}, masked{});
         }
     } else {
-        for (int kt = 0; kt < nk; kt += 2) {
-            step(kt, ic<0>{}, ic<0>{});
-            step(kt + 1, ic<1>{}, ic<1>{});
+        int kt = 0;
+        if constexpr (SPREAD && ADMA) {
+            const int nfull = tail == (uint32_t)kTileKBytes ? nk : nk - 1;   // whole steps
+            for (; kt + NS < nfull; kt += 2) {
+                step(kt, ic<0>{}, ic<0>{}, unmasked{});
+                step(kt + 1, ic<1>{}, ic<1>{}, unmasked{});
+            }
+        }
+        for (; kt < nk; kt += 2) {
+            step(kt, ic<0>{}, ic<0>{}, masked{});
+            step(kt + 1, ic<1>{}, ic<1>{}, masked{});
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
