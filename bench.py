@@ -202,14 +202,14 @@ def main():
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
         "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
         "bf16_skinny_32x8192x8192_preshuffled", "bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192",
-        "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "i8_8192", "w4a8_8192"])
+        "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
     results = {}
     inputs = {}
     for name in names:
         w = W.WORKLOADS[name]
         log("bench: generating", name)
         inp = W.make_inputs(w)
-        rotate = 3 if name.startswith("bf16_skinny_32x8192x8192") else 1
+        rotate = 3 if name.startswith("bf16_skinny_32x8192x8192") or name == "w4a8_32x8192x8192" else 1
         steps = args.steps if name == (args.only or HEADLINE) else max(10, args.steps // 2)
         split = name in SPLIT_K_WORKLOADS
         if split:
@@ -240,7 +240,10 @@ def main():
     head = args.only or HEADLINE
     w = W.WORKLOADS[head]
     r = results[head]
-    bound = "hbm" if head.startswith("bf16_skinny_32x8192x8192") else "mfma"
+    # the roofline that bounds the workload: HBM below the ridge point
+    # (peak flops / peak HBM bytes per second), MFMA above it
+    ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if w.flops / w.min_bytes < ridge else "mfma"
     traffic = None
     if head == HEADLINE:
         from profile_summary import read_traffic

@@ -175,6 +175,12 @@ def test_plan_choices(lib, monkeypatch):
         assert c["tile_m"] >= M
     c = info(65, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
     assert c["kernel"] == 0
+    # integer decode shapes: int8 with either B layout, W4A8 with B pre-shuffled
+    assert info(32, 8192, 8192, tg.GEMM_I8_OUT_BF16, tg.GEMM_LAYOUT_BT)["kernel"] == 1
+    assert info(32, 8192, 8192, tg.GEMM_I8_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 1
+    assert info(32, 8192, 8192, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 1
+    assert info(32, 8192, 8192, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT)["kernel"] == 0
+    assert info(32, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 0
     c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
     assert c["lds_stages"] == 4                      # fp8: B in registers
@@ -274,7 +280,11 @@ def test_int_plans(lib, monkeypatch, dtype, b_bits, layout):
     for M, N, K in [(8192, 8192, 8192), (32, 4096, 1024), (300, 272, 1152), (1, 16, 128)]:
         with tg.Plan(M, N, K, dtype, layout) as p:
             info = p.info()
-            assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 512   # 8-wave pipelined
+            skinny = M <= 64 and (b_bits == 8 or layout == tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+            if skinny:                       # decode shapes: the skinny kernels
+                assert info["kernel"] == 1 and info["tile_n"] == 32 and info["tile_m"] >= M
+            else:
+                assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 512   # 8-wave pipelined
             assert info["elem_bits"] == 8 and info["elem_bytes"] == 1 and info["b_elem_bits"] == b_bits
             assert info["out_bytes"] == 2
             assert tg.gemm_preshuffled_b_bytes(p.handle) == N * K * b_bits // 8

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import tiled_gemm_amd as tg
 import workloads as W
 from gpu_util import assert_epilogue_within_bound, decode, run_gemm, sample_entries
 
@@ -90,6 +91,66 @@ def test_int_with_epilogue_bit_exact(oracle_mod, monkeypatch, fmt, waves):
     _bits_equal(bits, oracle_mod.round_bf16(want), want)
 
 
+# Decode shapes (M <= 64) run on the skinny kernels: int8 with B N x K or
+# pre-shuffled, W4A8 with B pre-shuffled.
+SKINNY = [("i8", "bt"), ("i8", "bt_preshuffled"), ("w4a8", "bt_preshuffled")]
+
+
+@pytest.mark.parametrize("fmt,layout", SKINNY)
+@pytest.mark.parametrize("M", [1, 17, 32, 33, 64])
+@pytest.mark.parametrize("N", [544, 528])
+def test_int_skinny_bit_exact(oracle_mod, fmt, layout, M, N):
+    K = _k_for(fmt, True)
+    say("case int skinny exact", fmt, layout, M, N, K)
+    inp = W.int_inputs(M, N, K, fmt, seed=M + N, lo=-128, hi=127)
+    bits, info = run_gemm(inp.A, inp.B, M, N, K, fmt, "bf16", layout, return_plan_info=True)
+    assert info["kernel"] == 1
+    acc, S = oracle_mod.gemm_bt_int(inp.A, inp.B, K, fmt)
+    assert S.max() < 2.0 ** 24
+    _bits_equal(bits, oracle_mod.round_bf16(acc), acc)
+
+
+@pytest.mark.parametrize("fmt,layout", SKINNY)
+def test_int_skinny_large_sums_exact_in_int32(oracle_mod, fmt, layout):
+    # every product at its extreme over K = 8192: the waves' partial sums are
+    # combined in int32, so the one rounding is the final one
+    M, N, K = 32, 544, 8192
+    say("case int skinny extremes", fmt, layout)
+    A = np.full((M, K), 0x80, np.uint8)
+    B = np.full((N, K), 0x80, np.uint8) if fmt == "i8" else np.full((N, K // 2), 0x88, np.uint8)
+    bits = run_gemm(A, B, M, N, K, fmt, "bf16", layout)
+    acc, _ = oracle_mod.gemm_bt_int_entries(A, B, K, [0], [0], fmt)
+    assert acc[0] == (2.0 ** 27 if fmt == "i8" else 2.0 ** 23)
+    assert np.all(bits == oracle_mod.round_bf16(acc)[0])
+
+
+@pytest.mark.parametrize("fmt,layout", SKINNY)
+@pytest.mark.parametrize("kind", ["none", "bias_gelu"])
+def test_int_skinny_quantised_within_bound(oracle_mod, fmt, layout, kind):
+    M, N, K = 32, 784, 1536
+    say("case int skinny quantised", fmt, layout, kind)
+    inp = W.make_inputs(W.WORKLOADS[fmt + "_8192"], M=M, N=N, K=K, seed=41)
+    rng = np.random.default_rng(42)
+    e = dict(scale_a=inp.sa_rows.astype(np.float64), scale_b=inp.sb_cols.astype(np.float64), kind=kind)
+    if kind != "none":
+        e["bias"] = rng.normal(0.0, 1.0, N)
+    bits, info = run_gemm(inp.A, inp.B, M, N, K, fmt, "bf16", layout, epi=e, return_plan_info=True)
+    assert info["kernel"] == 1
+    acc, S = oracle_mod.gemm_bt_int(inp.A, inp.B, K, fmt)
+    want = oracle_mod.epilogue(acc, e["scale_a"], e["scale_b"], e.get("bias"), kind)
+    scale = np.abs(e["scale_a"][:, None] * e["scale_b"][None, :])
+    bias_abs = np.abs(e["bias"])[None, :] if "bias" in e else 0.0
+    r = assert_epilogue_within_bound(decode(bits), want, S * scale, np.abs(acc) * scale, bias_abs, fmt, kind,
+                                     "skinny %s %s" % (fmt, kind))
+    say("  worst err/bound", r)
+
+
+def test_w4a8_plain_decode_stays_tiled():
+    # W4A8 with B N x K (packed rows) has no skinny kernel
+    with tg.Plan(32, 8192, 8192, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert p.info()["kernel"] == 0
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_int_extremes(oracle_mod, fmt):
     # every product at its largest magnitude: -128 * -128 = 2^14 (int8) or
@@ -141,7 +202,7 @@ def test_int_quantised_within_bound(oracle_mod, monkeypatch, fmt, kind, waves):
     say("  worst err/bound", r)
 
 
-@pytest.mark.parametrize("name", ["i8_8192", "w4a8_8192"])
+@pytest.mark.parametrize("name", ["i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
 def test_int_full_size_sampled(oracle_mod, monkeypatch, name):
     set_waves(monkeypatch, None)
     w = W.WORKLOADS[name]

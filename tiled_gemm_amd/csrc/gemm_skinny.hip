@@ -32,7 +32,10 @@ constexpr int kRedPitch = kSkinnyTileN + 1;   // padded reduction row (bank spre
 // Sums the waves' partial 16 x 16 tiles through LDS in a fixed wave order
 // (deterministic), then applies the epilogue and stores C.  The caller has
 // drained every load that writes LDS and synchronised the workgroup.
-template <int MB, int OUT, int WAVES>
+// IUNIT = 0: fp32 accumulators.  Otherwise the accumulators hold int32 sums
+// (integer MFMAs): the waves' partials are summed in int32 (exact), then
+// converted to fp32 and multiplied by 1 / IUNIT (a power of two, exact).
+template <int MB, int OUT, int WAVES, int IUNIT = 0>
 __device__ inline void skinny_finish(const SkinnyArgs &p, const f32x4 (&acc)[MB][kSkinnyTileN / 16], uint8_t *lds,
                                      int n0)
 {
@@ -60,10 +63,21 @@ __device__ inline void skinny_finish(const SkinnyArgs &p, const f32x4 (&acc)[MB]
     for (int o = threadIdx.x * 2; o < ROWS_A * kSkinnyTileN; o += 64 * WAVES * 2) {
         const int row = o / kSkinnyTileN, col = o % kSkinnyTileN;
         float s0 = 0.f, s1 = 0.f;
+        if constexpr (IUNIT != 0) {
+            int32_t i0 = 0, i1 = 0;
 #pragma unroll
-        for (int ww = 0; ww < WAVES; ++ww) {
-            s0 += red[ww][row][col];
-            s1 += red[ww][row][col + 1];
+            for (int ww = 0; ww < WAVES; ++ww) {
+                i0 += __builtin_bit_cast(int32_t, red[ww][row][col]);
+                i1 += __builtin_bit_cast(int32_t, red[ww][row][col + 1]);
+            }
+            s0 = (float)i0 * (1.f / IUNIT);
+            s1 = (float)i1 * (1.f / IUNIT);
+        } else {
+#pragma unroll
+            for (int ww = 0; ww < WAVES; ++ww) {
+                s0 += red[ww][row][col];
+                s1 += red[ww][row][col + 1];
+            }
         }
         const int n = n0 + col;
         float sb[2], bz[2];
@@ -183,6 +197,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_kernel(const Skinny
                 if constexpr (ELEM == kBf16) {
                     acc[i][j] = mfma_bf16(b[j][0], a[i][0], acc[i][j]);
                     acc[i][j] = mfma_bf16(b[j][1], a[i][1], acc[i][j]);
+                } else if constexpr (ELEM == kI8) {
+                    acc[i][j] = mfma_i8(b[j][0], a[i][0], acc[i][j]);
+                    acc[i][j] = mfma_i8(b[j][1], a[i][1], acc[i][j]);
                 } else {
                     acc[i][j] = mfma_fp8x8(join32(b[j][0], b[j][1]), join32(a[i][0], a[i][1]), acc[i][j]);
                 }
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_kernel(const Skinny
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);
     __syncthreads();
 
-    skinny_finish<MB, OUT, WAVES>(p, acc, lds, n0);
+    skinny_finish<MB, OUT, WAVES, ELEM == kI8 ? 1 : 0>(p, acc, lds, n0);
 }
 
 template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool ROTATE>
@@ -230,11 +247,11 @@ static hipError_t launch_skinny(const SkinnyArgs &a, int grid, hipStream_t s)
 // in the MFMA order like the tiled kernels' A.  The step, the K split over
 // the waves, the rotation and the reduction are those of the kernel above.
 // ---------------------------------------------------------------------------
-template <int MB, int WAVES, int DEPTH, bool BLDS>
+template <int MB, int WAVES, int DEPTH, bool BLDS, int BH = 2>
 struct SkinnyPreCfg {
     static constexpr int ROWS_A = MB * 16;
     static constexpr int ASTAGE = ROWS_A * kTileKBytes;     // A bytes per stage
-    static constexpr int BL = 2 * (kSkinnyTileN / 16);      // 1 KiB B loads per stage
+    static constexpr int BL = BH * (kSkinnyTileN / 16);     // 1 KiB B loads per stage
     static constexpr int STAGE = ASTAGE + (BLDS ? BL * 1024 : 0);
     static constexpr int RING = DEPTH * STAGE;              // bytes per wave
     static constexpr int AL = ROWS_A / 8;                   // 1 KiB A loads per stage
@@ -248,7 +265,16 @@ struct SkinnyPreCfg {
 template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool BLDS, int ORD>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const SkinnyArgs p)
 {
-    using Cfg = SkinnyPreCfg<MB, WAVES, DEPTH, BLDS>;
+    // Packed int4 B (W4A8): one 1 KiB block per 16 columns and step, i.e. the
+    // 64 B-bytes of 128 K values per row; lane group q holds values 32 q ..
+    // 32 q + 31, unpacked into two int8 operands, half h pairing with A
+    // chunk 2 q + h.  Otherwise two blocks (K bytes 0..63 and 64..127 of the
+    // step) pairing with A chunks q and 4 + q.
+    constexpr bool W4 = ELEM == kW4A8;
+    constexpr bool INT = ELEM == kI8 || W4;
+    constexpr int BH = W4 ? 1 : 2;
+    static_assert(!INT || OUT == kOutBf16, "integer GEMMs write bf16");
+    using Cfg = SkinnyPreCfg<MB, WAVES, DEPTH, BLDS, BH>;
     constexpr int NB = kSkinnyTileN / 16;
     constexpr int AL = Cfg::AL;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
@@ -259,10 +285,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
     const int n0 = blockIdx.x * kSkinnyTileN;
     const uint32_t kb = (uint32_t)p.kbytes;
     const int rows_b = min(p.N - n0, kSkinnyTileN);
+    const uint32_t kbB = (uint32_t)p.kbytes_b;
     const auto rA = make_rsrc(p.A, (uint32_t)p.M * kb);
-    // The workgroup's 16-column blocks are contiguous in the image (16 * kb
+    // The workgroup's 16-column blocks are contiguous in the image (16 * kbB
     // bytes each); a block past N lies past the record count (zeros).
-    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kb, (uint32_t)rows_b * kb);
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
     const int nk = p.k_tiles;
     const uint32_t tail = (uint32_t)p.tail_bytes;
     uint8_t *const ring = lds + w * Cfg::RING;
@@ -286,8 +313,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
     const int nt = INTER ? (w < nk ? (nk - w + WAVES - 1) / WAVES : 0) : max(0, min(per, nk - first));
     const int rot = (ORD == 0 || ORD == 2) ? (int)((blockIdx.x * 37u) % (uint32_t)max(nk, 1)) : 0;
 
-    // B of one step: 64-byte K blocks 2 kt + h of 16-column block j.
-    u32x4 bq[DEPTH][NB][2];
+    // B of one step: image blocks BH kt + h of 16-column block j.
+    u32x4 bq[DEPTH][NB][BH];
 
     // Step t of this wave into stage s.  Every load is issued; those past the
     // run, or past K in a half-filled last step, are out of range (zeros).
@@ -304,15 +331,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
             const bool keep = in & (!part | (((half_keep >> j) & 1u) != 0));
             buf_load16_to_lds(rA, dst + j * 1024, keep_or_oob(keep, voffA[j]), soffA);
         }
-        const uint32_t soffB = in ? (uint32_t)kt * 2048u : 0u;
+        const uint32_t soffB = in ? (uint32_t)kt * (uint32_t)(BH * 1024) : 0u;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < BH; ++h) {
                 const bool keep = in & (!part | (h == 0));
-                const uint32_t voffB = keep_or_oob(keep, (uint32_t)j * 16u * kb + (uint32_t)h * 1024u + (uint32_t)l * 16u);
+                const uint32_t voffB =
+                    keep_or_oob(keep, (uint32_t)j * 16u * kbB + (uint32_t)h * 1024u + (uint32_t)l * 16u);
                 if constexpr (BLDS)
-                    buf_load16_to_lds(rB, dst + Cfg::ASTAGE + (2 * j + h) * 1024, voffB, soffB);
+                    buf_load16_to_lds(rB, dst + Cfg::ASTAGE + (BH * j + h) * 1024, voffB, soffB);
                 else
                     bq[S][j][h] = buf_load16(rB, voffB, soffB);
             }
@@ -337,27 +365,40 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 const int row = i * 16 + r16;
-                a[i][h] = lds_load16(st + row * kTileKBytes + swz_chunk(row, h * 4 + q) * kChunkBytes);
+                const int c = W4 ? 2 * q + h : h * 4 + q;
+                a[i][h] = lds_load16(st + row * kTileKBytes + swz_chunk(row, c) * kChunkBytes);
             }
         if constexpr (BLDS) {
             // the staged operand blocks are in lane order already
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    bq[S][j][h] = lds_load16(st + Cfg::ASTAGE + (2 * j + h) * 1024 + l * 16);
+                for (int h = 0; h < BH; ++h)
+                    bq[S][j][h] = lds_load16(st + Cfg::ASTAGE + (BH * j + h) * 1024 + l * 16);
         }
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int j = 0; j < NB; ++j) {
+            u32x4 b0, b1;
+            if constexpr (W4) {
+                b0 = int4x32_half_to_i8(bq[S][j][0], 0);
+                b1 = int4x32_half_to_i8(bq[S][j][0], 1);
+            } else {
+                b0 = bq[S][j][0];
+                b1 = bq[S][j][BH - 1];
+            }
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
+            for (int i = 0; i < MB; ++i) {
                 if constexpr (ELEM == kBf16) {
-                    acc[i][j] = mfma_bf16(bq[S][j][0], a[i][0], acc[i][j]);
-                    acc[i][j] = mfma_bf16(bq[S][j][1], a[i][1], acc[i][j]);
+                    acc[i][j] = mfma_bf16(b0, a[i][0], acc[i][j]);
+                    acc[i][j] = mfma_bf16(b1, a[i][1], acc[i][j]);
+                } else if constexpr (INT) {
+                    acc[i][j] = mfma_i8(b0, a[i][0], acc[i][j]);
+                    acc[i][j] = mfma_i8(b1, a[i][1], acc[i][j]);
                 } else {
-                    acc[i][j] = mfma_fp8x8(join32(bq[S][j][0], bq[S][j][1]), join32(a[i][0], a[i][1]), acc[i][j]);
+                    acc[i][j] = mfma_fp8x8(join32(b0, b1), join32(a[i][0], a[i][1]), acc[i][j]);
                 }
             }
+        }
     };
 
     // Waiting for the oldest stage leaves the DEPTH - 1 younger ones in
@@ -378,7 +419,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);
     __syncthreads();
-    skinny_finish<MB, OUT, WAVES>(p, acc, lds, n0);
+    skinny_finish<MB, OUT, WAVES, ELEM == kI8 ? 1 : (W4 ? 16 : 0)>(p, acc, lds, n0);
 }
 
 template <int MB, int ELEM, int OUT, int WAVES, int DEPTH, bool BLDS, int ORD>
@@ -394,7 +435,7 @@ static hipError_t launch_skinny_pre(const SkinnyArgs &a, int grid, hipStream_t s
                   &launch_skinny<MB, ELEM, OUT, WAVES, DEPTH, ROTATE>}
 
 #define TG_SKINNY_PRE_O(MB, ELEM, OUT, WAVES, DEPTH, BLDS, ORD)                                              \
-    SkinnyVariant{MB, ELEM, OUT, WAVES, DEPTH, SkinnyPreCfg<MB, WAVES, DEPTH, BLDS>::LDS,                    \
+    SkinnyVariant{MB, ELEM, OUT, WAVES, DEPTH, SkinnyPreCfg<MB, WAVES, DEPTH, BLDS, ELEM == kW4A8 ? 1 : 2>::LDS, \
                   &launch_skinny_pre<MB, ELEM, OUT, WAVES, DEPTH, BLDS, ORD>, true}
 #define TG_SKINNY_PRE_L(MB, ELEM, OUT, WAVES, DEPTH, BLDS) TG_SKINNY_PRE_O(MB, ELEM, OUT, WAVES, DEPTH, BLDS, 1)
 #define TG_SKINNY_PRE(MB, ELEM, OUT, WAVES, DEPTH) TG_SKINNY_PRE_L(MB, ELEM, OUT, WAVES, DEPTH, false)
@@ -423,6 +464,13 @@ static const SkinnyVariant kSkinny[] = {
     TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 3), TG_SKINNY_PRE(2, kBf16, kOutBf16, 10, 2),
     // alternative for the 64-row shape
     TG_SKINNY_PRE(4, kBf16, kOutBf16, 4, 4),                                                    // 29
+    // integer operands: int8 with B N x K or pre-shuffled, W4A8 pre-shuffled
+    TG_SKINNY(1, kI8, kOutBf16, 8, 3, true), TG_SKINNY(2, kI8, kOutBf16, 8, 2, true),          // 30
+    TG_SKINNY(4, kI8, kOutBf16, 4, 3, true),
+    TG_SKINNY_PRE(1, kI8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kI8, kOutBf16, 12, 2),             // 33
+    TG_SKINNY_PRE(4, kI8, kOutBf16, 8, 2),
+    TG_SKINNY_PRE(1, kW4A8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kW4A8, kOutBf16, 12, 2),         // 36
+    TG_SKINNY_PRE(4, kW4A8, kOutBf16, 8, 2),
 };
 
 const SkinnyVariant *skinny_variants(int *count)

@@ -90,6 +90,7 @@ struct SkinnyArgs {
     int32_t kbytes;
     int32_t k_tiles;
     int32_t tail_bytes;
+    int32_t kbytes_b;       // bytes of one row of B (kbytes, or kbytes / 2 for int4 B)
 };
 
 struct PreshuffleArgs {
