@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_preshuffled"
 # Workloads with fewer 256 x 256 tiles than CUs: timed through gemm_run_ws
 # (split K with a workspace), plain gemm_run reported beside.
-SPLIT_K_WORKLOADS = ("bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192")
+SPLIT_K_WORKLOADS = ("bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192")
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE scaled by a copy of known size (see the file for the commands).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_pipe_bf16_8192_preshuffled.txt")
@@ -105,7 +105,8 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None, ws=False):
         Wk = torch.empty(max(16, wsb), dtype=torch.uint8, device="cuda")
 
         def launch(A, B, C):
-            plan.run_ws(A.data_ptr(), B.data_ptr(), C.data_ptr(), Wk.data_ptr(), wsb, stream=s)
+            plan.run_ws(A.data_ptr(), B.data_ptr(), C.data_ptr(), Wk.data_ptr(), wsb, stream=s,
+                        scale_a=sp, scale_b=sp + 4 if sp else None)
     elif epi is None:
         def launch(A, B, C):
             plan.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp, s)
@@ -202,7 +203,7 @@ def main():
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
         "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
         "bf16_skinny_32x8192x8192_preshuffled", "bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192",
-        "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
+        "e4m3_1024x8192x8192", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
     results = {}
     inputs = {}
     for name in names:

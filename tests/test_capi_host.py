@@ -412,14 +412,18 @@ def test_split_k_plans(lib, monkeypatch):
     # K bounds the slices: 8 steps (1 KiB of K) each at least
     assert plan(256, 8192, 2048)[0]["ws_splits"] == 4            # 32 steps of 128 bytes
     assert plan(256, 8192, 512)[0]["ws_splits"] == 1
-    # skinny, fp8, MX, integer and K-major layouts never split
+    # skinny, MX, integer and K-major layouts never split
     assert plan(64, 8192, 8192)[0]["ws_splits"] == 1
+    # fp8 splits only where its unsplit plan takes 256 x 256 tiles
     assert plan(256, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)[0]["ws_splits"] == 1
+    assert plan(1024, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)[0]["ws_splits"] == 2
+    assert plan(1024, 8192, 8192, tg.GEMM_E4M3_OUT_BF16)[0]["ws_splits"] == 2
     assert plan(256, 8192, 8192, tg.GEMM_I8_OUT_BF16)[0]["ws_splits"] == 1
     assert plan(256, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)[0]["ws_splits"] == 1
     # a forced count, uneven slices; an impossible one is refused (no split)
     monkeypatch.setenv("TGEMM_SPLIT", "3")
     assert plan(136, 528, 4160)[0]["ws_splits"] == 3
+    assert plan(136, 528, 4160, tg.GEMM_E4M3_OUT_BF16)[0]["ws_splits"] == 3   # forced: fp8 too
     monkeypatch.setenv("TGEMM_SPLIT", "64")
     assert plan(136, 528, 4160)[0]["ws_splits"] == 1                # 65 steps: slices would be empty
     # the generic tiled kernel does not read the split fields: never split on it

@@ -19,7 +19,8 @@ from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, 
 
 pytestmark = pytest.mark.gpu
 
-CODES = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16}
+CODES = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
+         ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16}
 
 
 def say(*a):
@@ -42,9 +43,9 @@ def splits_of(M, N, K, dtype, out, layout):
         return p.info()["ws_splits"]
 
 
-def exact(oracle_mod, inp, M, N, K, dtype, out, layout, **kw):
-    bits = run_gemm(inp.A, inp.B, M, N, K, dtype, out, layout, **kw)
-    C_ref, _ = oracle_mod.gemm_bt(inp.A, inp.B, dtype=dtype, want_s=False)
+def exact(oracle_mod, inp, M, N, K, dtype, out, layout, scale=(1.0, 1.0), **kw):
+    bits = run_gemm(inp.A, inp.B, M, N, K, dtype, out, layout, scale=scale, **kw)
+    C_ref, _ = oracle_mod.gemm_bt(inp.A, inp.B, dtype=dtype, sigma=oracle_mod.sigma_of(*scale), want_s=False)
     want = C_ref.astype(np.float32).view(np.uint32) if out == "f32" else oracle_mod.round_bf16(C_ref)
     bad = np.argwhere(bits != want)
     assert bad.size == 0, "%d mismatches, first %s: got %s want %s" % (
@@ -64,6 +65,32 @@ def test_split_integer_exact(oracle_mod, layout, out, M):
     assert s > 1
     inp = W.int_inputs(M, N, K, "bf16", seed=M + 5)
     exact(oracle_mod, inp, M, N, K, "bf16", out, layout, workspace=True)
+
+
+@pytest.mark.parametrize("layout", ["bt", "bt_preshuffled"])
+@pytest.mark.parametrize("M", [65, 300])
+def test_split_fp8_exact(oracle_mod, monkeypatch, layout, M):
+    # e4m3 integers in [-4, 4], per-tensor scales 0.5 and 0.25 (applied by the
+    # reduction); K = 4160 bytes: 33 steps, the last one half full.  At these
+    # sizes the planner keeps fp8 unsplit, so the split is forced.
+    monkeypatch.setenv("TGEMM_SPLIT", "4")
+    N, K = 784, 4160
+    s = splits_of(M, N, K, "e4m3", "bf16", layout)
+    say("case split fp8 exact", layout, M, "splits", s)
+    assert s > 1
+    inp = W.int_inputs(M, N, K, "e4m3", seed=M + 9)
+    exact(oracle_mod, inp, M, N, K, "e4m3", "bf16", layout, scale=(0.5, 0.25), workspace=True)
+
+
+def test_split_fp8_random_within_bound(oracle_mod, monkeypatch):
+    monkeypatch.setenv("TGEMM_SPLIT", "3")
+    M, N, K = 200, 784, 4160
+    inp = W.make_inputs(W.WORKLOADS["e4m3_8192"], M=M, N=N, K=K, seed=4444)
+    bits = run_gemm(inp.A, inp.B, M, N, K, "e4m3", "bf16", "bt_preshuffled", scale=(inp.scale_a, inp.scale_b),
+                    workspace=True)
+    C_ref, S = oracle_mod.gemm_bt(inp.A, inp.B, dtype="e4m3", sigma=oracle_mod.sigma_of(inp.scale_a, inp.scale_b))
+    r = assert_within_bound(decode(bits), C_ref, S, "e4m3", "split fp8 random")
+    say("  worst err/bound", r)
 
 
 @pytest.mark.parametrize("splits", [2, 3, 5, 8])
@@ -144,17 +171,18 @@ def test_split_epilogue_smooth(oracle_mod, kind):
     say("  worst err/bound", r)
 
 
-@pytest.mark.parametrize("name", ["bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192"])
+@pytest.mark.parametrize("name", ["bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192"])
 def test_split_full_size_sampled(oracle_mod, name):
     w = W.WORKLOADS[name]
     say("case split full-size", name)
     inp = W.make_inputs(w)
     bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, workspace=True,
-                          return_plan_info=True)
+                          scale=(inp.scale_a, inp.scale_b), return_plan_info=True)
     say("  plan", info)
     assert info["ws_splits"] > 1
     rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
-    c_ref, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype)
+    c_ref, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype,
+                                          sigma=oracle_mod.sigma_of(inp.scale_a, inp.scale_b))
     r = assert_within_bound(decode(bits[rows, cols]), c_ref, s, w.dtype, name)
     say("  worst err/bound", r)
     assert np.all(np.isfinite(decode(bits)))

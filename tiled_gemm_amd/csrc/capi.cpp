@@ -94,6 +94,7 @@ int out_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? tg::kOutF32 : tg::kO
 
 // Static tile table: the first entry whose predicate holds.  An optional
 // TGEMM_TILE=<bm>x<bn> in the environment forces a tiled variant (sweeps).
+// force256: 256 x 256 tiles with fp32 output (the split-K partial tiles).
 const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = false)
 {
     int n = 0;
@@ -101,7 +102,7 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
     const bool bkn = I.layout == GEMM_LAYOUT_BN || I.layout == GEMM_LAYOUT_AT_BN;
     const bool akm = I.layout == GEMM_LAYOUT_AT || I.layout == GEMM_LAYOUT_AT_BN;
-    const int elem = elem_of(I.dtype), out = out_of(I.dtype);
+    const int elem = elem_of(I.dtype), out = force256 ? tg::kOutF32 : out_of(I.dtype);
     if (is_mx(I.dtype) || is_int(I.dtype)) {
         // MX and integer operands: only the pipelined 256 x 256 kernel (any
         // M, N: tails are masked).  TGEMM_PIPE_WAVES=<n> restricts the choice
@@ -228,8 +229,9 @@ void plan_split(gemm_plan *p)
     const gemm_plan_info &I = p->info;
     p->splits = 1;
     p->split_steps = p->k_tiles;
-    if (I.kernel != 0 || I.M == 0 || I.N == 0 || I.K == 0 || elem_of(I.dtype) != tg::kBf16 || is_mx(I.dtype) ||
-        is_int(I.dtype) || (I.layout != GEMM_LAYOUT_BT && I.layout != GEMM_LAYOUT_BT_PRESHUFFLED) ||
+    const int elem = elem_of(I.dtype);
+    if (I.kernel != 0 || I.M == 0 || I.N == 0 || I.K == 0 || (elem != tg::kBf16 && elem != tg::kFp8) ||
+        (I.layout != GEMM_LAYOUT_BT && I.layout != GEMM_LAYOUT_BT_PRESHUFFLED) ||
         I.N * 4 * 256 >= (int64_t(1) << 31))
         return;
     const int64_t tm = (I.M + 255) / 256, tn = (I.N + 255) / 256;
@@ -238,6 +240,11 @@ void plan_split(gemm_plan *p)
     const char *e = getenv("TGEMM_SPLIT");
     if (e) {
         s = atoi(e);
+    } else if (elem == tg::kFp8 && I.tile_m != 256) {
+        // fp8 B is half the bytes, so the fp32 partials weigh twice as much:
+        // measured, splitting beats the 128 x 128 tiles' plan only where that
+        // plan already takes 256 x 256 tiles (M around 1024 for N = 8192).
+        return;
     } else {
         while (tiles * s * 2 <= 256 && p->k_tiles / (s * 2) >= 8)
             s *= 2;
@@ -247,9 +254,7 @@ void plan_split(gemm_plan *p)
     const int per = (p->k_tiles + s - 1) / s;
     if ((int64_t)(s - 1) * per >= p->k_tiles)           // every slice non-empty
         return;
-    gemm_plan_info J = I;
-    J.dtype = GEMM_BF16_OUT_F32;
-    const tg::TiledVariant *v = pick_tiled(J, true);
+    const tg::TiledVariant *v = pick_tiled(I, true);
     // Only the pipelined and the LDS-staged kernels read the split fields.
     int np = 0, nd = 0;
     const tg::TiledVariant *pv = tg::pipe_variants(&np), *dv = tg::dma_variants(&nd);

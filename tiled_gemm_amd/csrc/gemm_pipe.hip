@@ -559,6 +559,9 @@ static const TiledVariant kPipe[] = {
     TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 28
     TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 29
     TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 30: loads in bursts
+    // fp8 with fp32 output: the split-K partial tiles
+    TG_PIPE_S(kFp8, kOutF32, false, 1, 8, 4, 3, true, true),    // 31
+    TG_PIPE_S(kFp8, kOutF32, true, 1, 8, 4, 3, true, true),
 };
 
 const TiledVariant *pipe_variants(int *count)

@@ -110,6 +110,9 @@ WORKLOADS = {
     "bf16_1024x8192x8192": Workload("bf16_1024x8192x8192", 1024, 8192, 8192, "bf16", "bf16", "bt",
                                     ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), 1016,
                                     "prefill chunk: 128 output tiles"),
+    "e4m3_1024x8192x8192": Workload("e4m3_1024x8192x8192", 1024, 8192, 8192, "e4m3", "bf16", "bt_preshuffled",
+                                    ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1018,
+                                    "prefill chunk in fp8, per-tensor scales amax/448, pre-shuffled weight"),
     "e4m3_8192": Workload("e4m3_8192", 8192, 8192, 8192, "e4m3", "bf16", "bt",
                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1005,
                           "per-tensor scales amax/448"),
