@@ -203,14 +203,16 @@ def main():
     names = [args.only] if args.only else [HEADLINE] + ([] if args.no_also else [
         "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
         "bf16_skinny_32x8192x8192_preshuffled", "bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192",
-        "e4m3_1024x8192x8192", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
+        "e4m3_1024x8192x8192", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "mxfp4_32x8192x8192",
+        "i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
     results = {}
     inputs = {}
     for name in names:
         w = W.WORKLOADS[name]
         log("bench: generating", name)
         inp = W.make_inputs(w)
-        rotate = 3 if name.startswith("bf16_skinny_32x8192x8192") or name == "w4a8_32x8192x8192" else 1
+        rotate = 3 if name.startswith("bf16_skinny_32x8192x8192") or name in ("w4a8_32x8192x8192",
+                                                                               "mxfp4_32x8192x8192") else 1
         steps = args.steps if name == (args.only or HEADLINE) else max(10, args.steps // 2)
         split = name in SPLIT_K_WORKLOADS
         if split:

@@ -180,7 +180,9 @@ def test_plan_choices(lib, monkeypatch):
     assert info(32, 8192, 8192, tg.GEMM_I8_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 1
     assert info(32, 8192, 8192, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 1
     assert info(32, 8192, 8192, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT)["kernel"] == 0
-    assert info(32, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 0
+    assert info(32, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 1
+    assert info(32, 8192, 8192, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)["kernel"] == 1
+    assert info(32, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT)["kernel"] == 0
     c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
     assert c["lds_stages"] == 4                      # fp8: B in registers
@@ -260,7 +262,10 @@ def test_mx_plans(lib, dtype, bits, layout):
     for M, N, K in [(8192, 8192, 8192), (32, 4096, 1024), (300, 272, 1152)]:
         with tg.Plan(M, N, K, dtype, layout) as p:
             info = p.info()
-            assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 256   # 4-wave pipelined
+            if M <= 64 and layout == tg.GEMM_LAYOUT_BT_PRESHUFFLED:      # decode: the skinny kernel
+                assert info["kernel"] == 1 and info["tile_n"] == 32
+            else:
+                assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 256   # 4-wave pipelined
             assert info["elem_bits"] == bits and info["elem_bytes"] == bits // 8
             assert tg.gemm_preshuffled_b_bytes(p.handle) == N * K * bits // 8
             groups = ((K + 127) // 128 + 3) // 4

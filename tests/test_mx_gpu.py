@@ -102,7 +102,52 @@ def test_mx_random_within_bound(oracle_mod, fmt, layout):
     say("  worst err/bound", r)
 
 
-@pytest.mark.parametrize("name,kind", [("mxfp8_8192", "none"), ("mxfp4_8192", "none"), ("mxfp4_8192", "bias_gelu")])
+# Decode shapes (M <= 64) with B pre-shuffled run on the skinny kernel: the
+# waves split K in whole scale groups, the scale words ride with each stage.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 17, 32, 33, 64])
+@pytest.mark.parametrize("N,ragged", [(544, False), (528, True)])
+def test_mx_skinny_bit_exact(oracle_mod, fmt, M, N, ragged):
+    K = _k_for(fmt, ragged)
+    say("case mx skinny exact", fmt, M, N, K)
+    inp = W.mx_int_inputs(M, N, K, fmt, seed=M + N + K)
+    bits, info = run_gemm(inp.A, inp.B, M, N, K, fmt, "bf16", "bt_preshuffled", sa_blocks=inp.sa_blocks,
+                          sb_blocks=inp.sb_blocks, return_plan_info=True)
+    assert info["kernel"] == 1
+    C, S = oracle_mod.gemm_bt_mx(inp.A, inp.sa_blocks, inp.B, inp.sb_blocks, K, fmt)
+    assert S.max() < 2.0 ** 18
+    want = oracle_mod.round_bf16(C)
+    bad = bits != want
+    assert not bad.any(), "%d mismatches, first at %s: got %r want %r" % (
+        int(bad.sum()), np.argwhere(bad)[0], decode(bits)[tuple(np.argwhere(bad)[0])], C[tuple(np.argwhere(bad)[0])])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [8, 48])
+def test_mx_skinny_random_within_bound(oracle_mod, fmt, M):
+    N, K = 784, 4096
+    say("case mx skinny random", fmt, M, N, K)
+    inp = W.make_inputs(W.WORKLOADS[fmt + "_8192"], M=M, N=N, K=K, seed=57)
+    e = dict(scale_a=np.full(M, 0.5), scale_b=np.linspace(0.5, 2.0, N), bias=np.linspace(-1.0, 1.0, N),
+             kind="bias_silu")
+    bits, info = run_gemm(inp.A, inp.B, M, N, K, fmt, "bf16", "bt_preshuffled", sa_blocks=inp.sa_blocks,
+                          sb_blocks=inp.sb_blocks, epi=e, return_plan_info=True)
+    assert info["kernel"] == 1
+    acc, S = oracle_mod.gemm_bt_mx(inp.A, inp.sa_blocks, inp.B, inp.sb_blocks, K, fmt)
+    want = oracle_mod.epilogue(acc, e["scale_a"], e["scale_b"], e["bias"], e["kind"])
+    scale = np.abs(e["scale_a"][:, None] * e["scale_b"][None, :])
+    r = assert_epilogue_within_bound(decode(bits), want, S * scale, np.abs(acc) * scale,
+                                     np.abs(e["bias"])[None, :], fmt, e["kind"], "mx skinny " + fmt)
+    say("  worst err/bound", r)
+
+
+def test_mx_plain_decode_stays_tiled():
+    with tg.Plan(32, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert p.info()["kernel"] == 0
+
+
+@pytest.mark.parametrize("name,kind", [("mxfp8_8192", "none"), ("mxfp4_8192", "none"), ("mxfp4_8192", "bias_gelu"),
+                                       ("mxfp4_32x8192x8192", "none")])
 def test_mx_full_size_sampled(oracle_mod, name, kind):
     w = W.WORKLOADS[name]
     say("case mx full-size", name, kind)

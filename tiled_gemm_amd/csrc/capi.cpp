@@ -196,10 +196,10 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
 const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
 {
     // Skinny kernels: bf16, fp8 and int8 with B N x K or pre-shuffled; W4A8
-    // with B pre-shuffled.
+    // and the MX formats with B pre-shuffled.
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
-    if ((I.layout != GEMM_LAYOUT_BT && !pre) || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") || is_mx(I.dtype) ||
-        (I.dtype == GEMM_W4A8_OUT_BF16 && !pre))
+    if ((I.layout != GEMM_LAYOUT_BT && !pre) || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") ||
+        ((I.dtype == GEMM_W4A8_OUT_BF16 || is_mx(I.dtype)) && !pre))
         return nullptr;
     const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
     int n = 0;
@@ -675,6 +675,9 @@ int run_impl(const gemm_plan *plan, const void *A, const void *B, void *C, const
         a.k_tiles = plan->k_tiles;
         a.tail_bytes = plan->tail_bytes;
         a.kbytes_b = (int32_t)plan->kbytes_b;
+        a.sa_img = (const uint8_t *)sa_img;
+        a.sb_img = (const uint8_t *)sb_img;
+        a.s_groups = (int32_t)scale_groups(I.K);
         e = plan->skinny->launch(a, I.grid, stream);
     } else {
         tg::TiledArgs a{};

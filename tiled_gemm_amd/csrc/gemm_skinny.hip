@@ -270,13 +270,26 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
     // 32 q + 31, unpacked into two int8 operands, half h pairing with A
     // chunk 2 q + h.  Otherwise two blocks (K bytes 0..63 and 64..127 of the
     // step) pairing with A chunks q and 4 + q.
+    //
+    // MX (MXFP8, MXFP4): the operands of the fp8 and bf16 schedules (chunks q
+    // and q + 4 as one 32-byte e4m3 operand; or per 64-byte half one 16-byte
+    // e2m1 operand), scaled per lane by the E8M0 bytes of the scale images:
+    // one 16-byte load per lane and stage brings the scales of 4 row blocks
+    // (A: the rows' quad; B: the columns' quad) for the 4 K-slices of the
+    // step's group.  A group is 4 steps (MXFP8, one 128-element slice per
+    // step) or 2 (MXFP4, two per step); each wave's run starts on a group and
+    // the ring depth is a multiple of it, so every slice index is a constant.
     constexpr bool W4 = ELEM == kW4A8;
     constexpr bool INT = ELEM == kI8 || W4;
+    constexpr bool MX = ELEM == kMx8 || ELEM == kMx4;
+    constexpr int SPG = ELEM == kMx8 ? 4 : 2;                 // steps per scale group
     constexpr int BH = W4 ? 1 : 2;
     static_assert(!INT || OUT == kOutBf16, "integer GEMMs write bf16");
+    static_assert(!MX || (DEPTH % SPG == 0 && ORD == 1 && !BLDS), "MX: whole scale groups per ring, runs");
     using Cfg = SkinnyPreCfg<MB, WAVES, DEPTH, BLDS, BH>;
     constexpr int NB = kSkinnyTileN / 16;
     constexpr int AL = Cfg::AL;
+    constexpr int LOADS = Cfg::LOADS + (MX ? 2 : 0);
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
 
     const int w = wave_id();
@@ -308,13 +321,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
     // ORD: 0 runs of steps, rotated start; 1 runs; 2 steps w, w + WAVES, ...,
     // rotated start; 3 the same without rotation
     constexpr bool INTER = ORD >= 2;
-    const int per = (nk + WAVES - 1) / WAVES;
+    const int per = MX ? ((nk + WAVES - 1) / WAVES + SPG - 1) / SPG * SPG : (nk + WAVES - 1) / WAVES;
     const int first = INTER ? w : w * per;
     const int nt = INTER ? (w < nk ? (nk - w + WAVES - 1) / WAVES : 0) : max(0, min(per, nk - first));
     const int rot = (ORD == 0 || ORD == 2) ? (int)((blockIdx.x * 37u) % (uint32_t)max(nk, 1)) : 0;
 
     // B of one step: image blocks BH kt + h of 16-column block j.
     u32x4 bq[DEPTH][NB][BH];
+    // MX: the scale words of each stage's group (A: row blocks 0..3 of quad 0;
+    // B: the columns' quad, whose blocks bq0, bq0 + 1 are this workgroup's).
+    u32x4 scA[DEPTH], scB[DEPTH];
+    const int G = p.s_groups;
+    const auto rSA = make_rsrc(p.sa_img, MX ? (uint32_t)G * 1024u : 0u);
+    const auto rSB = make_rsrc(p.sb_img, MX ? (uint32_t)((p.N + 63) / 64) * (uint32_t)G * 1024u : 0u);
+    const uint32_t sbase = (uint32_t)(n0 / 64) * (uint32_t)G;
+    const bool bq_hi = (n0 & 32) != 0;
 
     // Step t of this wave into stage s.  Every load is issued; those past the
     // run, or past K in a half-filled last step, are out of range (zeros).
@@ -344,6 +365,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
                 else
                     bq[S][j][h] = buf_load16(rB, voffB, soffB);
             }
+        if constexpr (MX) {
+            const uint32_t g = (uint32_t)(kt / SPG);
+            const bool sin = in & ((int)g < G);
+            scA[S] = buf_load16(rSA, keep_or_oob(sin, g * 1024u + (uint32_t)l * 16u), 0);
+            scB[S] = buf_load16(rSB, keep_or_oob(sin, (sbase + g) * 1024u + (uint32_t)l * 16u), 0);
+        }
         issue_fence();
     };
 
@@ -386,9 +413,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
                 b0 = bq[S][j][0];
                 b1 = bq[S][j][BH - 1];
             }
+            uint32_t sx = 0;
+            if constexpr (MX)
+                sx = bq_hi ? (j ? scB[S].w : scB[S].z) : (j ? scB[S].y : scB[S].x);
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                if constexpr (ELEM == kBf16) {
+                if constexpr (MX) {
+                    constexpr int GP = S % SPG;                 // the step's place in its group
+                    const uint32_t sy = scA[S][i];
+                    if constexpr (ELEM == kMx8) {
+                        mfma_mx8_a<GP>(acc[i][j], join32(b0, b1), join32(a[i][0], a[i][1]), sx, sy);
+                    } else {
+                        mfma_mx4_a<2 * GP>(acc[i][j], b0, a[i][0], sx, sy);
+                        mfma_mx4_a<2 * GP + 1>(acc[i][j], b1, a[i][1], sx, sy);
+                    }
+                } else if constexpr (ELEM == kBf16) {
                     acc[i][j] = mfma_bf16(b0, a[i][0], acc[i][j]);
                     acc[i][j] = mfma_bf16(b1, a[i][1], acc[i][j]);
                 } else if constexpr (INT) {
@@ -404,7 +443,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
     // Waiting for the oldest stage leaves the DEPTH - 1 younger ones in
     // flight.  The run is rounded up to whole rings; the extra steps load and
     // multiply zeros.
-    constexpr int kVm = (DEPTH - 1) * Cfg::LOADS;
+    constexpr int kVm = (DEPTH - 1) * LOADS;
+    static_assert(kVm < 64, "vmcnt holds 6 bits");
     constexpr int kWaitOldest = (kWaitVmcnt0 & ~0xC00F) | (kVm & 0xF) | ((kVm >> 4) << 14);
     constexpr int kWaitLds = 0xC07F;
     const int ntr = (nt + DEPTH - 1) / DEPTH * DEPTH;
@@ -418,6 +458,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_skinny_pre_kernel(const Sk
         });
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);
+    if constexpr (MX)
+        mfma_drain_acc(acc);                      // the scaled MFMAs are inline assembly
     __syncthreads();
     skinny_finish<MB, OUT, WAVES, ELEM == kI8 ? 1 : (W4 ? 16 : 0)>(p, acc, lds, n0);
 }
@@ -471,6 +513,11 @@ static const SkinnyVariant kSkinny[] = {
     TG_SKINNY_PRE(4, kI8, kOutBf16, 8, 2),
     TG_SKINNY_PRE(1, kW4A8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kW4A8, kOutBf16, 12, 2),         // 36
     TG_SKINNY_PRE(4, kW4A8, kOutBf16, 8, 2),
+    // MX block-scaled operands, B pre-shuffled
+    TG_SKINNY_PRE(1, kMx8, kOutBf16, 8, 4), TG_SKINNY_PRE(2, kMx8, kOutBf16, 8, 4),           // 39
+    TG_SKINNY_PRE(4, kMx8, kOutBf16, 4, 4),
+    TG_SKINNY_PRE(1, kMx4, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kMx4, kOutBf16, 12, 2),         // 42
+    TG_SKINNY_PRE(4, kMx4, kOutBf16, 8, 2),
 };
 
 const SkinnyVariant *skinny_variants(int *count)

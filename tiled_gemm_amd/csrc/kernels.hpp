@@ -91,6 +91,11 @@ struct SkinnyArgs {
     int32_t k_tiles;
     int32_t tail_bytes;
     int32_t kbytes_b;       // bytes of one row of B (kbytes, or kbytes / 2 for int4 B)
+    // MX operands only: the block-scale images (see BscaleArgs) and their
+    // number of 4-slice groups along K.
+    const uint8_t *sa_img;
+    const uint8_t *sb_img;
+    int32_t s_groups;
 };
 
 struct PreshuffleArgs {

@@ -119,6 +119,9 @@ WORKLOADS = {
     "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "mxfp8", "bf16", "bt_preshuffled",
                            ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1006,
                            "MX block scales, e4m3 elements"),
+    "mxfp4_32x8192x8192": Workload("mxfp4_32x8192x8192", 32, 8192, 8192, "mxfp4", "bf16", "bt_preshuffled",
+                                   ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1019,
+                                   "decode with an MXFP4 weight"),
     "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "mxfp4", "bf16", "bt_preshuffled",
                            ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1007,
                            "MX block scales, e2m1 elements"),
