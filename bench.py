@@ -32,7 +32,8 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_preshuffled"
 # Workloads with fewer 256 x 256 tiles than CUs: timed through gemm_run_ws
 # (split K with a workspace), plain gemm_run reported beside.
-SPLIT_K_WORKLOADS = ("bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192")
+SPLIT_K_WORKLOADS = ("bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192",
+                     "w4a8_256x8192x8192")
 # HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE scaled by a copy of known size (see the file for the commands).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_pipe_bf16_8192_preshuffled.txt")
@@ -97,9 +98,16 @@ def time_gemm(torch, tg, w, inp, steps, warmup, rotate=1, epi=None, ws=False):
         qa = torch.from_numpy(inp.sa_rows).cuda()
         qb = torch.from_numpy(inp.sb_cols).cuda()
 
+        wsb = plan.workspace_bytes() if ws else 0
+        Wk = torch.empty(max(16, wsb), dtype=torch.uint8, device="cuda")
+
         def launch(A, B, C):
-            plan.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream=s, scale_a=qa.data_ptr(),
-                        scale_a_per_row=True, scale_b=qb.data_ptr(), scale_b_per_col=True)
+            if ws:
+                plan.run_ws(A.data_ptr(), B.data_ptr(), C.data_ptr(), Wk.data_ptr(), wsb, stream=s,
+                            scale_a=qa.data_ptr(), scale_a_per_row=True, scale_b=qb.data_ptr(), scale_b_per_col=True)
+            else:
+                plan.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream=s, scale_a=qa.data_ptr(),
+                            scale_a_per_row=True, scale_b=qb.data_ptr(), scale_b_per_col=True)
     elif ws:
         wsb = plan.workspace_bytes()
         Wk = torch.empty(max(16, wsb), dtype=torch.uint8, device="cuda")
@@ -204,7 +212,7 @@ def main():
         "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
         "bf16_skinny_32x8192x8192_preshuffled", "bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192",
         "e4m3_1024x8192x8192", "e4m3_8192", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192", "mxfp4_32x8192x8192",
-        "i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
+        "i8_8192", "w4a8_8192", "w4a8_32x8192x8192", "w4a8_256x8192x8192"])
     results = {}
     inputs = {}
     for name in names:

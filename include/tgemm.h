@@ -204,8 +204,9 @@ int gemm_run_ex(const gemm_plan *plan, const void *A, const void *B, void *C,
  * tiles to the workspace; a second kernel sums the s partials of every
  * element in slice order (deterministic) and applies the epilogue of
  * gemm_run_ex.  The plan decides s (gemm_plan_info.ws_splits); plans with
- * s == 1 need no workspace.  bf16 and fp8 e4m3 plans with GEMM_LAYOUT_BT or
- * GEMM_LAYOUT_BT_PRESHUFFLED split; the others never do.  (The pages' GEMM
+ * s == 1 need no workspace.  bf16, fp8 e4m3, int8 and W4A8 plans with
+ * GEMM_LAYOUT_BT or GEMM_LAYOUT_BT_PRESHUFFLED split; MX plans and the other
+ * layouts never do.  (The pages' GEMM
  * has no split K: this is this library's answer to shapes whose tile grid
  * leaves most of the chip idle.)
  *

@@ -417,13 +417,15 @@ def test_split_k_plans(lib, monkeypatch):
     # K bounds the slices: 8 steps (1 KiB of K) each at least
     assert plan(256, 8192, 2048)[0]["ws_splits"] == 4            # 32 steps of 128 bytes
     assert plan(256, 8192, 512)[0]["ws_splits"] == 1
-    # skinny, MX, integer and K-major layouts never split
+    # skinny, MX and K-major layouts never split
     assert plan(64, 8192, 8192)[0]["ws_splits"] == 1
     # fp8 splits only where its unsplit plan takes 256 x 256 tiles
     assert plan(256, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)[0]["ws_splits"] == 1
     assert plan(1024, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)[0]["ws_splits"] == 2
     assert plan(1024, 8192, 8192, tg.GEMM_E4M3_OUT_BF16)[0]["ws_splits"] == 2
-    assert plan(256, 8192, 8192, tg.GEMM_I8_OUT_BF16)[0]["ws_splits"] == 1
+    assert plan(256, 8192, 8192, tg.GEMM_I8_OUT_BF16)[0]["ws_splits"] == 8          # 64 steps of 128 bytes
+    assert plan(256, 8192, 8192, tg.GEMM_W4A8_OUT_BF16, tg.GEMM_LAYOUT_BT)[0]["ws_splits"] == 4   # partials <= B
+    assert plan(256, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16)[0]["ws_splits"] == 1
     assert plan(256, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)[0]["ws_splits"] == 1
     # a forced count, uneven slices; an impossible one is refused (no split)
     monkeypatch.setenv("TGEMM_SPLIT", "3")

@@ -93,6 +93,32 @@ def test_split_fp8_random_within_bound(oracle_mod, monkeypatch):
     say("  worst err/bound", r)
 
 
+@pytest.mark.parametrize("fmt,layout", [("i8", "bt"), ("i8", "bt_preshuffled"), ("w4a8", "bt"),
+                                        ("w4a8", "bt_preshuffled")])
+@pytest.mark.parametrize("M", [65, 300])
+def test_split_int_exact(oracle_mod, monkeypatch, fmt, layout, M):
+    # full-range int8 / int4 values with sums below 2^24: the partials, their
+    # sum and the one rounding to bf16 are exact; per-row / per-column
+    # power-of-two dequantisation scales in the reduction's epilogue.  K =
+    # 2048 keeps every sum of |a b| below 2^24 (16 steps: two slices, forced,
+    # since the planner keeps the partials within B's bytes).
+    monkeypatch.setenv("TGEMM_SPLIT", "2")
+    N, K = 784, 2048
+    with tg.Plan(M, N, K, tg.GEMM_I8_OUT_BF16 if fmt == "i8" else tg.GEMM_W4A8_OUT_BF16, tg.LAYOUTS[layout]) as p:
+        s = p.info()["ws_splits"]
+    say("case split int exact", fmt, layout, M, "splits", s)
+    assert s > 1
+    inp = W.int_inputs(M, N, K, fmt, seed=M + len(layout), lo=-128, hi=127)
+    rng = np.random.default_rng(M)
+    e = dict(scale_a=2.0 ** rng.integers(-3, 1, M), scale_b=2.0 ** rng.integers(-3, 1, N), kind="none")
+    bits = run_gemm(inp.A, inp.B, M, N, K, fmt, "bf16", layout, epi=e, workspace=True)
+    acc, S = oracle_mod.gemm_bt_int(inp.A, inp.B, K, fmt)
+    assert S.max() < 2.0 ** 24
+    want = oracle_mod.round_bf16(oracle_mod.epilogue(acc, e["scale_a"], e["scale_b"], None, "none"))
+    bad = np.argwhere(bits != want)
+    assert bad.size == 0, "%d mismatches, first %s" % (len(bad), bad[:3].tolist())
+
+
 @pytest.mark.parametrize("splits", [2, 3, 5, 8])
 def test_split_forced_counts(oracle_mod, monkeypatch, splits):
     # uneven slices (65 steps over 3 or 5 slices), every slice non-empty
@@ -171,18 +197,29 @@ def test_split_epilogue_smooth(oracle_mod, kind):
     say("  worst err/bound", r)
 
 
-@pytest.mark.parametrize("name", ["bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192"])
+@pytest.mark.parametrize("name", ["bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192",
+                                  "w4a8_256x8192x8192"])
 def test_split_full_size_sampled(oracle_mod, name):
     w = W.WORKLOADS[name]
     say("case split full-size", name)
     inp = W.make_inputs(w)
-    bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, workspace=True,
-                          scale=(inp.scale_a, inp.scale_b), return_plan_info=True)
+    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    if w.dtype in ("i8", "w4a8"):
+        e = dict(scale_a=inp.sa_rows.astype(np.float64), scale_b=inp.sb_cols.astype(np.float64), kind="none")
+        bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, epi=e, workspace=True,
+                              return_plan_info=True)
+        acc, s = oracle_mod.gemm_bt_int_entries(inp.A, inp.B, w.K, rows, cols, w.dtype)
+        scale = np.abs(e["scale_a"][rows] * e["scale_b"][cols])
+        c_ref = oracle_mod.epilogue_entries(acc, e["scale_a"][rows], e["scale_b"][cols], None, "none")
+        r = assert_epilogue_within_bound(decode(bits[rows, cols]), c_ref, s * scale, np.abs(acc) * scale, 0.0,
+                                         w.dtype, "none", name)
+    else:
+        bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, workspace=True,
+                              scale=(inp.scale_a, inp.scale_b), return_plan_info=True)
+        c_ref, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype,
+                                              sigma=oracle_mod.sigma_of(inp.scale_a, inp.scale_b))
+        r = assert_within_bound(decode(bits[rows, cols]), c_ref, s, w.dtype, name)
     say("  plan", info)
     assert info["ws_splits"] > 1
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
-    c_ref, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype,
-                                          sigma=oracle_mod.sigma_of(inp.scale_a, inp.scale_b))
-    r = assert_within_bound(decode(bits[rows, cols]), c_ref, s, w.dtype, name)
     say("  worst err/bound", r)
     assert np.all(np.isfinite(decode(bits)))

@@ -222,15 +222,16 @@ const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
 // bound by how fast each CU streams its tile's operands, so K is divided into
 // s slices: tiles * s workgroups each write an fp32 partial tile, and a
 // reduction kernel sums the slices in order and applies the epilogue.  s is
-// the largest power of two with tiles * s <= 256 and at least 8 K steps
-// (1 KiB of K) per slice; TGEMM_SPLIT=<s> forces it (sweeps; 1 disables).
+// the largest power of two with tiles * s <= 256, at least 8 K steps (1 KiB
+// of K) per slice and partials no larger than B; TGEMM_SPLIT=<s> forces it
+// (sweeps; 1 disables).
 void plan_split(gemm_plan *p)
 {
     const gemm_plan_info &I = p->info;
     p->splits = 1;
     p->split_steps = p->k_tiles;
     const int elem = elem_of(I.dtype);
-    if (I.kernel != 0 || I.M == 0 || I.N == 0 || I.K == 0 || (elem != tg::kBf16 && elem != tg::kFp8) ||
+    if (I.kernel != 0 || I.M == 0 || I.N == 0 || I.K == 0 || is_mx(I.dtype) ||
         (I.layout != GEMM_LAYOUT_BT && I.layout != GEMM_LAYOUT_BT_PRESHUFFLED) ||
         I.N * 4 * 256 >= (int64_t(1) << 31))
         return;
@@ -246,7 +247,11 @@ void plan_split(gemm_plan *p)
         // plan already takes 256 x 256 tiles (M around 1024 for N = 8192).
         return;
     } else {
-        while (tiles * s * 2 <= 256 && p->k_tiles / (s * 2) >= 8)
+        // Also: the partials written and read back (s * M * N * 4 bytes) stay
+        // within B's bytes (measured: W4A8 at 256 x 8192 x 8192 takes 0.0516 ms
+        // with 4 slices, 0.0539 with 8).
+        while (tiles * s * 2 <= 256 && p->k_tiles / (s * 2) >= 8 &&
+               (int64_t)(s * 2) * I.M * 4 <= p->kbytes_b)
             s *= 2;
     }
     if (s < 2 || s > 64)

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_kernel(const Tile
     constexpr bool INT = ELEM == kI8 || ELEM == kW4A8;
     constexpr bool W4 = ELEM == kW4A8;
     constexpr int BH = W4 ? 1 : 2;                           // B loads per block and step
-    static_assert(!INT || OUT == kOutBf16, "integer GEMMs write bf16");
+    // Integer GEMMs write bf16; their fp32-output instances write split-K
+    // partials (the int32 sums converted, times 1/16 for int4 B).
     constexpr int NG = WIDE ? BP_FM : 2 * BP_FM;            // groups (FN MFMAs each)
     static_assert(!MX || (ACCA && ADMA && BP_WTM % 64 == 0 && BP_WTN % 64 == 0),
                   "MX operands run on the AGPR-accumulator kernel, whole 64-row scale quads per wave");
@@ -559,9 +560,13 @@ static const TiledVariant kPipe[] = {
     TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 28
     TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 29
     TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 30: loads in bursts
-    // fp8 with fp32 output: the split-K partial tiles
+    // fp8 and integer operands with fp32 output: the split-K partial tiles
     TG_PIPE_S(kFp8, kOutF32, false, 1, 8, 4, 3, true, true),    // 31
     TG_PIPE_S(kFp8, kOutF32, true, 1, 8, 4, 3, true, true),
+    TG_PIPE_S(kI8, kOutF32, true, 1, 8, 4, 6, true, true),      // 33
+    TG_PIPE_S(kI8, kOutF32, false, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kW4A8, kOutF32, true, 1, 8, 4, 6, true, true),
+    TG_PIPE_S(kW4A8, kOutF32, false, 1, 8, 4, 6, true, true),
 };
 
 const TiledVariant *pipe_variants(int *count)

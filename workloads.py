@@ -143,6 +143,9 @@ WORKLOADS = {
     "w4a8_32x8192x8192": Workload("w4a8_32x8192x8192", 32, 8192, 8192, "w4a8", "bf16", "bt_preshuffled",
                                   ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1017,
                                   "decode with an int4 weight: int8 A, packed int4 B"),
+    "w4a8_256x8192x8192": Workload("w4a8_256x8192x8192", 256, 8192, 8192, "w4a8", "bf16", "bt_preshuffled",
+                                   ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1020,
+                                   "batched decode with an int4 weight"),
     "w4a8_8192": Workload("w4a8_8192", 8192, 8192, 8192, "w4a8", "bf16", "bt_preshuffled",
                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1009,
                           "int8 A, int4 B, per-row / per-channel absmax scales"),
