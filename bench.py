@@ -299,9 +299,14 @@ def main():
                       "tile": "%dx%d" % (rr["info"]["tile_m"], rr["info"]["tile_n"]),
                       "input_sets_rotated": rr["rotate"]}
         if "ms_gemm_run" in rr:
+            # gemm_run_ws: 256 x 256 tiles, K split (the plain gemm_run's own tile may differ)
+            also[name]["tile"] = "256x256" if rr["info"]["ws_splits"] > 1 else also[name]["tile"]
             also[name]["split_k"] = rr["info"]["ws_splits"]
             also[name]["ms_gemm_run"] = round(rr["ms_gemm_run"], 5)
     if head in SPLIT_K_WORKLOADS:
+        if r["info"]["ws_splits"] > 1:
+            line["config"]["tile"] = "256x256"
+            line["config"]["grid"] = r["info"]["ws_grid"]
         line["config"]["split_k"] = r["info"]["ws_splits"]
         line["config"]["ms_gemm_run"] = round(r["ms_gemm_run"], 5)
     if also:
