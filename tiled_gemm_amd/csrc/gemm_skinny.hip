@@ -1,5 +1,9 @@
 // Skinny GEMM (M <= 64): C = A * B^T when B is the only large operand and
-// the product is bound by streaming B from HBM once.
+// the product is bound by streaming B from HBM once (decode shapes).  Two
+// kernels share the workgroup shape, the K split over the waves and the
+// reduction: gemm_skinny_kernel below (B N x K, bf16 / fp8 / int8, both
+// operands staged through LDS) and gemm_skinny_pre_kernel further down (B
+// pre-shuffled, streamed straight into VGPRs; also W4A8 and MX).
 //
 // One workgroup owns 32 columns of C (two 16-column MFMA blocks) and every
 // row.  Its WAVES waves split K: wave w takes a contiguous run of 128-byte K
