@@ -24,9 +24,10 @@
  * so C = A * B with b(n,k) = B[k][n].  The kernel reads it through the
  * gfx950 LDS transpose load (ds_read_b64_tr_b16, the 16-lane copy atom of
  * FlyDSL's "add-target-atom-op" skill, section 1.5.2 "Shape-product
- * invariants"; for fp8 its 8-bit form ds_read_b64_tr_b8).  bf16 or fp8
- * e4m3 inputs; K * N * elem_bytes < 2^31; no pre-shuffled image
- * (gemm_preshuffle_b rejects such plans); fp8 plans use 256 x 256 tiles.
+ * invariants"; for 8-bit elements its form ds_read_b64_tr_b8).  bf16, fp8
+ * e4m3 or int8 inputs; K * N * elem_bytes < 2^31; no pre-shuffled image
+ * (gemm_preshuffle_b rejects such plans); fp8 and int8 plans use 256 x 256
+ * tiles.
  *
  * GEMM_LAYOUT_AT and GEMM_LAYOUT_AT_BN store A as K x M row-major (lda = M),
  * so a(m,k) = A[k][m]; B is N x K (AT) or K x N (AT_BN, b(n,k) = B[k][n]).

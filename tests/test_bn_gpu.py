@@ -149,3 +149,43 @@ def test_bn_fp8_random_within_bound(oracle_mod, monkeypatch, M, N, K):
         assert np.all(np.isfinite(decode(bits)))
     r = assert_within_bound(got, C, S, "e4m3", "bn fp8 random %dx%dx%d" % (M, N, K))
     say("  worst err/bound", r)
+
+
+# ------------------------------------------------------------------ int8 (8-bit transpose read, int32 sums)
+
+@pytest.mark.parametrize("M,N,K", [(300, 272, 1088), (256, 512, 1024), (1, 16, 64), (77, 48, 192)])
+def test_bn_int8_bit_exact(oracle_mod, monkeypatch, M, N, K):
+    # full-range int8 with sums of |a b| below 2^24: the bf16 output is the
+    # single RNE of the exact int32 sum, dequantised by per-row / per-column
+    # powers of two; B is handed over K x N, the oracle takes the N x K copy
+    set_tile(monkeypatch, None)
+    say("case bn int8 exact", M, N, K)
+    inp = W.int_inputs(M, N, K, "i8", seed=M + 5 * N + K, lo=-128, hi=127)
+    B_kn = np.ascontiguousarray(inp.B.T)
+    rng = np.random.default_rng(M + N)
+    e = dict(scale_a=2.0 ** rng.integers(-3, 1, M), scale_b=2.0 ** rng.integers(-3, 1, N), kind="none")
+    bits, info = run_gemm(inp.A, B_kn, M, N, K, "i8", "bf16", "bn", epi=e, return_plan_info=True)
+    assert info["tile_m"] == 256 and info["kernel"] == 0
+    acc, S = oracle_mod.gemm_bt_int(inp.A, inp.B, K, "i8")
+    assert S.max() < 2.0 ** 24
+    want = oracle_mod.round_bf16(oracle_mod.epilogue(acc, e["scale_a"], e["scale_b"], None, "none"))
+    bad = np.argwhere(bits != want)
+    assert bad.size == 0, "%d mismatches, first %s" % (len(bad), bad[:3].tolist())
+
+
+def test_bn_int8_quantised_full_size_sampled(oracle_mod, monkeypatch):
+    set_tile(monkeypatch, None)
+    M = N = K = 4096
+    say("case bn int8 quantised", M, N, K)
+    inp = W.make_inputs(W.WORKLOADS["i8_8192"], M=M, N=N, K=K, seed=61)
+    B_kn = np.ascontiguousarray(inp.B.T)
+    e = dict(scale_a=inp.sa_rows.astype(np.float64), scale_b=inp.sb_cols.astype(np.float64), kind="none")
+    bits = run_gemm(inp.A, B_kn, M, N, K, "i8", "bf16", "bn", epi=e)
+    rows, cols = sample_entries(M, N, 8192, seed=62)
+    acc, S = oracle_mod.gemm_bt_int_entries(inp.A, inp.B, K, rows, cols, "i8")
+    want = oracle_mod.epilogue_entries(acc, e["scale_a"][rows], e["scale_b"][cols], None, "none")
+    scale = np.abs(e["scale_a"][rows] * e["scale_b"][cols])
+    r = assert_epilogue_within_bound(decode(bits[rows, cols]), want, S * scale, np.abs(acc) * scale, 0.0, "i8",
+                                     "none", "bn int8 4096^3")
+    say("  worst err/bound", r)
+    assert np.all(np.isfinite(decode(bits)))

@@ -340,15 +340,16 @@ def test_bn_layout_plans(lib, monkeypatch):
         with tg.Plan(4096, 4096, 4096, dtype, tg.GEMM_LAYOUT_BN) as p:
             assert p.info()["threads"] == 256                # the generic tiled kernel
         monkeypatch.delenv("TGEMM_DMA")
-    # fp8 e4m3 with B stored K x N: the LDS-staged kernel on 256 x 256 tiles at every size
-    for M, N, K in [(4096, 4096, 4096), (300, 272, 1088), (1, 16, 64)]:
-        with tg.Plan(M, N, K, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BN) as p:
-            info = p.info()
-            assert (info["kernel"], info["tile_m"], info["threads"], info["lds_stages"]) == (0, 256, 512, 2)
-            assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == ((K, N), (N, 1))
-            assert tg.gemm_preshuffled_b_bytes(p.handle) == 0
-    for dtype in (tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_I8_OUT_BF16, tg.GEMM_W4A8_OUT_BF16):
-        with pytest.raises(tg.GemmError, match="bf16 and fp8"):
+    # fp8 e4m3 and int8 with B stored K x N: the LDS-staged kernel on 256 x 256 tiles at every size
+    for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_I8_OUT_BF16):
+        for M, N, K in [(4096, 4096, 4096), (300, 272, 1088), (1, 16, 64)]:
+            with tg.Plan(M, N, K, dtype, tg.GEMM_LAYOUT_BN) as p:
+                info = p.info()
+                assert (info["kernel"], info["tile_m"], info["threads"], info["lds_stages"]) == (0, 256, 512, 2)
+                assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == ((K, N), (N, 1))
+                assert tg.gemm_preshuffled_b_bytes(p.handle) == 0
+    for dtype in (tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_W4A8_OUT_BF16):
+        with pytest.raises(tg.GemmError, match="bf16, fp8 e4m3 and int8"):
             tg.Plan(256, 256, 256, dtype, tg.GEMM_LAYOUT_BN)
     with pytest.raises(tg.GemmError, match="2\\^31"):
         tg.Plan(256, 1 << 16, 1 << 14, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)

@@ -103,6 +103,21 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
     const bool bkn = I.layout == GEMM_LAYOUT_BN || I.layout == GEMM_LAYOUT_AT_BN;
     const bool akm = I.layout == GEMM_LAYOUT_AT || I.layout == GEMM_LAYOUT_AT_BN;
     const int elem = elem_of(I.dtype), out = force256 ? tg::kOutF32 : out_of(I.dtype);
+    // A stored K x M, and 8-bit B stored K x N: only the LDS-staged 256 x 256
+    // kernel reads them.
+    if (akm || (bkn && (elem == tg::kFp8 || elem == tg::kI8))) {
+        int nd = 0;
+        const tg::TiledVariant *d = tg::dma_variants(&nd);
+        if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
+            const int k = atoi(e);
+            if (k >= 0 && k < nd && d[k].akm == akm && d[k].elem == elem && d[k].out == out && d[k].bkn == bkn)
+                return &d[k];
+        }
+        for (int i = 0; i < nd; ++i)
+            if (d[i].akm == akm && d[i].elem == elem && d[i].out == out && d[i].bkn == bkn)
+                return &d[i];
+        return nullptr;
+    }
     if (is_mx(I.dtype) || is_int(I.dtype)) {
         // MX and integer operands: only the pipelined 256 x 256 kernel (any
         // M, N: tails are masked).  TGEMM_PIPE_WAVES=<n> restricts the choice
@@ -115,21 +130,6 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
             if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre &&
                 (waves == 0 || b[i].wgm * b[i].wgn == waves))
                 return &b[i];
-        return nullptr;
-    }
-    // A stored K x M, and fp8 B stored K x N: only the LDS-staged 256 x 256
-    // kernel reads them.
-    if (akm || (bkn && elem == tg::kFp8)) {
-        int nd = 0;
-        const tg::TiledVariant *d = tg::dma_variants(&nd);
-        if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
-            const int k = atoi(e);
-            if (k >= 0 && k < nd && d[k].akm == akm && d[k].elem == elem && d[k].out == out && d[k].bkn == bkn)
-                return &d[k];
-        }
-        for (int i = 0; i < nd; ++i)
-            if (d[i].akm == akm && d[i].elem == elem && d[i].out == out && d[i].bkn == bkn)
-                return &d[i];
         return nullptr;
     }
     int want_bm = 0, want_bn = 0;
@@ -372,8 +372,8 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "A stored K x M is supported for bf16 inputs");
         return nullptr;
     }
-    if (b_kn && !bf16_in && dtype != GEMM_E4M3_OUT_BF16) {
-        fail(GEMM_ERR_UNSUPPORTED, "B stored K x N is supported for bf16 and fp8 e4m3 inputs");
+    if (b_kn && !bf16_in && dtype != GEMM_E4M3_OUT_BF16 && dtype != GEMM_I8_OUT_BF16) {
+        fail(GEMM_ERR_UNSUPPORTED, "B stored K x N is supported for bf16, fp8 e4m3 and int8 inputs");
         return nullptr;
     }
     if (M < 0 || N < 0 || K < 0) {

@@ -98,6 +98,10 @@ __device__ inline f32x4 mfma_fp8x8(i32x8 x, i32x8 y, f32x4 acc)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc, 0, 0, 0, 127, 0, 127);
 }
 
+// The 16-byte halves of a 32-byte operand.
+__device__ inline u32x4 lo16(i32x8 v) { return u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]}; }
+__device__ inline u32x4 hi16(i32x8 v) { return u32x4{(uint32_t)v[4], (uint32_t)v[5], (uint32_t)v[6], (uint32_t)v[7]}; }
+
 // Two 16-byte halves as one 32-byte fp8 operand.
 __device__ inline i32x8 join32(u32x4 lo, u32x4 hi)
 {

@@ -52,7 +52,8 @@ using dic = std::integral_constant<int, N>;
 template <int ELEM, int OUT, bool BPRE, int WGM, int WGN, int PD, bool BKN, bool AKM>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const TiledArgs p)
 {
-    static_assert(ELEM == kBf16 || ELEM == kFp8, "bf16 or fp8 e4m3 operands");
+    static_assert(ELEM == kBf16 || ELEM == kFp8 || (ELEM == kI8 && OUT == kOutBf16),
+                  "bf16, fp8 e4m3 or int8 operands");
     // BKN: B stored K x N (C = A * B): a step's K-rows of the tile's 256
     // columns are the B stage (bf16: 64 rows of 512 bytes, chunks swizzled by
     // bkn_swz, two 16-bit transpose reads per operand; fp8: 128 rows of 256
@@ -63,7 +64,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     static_assert(!AKM || (ELEM == kBf16 && !BPRE), "K x M A: bf16");
     // fp8: one 128-byte K slice per step and MFMA (16x16x128, 32 bytes per
     // lane: chunks q and q + 4 of the slice); bf16: two 64-byte halves.
-    constexpr bool F8 = ELEM == kFp8;
+    // int8 shares the fp8 staging and fragments (8-bit elements); each 32-byte
+    // fragment feeds two 16x16x64 int8 MFMAs, one per 16-byte half (chunk q,
+    // then chunk q + 4: the same K slots in A and in B), into int32 sums.
+    constexpr bool I8 = ELEM == kI8;
+    constexpr bool F8 = ELEM == kFp8 || I8;                 // 8-bit elements
     // K x N B geometry per step: bf16 64 K-rows of 512 bytes (swizzle
     // bkn_swz), fp8 128 K-rows of 256 bytes (swizzle bkn8_swz).
     constexpr int KN_ROWS = F8 ? 128 : 64;
@@ -321,10 +326,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
             const int i = g % FM, h = g / FM;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                if constexpr (F8)
+                if constexpr (I8) {
+                    acc[i][j] = mfma_i8(lo16(fb[S][j]), lo16(fa[g]), acc[i][j]);
+                    acc[i][j] = mfma_i8(hi16(fb[S][j]), hi16(fa[g]), acc[i][j]);
+                } else if constexpr (F8) {
                     acc[i][j] = mfma_fp8x8(fb[S][j], fa[g], acc[i][j]);
-                else
+                } else {
                     acc[i][j] = mfma_bf16(fb[h][j], fa[g], acc[i][j]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -379,7 +388,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         for (int j = 0; j < FN; ++j) {
             const int col = n0 + wn * WTN + j * 16 + 4 * q;
             const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * OB : kOobOffset;
-            const f32x4 v = epi_apply4(ev, acc[i][j], sa, sbv[j], bzv[j]);
+            const f32x4 a = I8 ? int_acc_to_f32(acc[i][j], 1.f) : acc[i][j];
+            const f32x4 v = epi_apply4(ev, a, sa, sbv[j], bzv[j]);
             if constexpr (OUT == kOutF32)
                 buf_store16(rC, __builtin_bit_cast(u32x4, v), voff);
             else
@@ -403,9 +413,10 @@ static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
     TiledVariant{DM_BM, DM_BN, WGM, WGN, kBf16, OUT, false, DM_LDS, 2,                                  \
                  &launch_dma<kBf16, OUT, false, WGM, WGN, PD, BKN, AKM>, BKN, AKM}
 #define TG_DMA_KN(OUT, WGM, WGN, PD) TG_DMA_L(OUT, WGM, WGN, PD, true, false)
-#define TG_DMA_KN8(WGM, WGN, PD)                                                                   \
-    TiledVariant{DM_BM, DM_BN, WGM, WGN, kFp8, kOutBf16, false, DM_LDS, 2,                              \
-                 &launch_dma<kFp8, kOutBf16, false, WGM, WGN, PD, true, false>, true, false}
+#define TG_DMA_KN8E(ELEM, WGM, WGN, PD)                                                            \
+    TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, kOutBf16, false, DM_LDS, 2,                              \
+                 &launch_dma<ELEM, kOutBf16, false, WGM, WGN, PD, true, false>, true, false}
+#define TG_DMA_KN8(WGM, WGN, PD) TG_DMA_KN8E(kFp8, WGM, WGN, PD)
 
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
@@ -418,12 +429,23 @@ static const TiledVariant kDma[] = {
     TG_DMA_KN(kOutBf16, 2, 4, 4),              // 7: B stored K x N
     TG_DMA_KN(kOutF32, 2, 4, 4),
     TG_DMA_KN(kOutBf16, 2, 4, 6),
-    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 10: A stored K x M, B N x K
-    TG_DMA_L(kOutF32, 2, 4, 4, false, true),
-    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 12: A stored K x M, B K x N
-    TG_DMA_L(kOutF32, 2, 4, 4, true, true),
+    // A stored K x M: prefetch distance 2 (a K x M fragment is two transpose
+    // reads and their addresses; at 4 the kernel spilled 19-38 VGPRs and ran
+    // 13-17% slower)
+    TG_DMA_L(kOutBf16, 2, 4, 2, false, true),  // 10: A stored K x M, B N x K
+    TG_DMA_L(kOutF32, 2, 4, 2, false, true),
+    TG_DMA_L(kOutBf16, 2, 4, 2, true, true),   // 12: A stored K x M, B K x N
+    TG_DMA_L(kOutF32, 2, 4, 2, true, true),
     TG_DMA_KN8(1, 8, 3),                       // 14: fp8, B stored K x N
     TG_DMA_KN8(1, 8, 2),
+    TG_DMA_KN8E(kI8, 1, 8, 3),                 // 16: int8, B stored K x N
+    // sweep: other prefetch distances for the transposed layouts
+    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 17: A K x M
+    TG_DMA_L(kOutBf16, 2, 4, 3, false, true),
+    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 19: A K x M, B K x N
+    TG_DMA_L(kOutBf16, 2, 4, 3, true, true),
+    TG_DMA_KN(kOutBf16, 2, 4, 3),              // 21: B K x N
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 22: B N x K
 };
 
 const TiledVariant *dma_variants(int *count)
