@@ -272,6 +272,10 @@ def test_mx_plans(lib, dtype, bits, layout):
             assert p.bscale_image_bytes(0) == (M + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(1) == (N + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(2) == 0
+    with pytest.raises(tg.GemmError, match="2\\^31"):
+        tg.Plan(64, 1 << 21, 1 << 16, dtype, layout)    # block-scale image past 32-bit offsets
+    with tg.Plan(64, 1 << 20, 1 << 14, dtype, layout) as p:
+        assert p.bscale_image_bytes(1) < 1 << 31
     with pytest.raises(tg.GemmError):
         tg.Plan(64, 64, 80, dtype, layout)              # K % 32
     if bits == 4:

@@ -430,6 +430,15 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "M=%lld must be a multiple of 8 for A stored K x M", (long long)M);
         return nullptr;
     }
+    if (is_mx(dtype)) {
+        // The kernels address the block-scale images with 32-bit offsets and
+        // use 2^31 as their out-of-range offset.
+        const int64_t quads = ((M > N ? M : N) + 63) / 64;
+        if (quads * scale_groups(K) * 1024 >= (int64_t(1) << 31)) {
+            fail(GEMM_ERR_UNSUPPORTED, "MX block-scale image above 2^31 bytes (32-bit offsets)");
+            return nullptr;
+        }
+    }
     if (M * kbytes >= (int64_t(1) << 32) && M <= 64) {
         fail(GEMM_ERR_UNSUPPORTED, "skinny A above 4 GiB");
         return nullptr;
