@@ -32,9 +32,10 @@
  * GEMM_LAYOUT_AT and GEMM_LAYOUT_AT_BN store A as K x M row-major (lda = M),
  * so a(m,k) = A[k][m]; B is N x K (AT) or K x N (AT_BN, b(n,k) = B[k][n]).
  * The other operand layout the same skill's naive template and transpose
- * atom describe, read through the same LDS transpose load.  bf16 inputs
- * only; M % 8 == 0 (16-byte pieces of A's K-rows); K * M * 2 < 2^31; such
- * plans always use 256 x 256 tiles.  B is read as stored; only
+ * atom describe, read through the same LDS transpose load (16-bit or 8-bit
+ * form).  bf16, fp8 e4m3 or int8 inputs; M * elem_bytes % 16 == 0 (16-byte
+ * pieces of A's K-rows); K * M * elem_bytes < 2^31; such plans always use
+ * 256 x 256 tiles.  B is read as stored; only
  * GEMM_LAYOUT_BT_PRESHUFFLED plans read the pre-shuffled image.
  *
  * Every pointer passed to gemm_preshuffle_b / gemm_run is a DEVICE pointer

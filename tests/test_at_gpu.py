@@ -101,3 +101,53 @@ def test_at_full_size_sampled(oracle_mod, name):
     r = assert_within_bound(decode(bits[rows, cols]), C, S, "bf16", w.name)
     say("  worst err/bound", r)
     assert np.all(np.isfinite(decode(bits)))
+
+
+# ------------------------------------------------------------------ 8-bit A stored K x M (8-bit transpose reads)
+
+EIGHT_BIT_SHAPES = [(304, 272, 1088), (256, 512, 1024), (16, 16, 64), (528, 48, 192)]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", EIGHT_BIT_SHAPES)
+def test_at_fp8_bit_exact(oracle_mod, layout, M, N, K):
+    # e4m3 integers in [-4, 4] and power-of-two scales: exact sums, one RNE
+    say("case at fp8 exact", layout, M, N, K)
+    inp = W.int_inputs(M, N, K, "e4m3", seed=M + 7 * N + K)
+    A_km = np.ascontiguousarray(inp.A.T)
+    B = np.ascontiguousarray(inp.B.T) if layout == "at_bn" else inp.B
+    bits, info = run_gemm(A_km, B, M, N, K, "e4m3", "bf16", layout, scale=(0.5, 0.25), return_plan_info=True)
+    assert info["tile_m"] == 256
+    C, _ = oracle_mod.gemm_at(A_km, B, dtype="e4m3", sigma=oracle_mod.sigma_of(0.5, 0.25), want_s=False,
+                              b_kn=layout == "at_bn")
+    _exact(oracle_mod, bits, "bf16", C)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", EIGHT_BIT_SHAPES)
+def test_at_int8_bit_exact(oracle_mod, layout, M, N, K):
+    # full-range int8 with sums of |a b| below 2^24: exact int32 sums, one RNE
+    say("case at int8 exact", layout, M, N, K)
+    inp = W.int_inputs(M, N, K, "i8", seed=M + 11 * N + K, lo=-128, hi=127)
+    A_km = np.ascontiguousarray(inp.A.T)
+    B = np.ascontiguousarray(inp.B.T) if layout == "at_bn" else inp.B
+    bits = run_gemm(A_km, B, M, N, K, "i8", "bf16", layout)
+    acc, S = oracle_mod.gemm_bt_int(inp.A, inp.B, K, "i8")
+    assert S.max() < 2.0 ** 24
+    _exact(oracle_mod, bits, "bf16", acc)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_at_fp8_random_4096_sampled(oracle_mod, layout):
+    M = N = K = 4096
+    say("case at fp8 random", layout, M, N, K)
+    inp = W.make_inputs(W.WORKLOADS["e4m3_8192"], M=M, N=N, K=K, seed=71)
+    A_km = np.ascontiguousarray(inp.A.T)
+    B = np.ascontiguousarray(inp.B.T) if layout == "at_bn" else inp.B
+    bits = run_gemm(A_km, B, M, N, K, "e4m3", "bf16", layout, scale=(inp.scale_a, inp.scale_b))
+    rows, cols = sample_entries(M, N, 8192, seed=72)
+    sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+    C, S = oracle_mod.gemm_at_entries(A_km, B, rows, cols, dtype="e4m3", sigma=sigma, b_kn=layout == "at_bn")
+    r = assert_within_bound(decode(bits[rows, cols]), C, S, "e4m3", "at fp8 %s 4096^3" % layout)
+    say("  worst err/bound", r)
+    assert np.all(np.isfinite(decode(bits)))

@@ -374,10 +374,19 @@ def test_at_layout_plans(lib):
                     want_b = ((K, 2 * N), (2 * N, 1)) if b_kn else ((N, 2 * K), (2 * K, 1))
                     assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == want_b
                     assert tg.gemm_preshuffled_b_bytes(p.handle) == (0 if b_kn else N * K * 2)
-        for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_I8_OUT_BF16):
-            with pytest.raises(tg.GemmError, match="bf16"):
+        # 8-bit A stored K x M: the same kernel, 8-bit transpose reads
+        for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_I8_OUT_BF16):
+            for M, N, K in [(4096, 4096, 4096), (304, 272, 1088), (16, 16, 64)]:
+                with tg.Plan(M, N, K, dtype, layout) as p:
+                    info = p.info()
+                    assert (info["kernel"], info["tile_m"], info["threads"]) == (0, 256, 512)
+                    assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_A) == ((K, M), (M, 1))
+            with pytest.raises(tg.GemmError, match="16-byte"):
+                tg.Plan(296, 256, 256, dtype, layout)                     # M bytes % 16
+        for dtype in (tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_W4A8_OUT_BF16):
+            with pytest.raises(tg.GemmError, match="bf16, fp8 e4m3 and int8"):
                 tg.Plan(256, 256, 256, dtype, layout)
-        with pytest.raises(tg.GemmError, match="multiple of 8"):
+        with pytest.raises(tg.GemmError, match="16-byte"):
             tg.Plan(300, 256, 256, tg.GEMM_BF16_OUT_BF16, layout)        # M % 8
         with pytest.raises(tg.GemmError, match="2\\^31"):
             tg.Plan(1 << 16, 256, 1 << 14, tg.GEMM_BF16_OUT_BF16, layout)

@@ -368,8 +368,8 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     const bool b_kn = layout == GEMM_LAYOUT_BN || layout == GEMM_LAYOUT_AT_BN;
     const bool a_km = layout == GEMM_LAYOUT_AT || layout == GEMM_LAYOUT_AT_BN;
     const bool bf16_in = dtype == GEMM_BF16_OUT_F32 || dtype == GEMM_BF16_OUT_BF16;
-    if (a_km && !bf16_in) {
-        fail(GEMM_ERR_UNSUPPORTED, "A stored K x M is supported for bf16 inputs");
+    if (a_km && !bf16_in && dtype != GEMM_E4M3_OUT_BF16 && dtype != GEMM_I8_OUT_BF16) {
+        fail(GEMM_ERR_UNSUPPORTED, "A stored K x M is supported for bf16, fp8 e4m3 and int8 inputs");
         return nullptr;
     }
     if (b_kn && !bf16_in && dtype != GEMM_E4M3_OUT_BF16 && dtype != GEMM_I8_OUT_BF16) {
@@ -422,12 +422,12 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "B stored K x N must stay below 2^31 bytes (32-bit offsets)");
         return nullptr;
     }
-    if (a_km && K * M * 2 >= (int64_t(1) << 31)) {
+    if (a_km && K * M * (ebits / 8) >= (int64_t(1) << 31)) {
         fail(GEMM_ERR_UNSUPPORTED, "A stored K x M must stay below 2^31 bytes (32-bit offsets)");
         return nullptr;
     }
-    if (a_km && M % 8 != 0) {
-        fail(GEMM_ERR_UNSUPPORTED, "M=%lld must be a multiple of 8 for A stored K x M", (long long)M);
+    if (a_km && (M * (ebits / 8)) % 16 != 0) {
+        fail(GEMM_ERR_UNSUPPORTED, "M=%lld must make the K-rows of A (K x M) whole 16-byte pieces", (long long)M);
         return nullptr;
     }
     if (is_mx(dtype)) {

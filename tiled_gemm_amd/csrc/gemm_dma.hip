@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     static_assert(!BKN || !BPRE, "K x N B is not pre-shuffled");
     // AKM: A stored K x M, staged and read the same way (64 K-rows of the
     // tile's 256 rows of C per step).
-    static_assert(!AKM || (ELEM == kBf16 && !BPRE), "K x M A: bf16");
+    static_assert(!AKM || !BPRE, "K x M A with a plain B");
     // fp8: one 128-byte K slice per step and MFMA (16x16x128, 32 bytes per
     // lane: chunks q and q + 4 of the slice); bf16: two 64-byte halves.
     // int8 shares the fp8 staging and fragments (8-bit elements); each 32-byte
@@ -104,9 +104,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     const uint32_t lda = (uint32_t)p.lda_bytes;
     // A split starts its operands' resources at its first K step (kAStep /
     // kBStep bytes per step, below), so every step index is split-relative.
-    const uint32_t shA = (uint32_t)sk.kt0 * (AKM ? 64u * lda : (uint32_t)kTileKBytes);
-    const auto rA = AKM ? make_rsrc((const uint8_t *)p.A + (size_t)m0 * 2 + shA,
-                                    (uint32_t)((size_t)p.K * lda - (size_t)m0 * 2 - shA))
+    // K x M A (like K x N B): per step 64 K-rows of 2-byte elements or 128 of
+    // 1-byte ones, the tile's 256 rows of C each.
+    constexpr int EA = F8 ? 1 : 2;                       // bytes per element of A
+    const uint32_t shA = (uint32_t)sk.kt0 * (AKM ? (uint32_t)KN_ROWS * lda : (uint32_t)kTileKBytes);
+    const auto rA = AKM ? make_rsrc((const uint8_t *)p.A + (size_t)m0 * EA + shA,
+                                    (uint32_t)((size_t)p.K * lda - (size_t)m0 * EA - shA))
                         : make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb + shA, (uint32_t)rows_a * kb - shA);
     // K x N B: the resource starts at column n0 and ends with the matrix, so
     // K-rows past K read zeros; columns past N read neighbouring data or
@@ -131,8 +134,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     for (int r = 0; r < AR; ++r) {
         const int pc = (r * WAVES + w) * 64 + l;
         if constexpr (AKM) {
-            const int row = pc >> 5;                    // 32 chunks per K-row
-            const int c = (pc & 31) ^ bkn_swz(row);
+            const int row = pc / KN_CPR;                // 32 (2-byte) or 16 (1-byte) chunks per K-row
+            const int c = (pc % KN_CPR) ^ kn_swz(row);
             voffA[r] = (uint32_t)row * lda + (uint32_t)c * kChunkBytes;
             tailA |= 1u << r;                           // rows past K are out of range
         } else {
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
             tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
         }
     }
-    const uint32_t kAStep = AKM ? 64u * lda : (uint32_t)kTileKBytes;   // bytes of A per step
+    const uint32_t kAStep = AKM ? (uint32_t)KN_ROWS * lda : (uint32_t)kTileKBytes;   // bytes of A per step
     // bytes of B per step: pre-shuffled image 2 KiB per block row, N x K 128
     // per row, K x N 64 K-rows
     const uint32_t kBStep = BKN ? (uint32_t)KN_ROWS * ldb : (BPRE ? 2048u : (uint32_t)kTileKBytes);
@@ -213,6 +216,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
             t2[t] = lds_read_tr16(sA + k * 512 + ((c ^ bkn_swz(k)) << 4) + off);
         }
         return u32x4{t2[0].x, t2[0].y, t2[1].x, t2[1].y};
+    };
+    // 8-bit K x M A: the 32-byte operand of row block g as four 8-bit
+    // transpose reads, K positions as in bkn8_frag (the rows of C play the
+    // part of B's columns there).
+    auto akm8_frag = [&](int s, int g) -> i32x8 {
+        const uint8_t *sA = lds + s * DM_STAGE;
+        const int e = r16 >> 1, b = r16 & 1;
+        const int rb = wm * WTM + (g % FM) * 16 + 8 * b;        // this lane's 8 source rows of C
+        const int c = rb >> 4, off = rb & 15;
+        u32x2 t4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = (t >> 1) * 64 + 16 * q + 8 * (t & 1) + e;
+            t4[t] = lds_read_tr8(sA + k * 256 + ((c ^ bkn8_swz(k)) << 4) + off);
+        }
+        return i32x8{(int)t4[0].x, (int)t4[0].y, (int)t4[1].x, (int)t4[1].y,
+                     (int)t4[2].x, (int)t4[2].y, (int)t4[3].x, (int)t4[3].y};
     };
     auto a_addr = [&](int s, int g, int h) -> const uint8_t * {
         const int i = g % FM;
@@ -280,7 +300,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
                         fb[s][j] = join32(lds_load16(b_addr(s, 0, j)), lds_load16(b_addr(s, 1, j)));
                 }
             }
-            fa[t] = join32(lds_load16(a_addr(s, t, 0)), lds_load16(a_addr(s, t, 1)));
+            if constexpr (AKM)
+                fa[t] = akm8_frag(s, t);
+            else
+                fa[t] = join32(lds_load16(a_addr(s, t, 0)), lds_load16(a_addr(s, t, 1)));
         } else {
             if (t % FM == 0) {
 #pragma unroll
@@ -417,6 +440,9 @@ static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
     TiledVariant{DM_BM, DM_BN, WGM, WGN, ELEM, kOutBf16, false, DM_LDS, 2,                              \
                  &launch_dma<ELEM, kOutBf16, false, WGM, WGN, PD, true, false>, true, false}
 #define TG_DMA_KN8(WGM, WGN, PD) TG_DMA_KN8E(kFp8, WGM, WGN, PD)
+#define TG_DMA_AT8(ELEM, BKN)                                                                      \
+    TiledVariant{DM_BM, DM_BN, 1, 8, ELEM, kOutBf16, false, DM_LDS, 2,                                  \
+                 &launch_dma<ELEM, kOutBf16, false, 1, 8, 2, BKN, true>, BKN, true}
 
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
@@ -446,6 +472,11 @@ static const TiledVariant kDma[] = {
     TG_DMA_L(kOutBf16, 2, 4, 3, true, true),
     TG_DMA_KN(kOutBf16, 2, 4, 3),              // 21: B K x N
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 22: B N x K
+    // 8-bit A stored K x M (8-bit transpose reads on both operands)
+    TG_DMA_AT8(kFp8, false),                   // 23: fp8, A K x M, B N x K
+    TG_DMA_AT8(kFp8, true),                    //     fp8, A K x M, B K x N
+    TG_DMA_AT8(kI8, false),                    // 25: int8, A K x M, B N x K
+    TG_DMA_AT8(kI8, true),                     //     int8, A K x M, B K x N
 };
 
 const TiledVariant *dma_variants(int *count)
