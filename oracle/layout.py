@@ -123,3 +123,28 @@ def bscale_image(S: np.ndarray, K: int) -> np.ndarray:
                         if blk < kb:
                             img[quad, g, lane, b, s] = S[row, blk]
     return img.reshape(-1)
+
+
+def bscale_image_32(S: np.ndarray, K: int) -> np.ndarray:
+    """Block-scale image, form 1 (the 32x32x64 MFMA's lane order): the same
+    (ceil(R/64), G, 64, 4, 4) bytes, where entry (quad, g, lane, w, b) is
+    S[64 quad + 32 (w // 2) + lane % 32][16 g + 2 (2 b + w % 2) + lane // 32],
+    or 127 past the rows or the blocks.  Written out index by index."""
+    S = np.asarray(S, np.uint8)
+    R, kb = S.shape
+    assert kb == K // 32
+    groups = ((K + 127) // 128 + 3) // 4
+    quads = (R + 63) // 64
+    img = np.full((quads, groups, 64, 4, 4), 127, np.uint8)
+    for quad in range(quads):
+        for g in range(groups):
+            for lane in range(64):
+                for w in range(4):
+                    row = 64 * quad + 32 * (w // 2) + lane % 32
+                    if row >= R:
+                        continue
+                    for b in range(4):
+                        blk = 16 * g + 2 * (2 * b + w % 2) + lane // 32
+                        if blk < kb:
+                            img[quad, g, lane, w, b] = S[row, blk]
+    return img.reshape(-1)

@@ -258,20 +258,29 @@ def test_epilogue_enum_matches_header():
 
 @pytest.mark.parametrize("dtype,bits", [(tg.GEMM_MXFP8_OUT_BF16, 8), (tg.GEMM_MXFP4_OUT_BF16, 4)])
 @pytest.mark.parametrize("layout", [tg.GEMM_LAYOUT_BT, tg.GEMM_LAYOUT_BT_PRESHUFFLED])
-def test_mx_plans(lib, dtype, bits, layout):
+def test_mx_plans(lib, monkeypatch, dtype, bits, layout):
     for M, N, K in [(8192, 8192, 8192), (32, 4096, 1024), (300, 272, 1152)]:
         with tg.Plan(M, N, K, dtype, layout) as p:
             info = p.info()
             if M <= 64 and layout == tg.GEMM_LAYOUT_BT_PRESHUFFLED:      # decode: the skinny kernel
                 assert info["kernel"] == 1 and info["tile_n"] == 32
-            else:
+                assert info["scale_form"] == 0
+            elif bits == 8:
                 assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 256   # 4-wave pipelined
+                assert info["scale_form"] == 0
+            else:                            # MXFP4 tiles: the 32x32x64 kernel, image form 1
+                assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] in (256, 512)
+                assert info["scale_form"] == 1
             assert info["elem_bits"] == bits and info["elem_bytes"] == bits // 8
             assert tg.gemm_preshuffled_b_bytes(p.handle) == N * K * bits // 8
             groups = ((K + 127) // 128 + 3) // 4
             assert p.bscale_image_bytes(0) == (M + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(1) == (N + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(2) == 0
+    monkeypatch.setenv("TGEMM_MX4W", "0")             # the 16x16x128 kernel reads form 0
+    with tg.Plan(300, 272, 1152, dtype, layout) as p:
+        assert p.info()["threads"] == 256 and p.info()["scale_form"] == 0
+    monkeypatch.delenv("TGEMM_MX4W")
     with pytest.raises(tg.GemmError, match="2\\^31"):
         tg.Plan(64, 1 << 21, 1 << 16, dtype, layout)    # block-scale image past 32-bit offsets
     with tg.Plan(64, 1 << 20, 1 << 14, dtype, layout) as p:

@@ -50,6 +50,25 @@ def test_bscale_image_byte_exact(R, K):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("R,K", [(200, 1152), (513, 4096)])
+def test_bscale_image_form1_byte_exact(R, K):
+    # MXFP4 on 256 x 256 tiles runs the 32x32x64 kernel, whose plan writes form 1.
+    say("case bscale image form 1", R, K)
+    rng = np.random.default_rng(R * K)
+    S = rng.integers(0, 255, (R, K // 32)).astype(np.uint8)
+    with tg.Plan(R, 512, K, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED) as p:
+        assert p.info()["scale_form"] == 1 and p.info()["tile_m"] == 256
+        n = p.bscale_image_bytes(0)
+        src = torch.from_numpy(S).cuda()
+        img = torch.full((n,), 0xEE, dtype=torch.uint8, device="cuda")
+        p.preshuffle_bscale(0, src.data_ptr(), img.data_ptr())
+        torch.cuda.synchronize()
+        got = img.cpu().numpy()
+    want = OL.bscale_image_32(S, K)
+    assert got.size == want.size
+    assert np.array_equal(got, want)
+
+
 def _k_for(fmt, ragged):
     # ragged: K bytes an odd multiple of 64, so the last 128-byte step is half full
     if fmt == "mxfp8":

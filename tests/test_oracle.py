@@ -420,6 +420,40 @@ def test_bscale_image_hand_computed_entries():
     assert img[1, 0, 6, 0, 0] == 127 and img[1, 0, 5, 0, 0] == S[69, 0]
 
 
+def test_bscale_image_32_consumer_view():
+    # Form 1 from the reader's side: lane l of the 32x32x64 MFMA, row half u
+    # of a quad and 64-element slice s' (0..7) of a 512-element group needs
+    # the scale of row 32 u + l % 32 for K block 2 s' + l // 32, and reads it
+    # from word 2 u + s' % 2, byte s' // 2 of its 16 bytes.  R = 100 rows and
+    # K = 640 (20 blocks, 2 groups, the second one partial): every in-range
+    # scale appears exactly once and the rest is the unit scale 127.
+    R, K = 100, 640
+    S = (np.arange(R * (K // 32)) * 7 % 251).astype(np.uint8).reshape(R, K // 32)
+    img = L.bscale_image_32(S, K).reshape(2, 2, 64, 4, 4)
+    seen = np.zeros(img.shape, bool)
+    for quad in range(2):
+        for g in range(2):
+            for lane in range(64):
+                for u in range(2):
+                    for sp in range(8):
+                        row = 64 * quad + 32 * u + lane % 32
+                        blk = 16 * g + 2 * sp + lane // 32
+                        pos = (quad, g, lane, 2 * u + sp % 2, sp // 2)
+                        seen[pos] = True
+                        want = S[row, blk] if row < R and blk < K // 32 else 127
+                        assert img[pos] == want, (pos, row, blk)
+    assert seen.all()
+    # hand-computed: quad 1, group 1, lane 37 (row 5 of the half, K half 1),
+    # word 3 (half 1, odd slice), byte 2 -> slice 5: row 64 + 32 + 5 = 101 is
+    # past R; lane 37 of word 1 instead: row 69, block 16 + 10 + 1 = 27 past K;
+    # byte 0 of word 1 -> slice 1: block 16 + 2 + 1 = 19
+    assert img[1, 1, 37, 3, 2] == 127
+    assert img[1, 1, 37, 1, 2] == 127
+    assert img[1, 1, 37, 1, 0] == S[69, 19]
+    # the two forms hold the same bytes, permuted
+    assert np.array_equal(np.sort(img.reshape(-1)), np.sort(L.bscale_image(S, K)))
+
+
 # ---------------------------------------------------------------------------
 # Integer operands (int8 A; int8 or packed int4 B)
 # ---------------------------------------------------------------------------

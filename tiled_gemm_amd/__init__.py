@@ -69,7 +69,7 @@ class gemm_plan_info(ctypes.Structure):
         (f, ctypes.c_int32) for f in (
             "dtype", "layout", "elem_bytes", "out_bytes", "kernel", "tile_m", "tile_n",
             "tile_k_bytes", "threads", "lds_stages", "lds_bytes", "grid", "tiles_m", "tiles_n",
-            "group_m", "split_k", "elem_bits", "b_elem_bits", "ws_splits", "ws_grid")]
+            "group_m", "split_k", "elem_bits", "b_elem_bits", "ws_splits", "ws_grid", "scale_form")]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -35,6 +35,15 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// The plan's tile kernel is the 32x32x64 MXFP4 one, which reads block-scale
+// image form 1.
+bool wide_scales(const gemm_plan *p)
+{
+    int n = 0;
+    const tg::TiledVariant *x = tg::mx4w_variants(&n);
+    return p->info.kernel == 0 && p->tiled && p->tiled >= x && p->tiled < x + n;
+}
+
 int fail(int code, const char *fmt, ...)
 {
     char buf[512];
@@ -124,6 +133,22 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
         // to n-wave variants.
         const char *ew = getenv("TGEMM_PIPE_WAVES");
         const int waves = ew ? atoi(ew) : 0;
+        // MXFP4 runs on the 32x32x64 kernel (twice the e2m1 rate of the
+        // 16x16x128 form) unless TGEMM_MX4W=0; TGEMM_MX4W_VARIANT=<index>
+        // picks one of its sweep variants.
+        const char *e4 = getenv("TGEMM_MX4W");
+        if (elem == tg::kMx4 && !(e4 && e4[0] == '0')) {
+            int nw = 0;
+            const tg::TiledVariant *x = tg::mx4w_variants(&nw);
+            if (const char *ev = getenv("TGEMM_MX4W_VARIANT")) {
+                const int k = atoi(ev);
+                if (k >= 0 && k < nw && x[k].preshuffled == pre)
+                    return &x[k];
+            }
+            for (int i = 0; i < nw; ++i)
+                if (x[i].preshuffled == pre && (waves == 0 || x[i].wgm * x[i].wgn == waves))
+                    return &x[i];
+        }
         int nb = 0;
         const tg::TiledVariant *b = tg::pipe_variants(&nb);
         for (int i = 0; i < nb; ++i)
@@ -510,6 +535,7 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     plan_split(p);
     I.ws_splits = p->splits;
     I.ws_grid = p->splits > 1 ? p->split_grid : I.grid;
+    I.scale_form = wide_scales(p) ? 1 : 0;
     ok();
     return p;
 }
@@ -912,6 +938,7 @@ int gemm_preshuffle_bscale(const gemm_plan *plan, int operand, const void *scale
     a.kblocks = (int32_t)(plan->info.K / 32);
     a.groups = (int32_t)scale_groups(plan->info.K);
     a.quads = (int32_t)((rows + 63) / 64);
+    a.form = plan->info.scale_form;
     const hipError_t e = tg::launch_bscale_image(a, stream);
     if (e != hipSuccess)
         return fail(GEMM_ERR_HIP, "block-scale image launch: %s", hipGetErrorString(e));

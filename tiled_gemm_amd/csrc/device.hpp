@@ -17,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -41,6 +42,11 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+__device__ inline uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
 // Compiler-only memory fence: keeps the loads issued before it ahead of the
@@ -172,6 +178,29 @@ __device__ inline void mfma_mx4_a(f32x4 &acc, u32x4 x, u32x4 y, uint32_t sx, uin
 }
 #undef TG_MX_ASM
 
+// The 32x32x64 form for e2m1 operands (4 VGPRs each), accumulator in AGPRs:
+// D[32 x 32] += (X * 2^(sx - 127)) * (Y * 2^(sy - 127))^T.  Lane l feeds row
+// l % 32 of its operand with elements 32 (l / 32) .. +31 of the 64-element
+// slice (16 bytes), and its scale byte covers those 32 elements.  Lane l
+// receives D[8 u + 4 (l / 32) + j][l % 32] in accumulator element 4 u + j.
+#define TG_MX32_ASM(LO, HI)                                                                     \
+    "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #LO "," #LO ",0] "     \
+    "op_sel_hi:[" #HI "," #HI ",0] cbsz:4 blgp:4"
+template <int BYTE>
+__device__ inline void mfma_mx4w_a(f32x16 &acc, u32x4 x, u32x4 y, uint32_t sx, uint32_t sy)
+{
+    static_assert(BYTE >= 0 && BYTE < 4, "scale byte");
+    if constexpr (BYTE == 0)
+        asm volatile(TG_MX32_ASM(0, 0) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 1)
+        asm volatile(TG_MX32_ASM(1, 0) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 2)
+        asm volatile(TG_MX32_ASM(0, 1) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else
+        asm volatile(TG_MX32_ASM(1, 1) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+}
+#undef TG_MX32_ASM
+
 // int8 atom: D += X * Y^T over 64 int8 values per row (16 bytes per lane, the
 // same lane / K slot assignment as the bf16 atom), int32 sums.  The
 // accumulator travels as f32x4 storage holding the int32 bits, so the
@@ -229,6 +258,17 @@ __device__ inline void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_no
 // reads above it, right behind the MFMA that is still writing them.
 template <int FM, int FN>
 __device__ inline void mfma_drain_acc(f32x4 (&acc)[FM][FN])
+{
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            asm volatile("" : "+a"(acc[i][j]));
+}
+
+template <int FM, int FN>
+__device__ inline void mfma_drain_acc(f32x16 (&acc)[FM][FN])
 {
     mfma_drain();
 #pragma unroll

@@ -1,0 +1,350 @@
+// MXFP4 GEMM C = A * B^T on the 32x32x64 form of gfx950's scaled MFMA,
+// 256 x 256 tiles (FlyDSL "Kernel Authoring" skill, section 6 "GEMM Pattern
+// (Preshuffle)": B pre-shuffled into operand order, A staged through
+// XOR-swizzled LDS, LDS ping-pong; section 3 "Runtime Loops with
+// Loop-Carried Values" for the load-next / compute-current loop; the "FlyDSL
+// Kernel authoring guide", section 4.3 "ROCm intrinsics", for the f8f6f4
+// scaled MFMA family and its E8M0 block scales).
+//
+// Why a second MXFP4 kernel: e2m1 operands run at twice the e4m3 rate only in
+// the 32x32x64 shape (the 16x16x128 shape is capped near the e4m3 rate; an
+// independent-accumulator microbenchmark on every CU measured 7.3 against
+// 4.7 PFLOP/s).  Per 64-element K slice a lane feeds one 16-byte operand of
+// row l % 32, elements 32 (l / 32) .. +31, and one scale byte for them.
+//
+// Workgroup: WAVES waves side by side along N; wave w owns all 256 rows and
+// the WN = 256 / WAVES columns from WN w (JB = WN / 32 blocks of 32), i.e.
+// 8 x JB accumulators of 32 x 32 in AGPRs.  Main-loop step: 128 bytes of K
+// (256 elements, four 64-element slices).
+//
+//   A   global -> LDS by loads that write LDS directly, ring of 4 stages of
+//       32 KiB (rows of 128 bytes, 16-byte chunks XOR-swizzled); a fragment
+//       is one 16-byte LDS read (row 32 i + l % 32, chunk 2 s + l / 32).
+//   B   global -> VGPRs, 4 JB 16-byte loads per lane and step, issued one
+//       step ahead into two register sets renamed by unrolling.  From the
+//       pre-shuffled image, lane l of column block J and slice s reads
+//       16-row block n / 16, k-block 2 kt + s / 2, quarter 2 (s % 2) + l / 32,
+//       row n % 16 (n = WN w + 32 J + l % 32): two 512-byte runs per wave load.
+//   Scales from block-scale image form 1 (one record of 1 KiB per 64-row
+//       quad and 512-element group): lane l's 16 bytes hold, in word 2 u + par,
+//       byte b, the scale of row 32 u + l % 32 of the quad for K block
+//       2 s' + l / 32 of slice s' = 2 b + par.  One 16-byte load per quad and
+//       group brings a lane every scale it feeds; op_sel picks the byte.
+//   Sync  one barrier per step, PD groups before its end, after an exact vmcnt
+//       wait for A's next stage; every load is issued unconditionally (steps
+//       past the end read out of range and return zeros, whose products are
+//       zero whatever the scale).
+//   Epilogue (acc * s_a) * s_b (+ bias, activation) in fp32, RNE to bf16.
+#include "device.hpp"
+#include "kernels.hpp"
+
+#include <type_traits>
+
+namespace tg {
+
+namespace {
+
+constexpr int W4_BM = 256;
+constexpr int W4_BN = 256;
+constexpr int W4_NS = 4;                                   // LDS stages of A
+constexpr int W4_STAGE = W4_BM * kTileKBytes;              // 32 KiB
+constexpr int W4_NG = 32;                                  // groups per step: (row block, slice)
+
+template <int N>
+using xc = std::integral_constant<int, N>;
+
+// The scaled MFMA with scale byte `byte` (a constant once the loops unroll).
+__device__ inline void mx4w(f32x16 &acc, u32x4 x, u32x4 y, uint32_t sx, uint32_t sy, int byte)
+{
+    switch (byte) {
+    case 0: mfma_mx4w_a<0>(acc, x, y, sx, sy); break;
+    case 1: mfma_mx4w_a<1>(acc, x, y, sx, sy); break;
+    case 2: mfma_mx4w_a<2>(acc, x, y, sx, sy); break;
+    default: mfma_mx4w_a<3>(acc, x, y, sx, sy); break;
+    }
+}
+
+}  // namespace
+
+template <bool BPRE, int WAVES, int PD>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArgs p)
+{
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int WN = W4_BN / WAVES;                      // columns per wave
+    constexpr int JB = WN / 32;                            // 32-column blocks per wave
+    constexpr int AR = W4_STAGE / (THREADS * kChunkBytes); // A loads per lane and step
+    constexpr int BR = 4 * JB;                             // B loads per lane and step
+    constexpr int SL = 5;                                  // scale loads per group
+    static_assert(JB >= 1 && WN % 32 == 0, "whole 32-column blocks per wave");
+    static_assert(PD >= 1 && PD < W4_NG / 2, "prefetch distance");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W4_NS * W4_STAGE];
+
+    const int w = wave_id();
+    const int l = lane_id();
+    const int r32 = l & 31, g = l >> 5;
+
+    const SplitK sk = split_k_of(p);
+    int tm, tn;
+    tile_of_wg(sk.wg, sk.grid, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const int m0 = tm * W4_BM, n0 = tn * W4_BN;
+    const int rows_a = min(p.M - m0, W4_BM);
+    const int rows_b = min(p.N - n0, W4_BN);
+    const uint32_t kb = (uint32_t)p.kbytes;
+    const uint32_t kbB = (uint32_t)p.kbytes_b;
+    const auto rA = make_rsrc((const uint8_t *)p.A + (size_t)m0 * kb, (uint32_t)rows_a * kb);
+    const auto rB = make_rsrc((const uint8_t *)p.B + (size_t)n0 * kbB, (uint32_t)rows_b * kbB);
+    const int nk = sk.nk;
+    const uint32_t tail = sk.tail;
+
+    // ---- A: load r of a step lands at byte (r * WAVES + w) * 1024 + 16 l of
+    // the stage, i.e. row pc / 8, physical chunk pc % 8; the lane fetches
+    // logical chunk swz_chunk(row, pc % 8).
+    uint32_t voffA[AR];
+    uint32_t tailA = 0;
+#pragma unroll
+    for (int r = 0; r < AR; ++r) {
+        const int pc = (r * WAVES + w) * 64 + l;
+        const int row = pc >> 3;
+        const int c = swz_chunk(row, pc & 7);
+        voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
+        tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
+    }
+    // ---- B: load b = 4 J + s brings chunk 2 s + g of column WN w + 32 J + r32.
+    uint32_t voffB[BR];
+    uint32_t tailB = 0;
+#pragma unroll
+    for (int b = 0; b < BR; ++b) {
+        const int J = b >> 2, s = b & 3;
+        const int n = WN * w + 32 * J + r32;
+        const int c = 2 * s + g;
+        if constexpr (BPRE)
+            voffB[b] = (uint32_t)(n >> 4) * 16u * kbB + (uint32_t)(s >> 1) * 1024u +
+                       (uint32_t)((2 * (s & 1) + g) * 16 + (n & 15)) * 16u;
+        else
+            voffB[b] = (uint32_t)n * kbB + (uint32_t)c * kChunkBytes;
+        tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << b;
+    }
+    constexpr uint32_t kBStep = BPRE ? 2048u : (uint32_t)kTileKBytes;
+
+    // MASK false: the caller guarantees tile kt is whole and in range.
+    auto issue_a_one = [&](int kt, int r, auto mask_c) {
+        uint32_t vo = voffA[r];
+        if constexpr (decltype(mask_c)::value) {
+            const bool beyond = kt >= nk;
+            const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+            vo = keep_or_oob(!beyond & (!part | (((tailA >> r) & 1u) != 0)), vo);
+        }
+        buf_load16_to_lds(rA, lds + (kt % W4_NS) * W4_STAGE + (r * WAVES + w) * 1024, vo,
+                          (uint32_t)kt * kTileKBytes);
+        issue_fence();
+    };
+    u32x4 bq[2][BR];
+    auto issue_b_one = [&](int kt, auto set_c, int b, auto mask_c) {
+        constexpr int S = decltype(set_c)::value;
+        uint32_t vo = voffB[b];
+        if constexpr (decltype(mask_c)::value) {
+            const bool beyond = kt >= nk;
+            const bool part = (kt == nk - 1) && tail != (uint32_t)kTileKBytes;
+            vo = keep_or_oob(!beyond & (!part | (((tailB >> b) & 1u) != 0)), vo);
+        }
+        bq[S][b] = buf_load16(rB, vo, (uint32_t)kt * kBStep);
+        issue_fence();
+    };
+
+    // ---- block scales of one group (two steps), from image form 1: one
+    // 16-byte record slot per lane and quad, word 2 u + par for row half u and
+    // slice parity par, byte s' / 2 for slice s' of the group.  A: the four
+    // quads of the tile's rows; B: the quad of the wave's columns.
+    const int G = p.s_groups;
+    const auto rSA = make_rsrc(p.sa_img, (uint32_t)((p.M + 63) / 64) * (uint32_t)G * 1024u);
+    const auto rSB = make_rsrc(p.sb_img, (uint32_t)((p.N + 63) / 64) * (uint32_t)G * 1024u);
+    const uint32_t qb = (uint32_t)((n0 + WN * w) / 64);
+    const int ub0 = ((WN * w) >> 5) & 1;                  // row half of the quad of block J = 0
+    u32x4 scA[4], scA_n[4], scB, scB_n;
+    auto issue_scales = [&](int g2) {
+        const bool in = g2 < G;              // past the last group: out of range
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q)
+            scA_n[Q] = buf_load16(
+                rSA, keep_or_oob(in, ((uint32_t)(m0 / 64 + Q) * (uint32_t)G + (uint32_t)g2) * 1024u + (uint32_t)l * 16u),
+                0);
+        scB_n = buf_load16(rSB, keep_or_oob(in, (qb * (uint32_t)G + (uint32_t)g2) * 1024u + (uint32_t)l * 16u), 0);
+        issue_fence();
+    };
+
+    f32x16 acc[8][JB];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int J = 0; J < JB; ++J)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[i][J][v] = 0.f;
+
+    // ---- fragments: group t of a step = (row block t % 8, slice t / 8).
+    u32x4 fa[W4_NG];
+    auto load_frag = [&](int stage, int t) {
+        const int i = t & 7, s = t >> 3;
+        const int row = 32 * i + r32;
+        fa[t] = lds_load16(lds + stage * W4_STAGE + row * kTileKBytes + swz_chunk(row, 2 * s + g) * kChunkBytes);
+    };
+
+    // Load issue order per step k: the next group's scales at the start of
+    // its first step (k even), B(k+1) spread over the groups before the
+    // barrier, A(k+3) over the groups after it.  At the start of step k, B(k)
+    // needs every load issued after it done except A(k+2): vmcnt(AR).  At
+    // barrier(k), A(k+1) has two B steps, one A step and one group of
+    // scales behind it.
+    constexpr int kVmStart = AR;
+    constexpr int kVmBar = 2 * BR + AR + SL;
+    static_assert(kVmBar < 64, "vmcnt is 6 bits");
+    auto wait_vm = [&](auto n_c) {
+        constexpr int n = decltype(n_c)::value;
+        __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | (n & 0xF) | ((n >> 4) << 14));
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // One step; CUR: its B register set, GP: its position in the scale group.
+    auto step = [&](int kt, auto cur_c, auto gp_c, auto mask_c) {
+        constexpr int CUR = decltype(cur_c)::value;
+        constexpr int GP = decltype(gp_c)::value;
+        const int st = kt % W4_NS;
+        wait_vm(xc<kVmStart>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GP == 0) {
+#pragma unroll
+            for (int Q = 0; Q < 4; ++Q)
+                scA[Q] = scA_n[Q];
+            scB = scB_n;
+            issue_scales(kt / 2 + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < W4_NG; ++t) {
+            if (t < W4_NG - PD) {
+#pragma unroll
+                for (int b = t * BR / (W4_NG - PD); b < (t + 1) * BR / (W4_NG - PD); ++b)
+                    issue_b_one(kt + 1, xc<1 - CUR>{}, b, mask_c);
+            } else {
+                const int go = t - (W4_NG - PD);
+                if (go == 0) {
+                    wait_vm(xc<kVmBar>{});
+                    barrier();
+                }
+#pragma unroll
+                for (int r = go * AR / PD; r < (go + 1) * AR / PD; ++r)
+                    issue_a_one(kt + W4_NS - 1, r, mask_c);
+            }
+            if (t + PD < W4_NG)
+                load_frag(st, t + PD);
+            else
+                load_frag((kt + 1) % W4_NS, t + PD - W4_NG);
+            const int i = t & 7, s = t >> 3;
+#pragma unroll
+            for (int J = 0; J < JB; ++J)
+                mx4w(acc[i][J], bq[CUR][4 * J + s], fa[t], scB[2 * (ub0 + J) + (s & 1)],
+                     scA[i >> 1][2 * (i & 1) + (s & 1)], 2 * GP + (s >> 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- prologue: group 0's scales, A tiles 0 .. NS-2 and B(0), then the
+    // first fragments.
+    using masked = std::true_type;
+    using unmasked = std::false_type;
+    issue_scales(0);
+    for (int v = 1 - W4_NS; v < 0; ++v) {
+        if (v == -1) {
+#pragma unroll
+            for (int b = 0; b < BR; ++b)
+                issue_b_one(0, xc<0>{}, b, masked{});
+        }
+#pragma unroll
+        for (int r = 0; r < AR; ++r)
+            issue_a_one(v + W4_NS - 1, r, masked{});
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 & ~0x0F00);      // vmcnt(0) lgkmcnt(0)
+    barrier();
+#pragma unroll
+    for (int t = 0; t < PD; ++t)
+        load_frag(0, t);
+    // Steps run in pairs (one scale group); a step past nk is a phantom on
+    // zeros.  A pair whose loads (B up to kt + 2, A up to kt + NS) all cover
+    // whole, in-range tiles runs without per-lane masks.
+    int kt = 0;
+    const int nfull = tail == (uint32_t)kTileKBytes ? nk : nk - 1;
+    for (; kt + W4_NS < nfull; kt += 2) {
+        step(kt, xc<0>{}, xc<0>{}, unmasked{});
+        step(kt + 1, xc<1>{}, xc<1>{}, unmasked{});
+    }
+    for (; kt < nk; kt += 2) {
+        step(kt, xc<0>{}, xc<0>{}, masked{});
+        step(kt + 1, xc<1>{}, xc<1>{}, masked{});
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    mfma_drain_acc(acc);
+
+    // ---- epilogue.  Lane l of block (i, J) holds C[32 i + r32][WN w + 32 J
+    // + 8 u + 4 g + j] in acc[i][J][4 u + j].  Row blocks outside, the lane's
+    // column runs inside, so a wave writes adjacent pieces of a C row back to
+    // back.
+    const EpiView ev = epi_view(p.epi, p.M, p.N);
+    const uint32_t ldc = (uint32_t)p.N * 2u;
+    const auto rC = make_rsrc((uint8_t *)sk.C + (size_t)m0 * ldc, (uint32_t)rows_a * ldc);
+    f32x4 sbv[JB][4], bzv[JB][4];
+#pragma unroll
+    for (int J = 0; J < JB; ++J)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int col = n0 + WN * w + 32 * J + 8 * u + 4 * g;
+            sbv[J][u] = epi_col_scale4(ev, col);
+            bzv[J][u] = epi_bias4(ev, col);
+        }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 32 * i + r32;
+        const float sa = epi_row_scale(ev, m0 + row);
+#pragma unroll
+        for (int J = 0; J < JB; ++J)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col = n0 + WN * w + 32 * J + 8 * u + 4 * g;
+                const uint32_t voff = col < p.N ? (uint32_t)row * ldc + (uint32_t)col * 2u : kOobOffset;
+                const f32x4 a = f32x4{acc[i][J][4 * u], acc[i][J][4 * u + 1], acc[i][J][4 * u + 2],
+                                      acc[i][J][4 * u + 3]};
+                const f32x4 v = epi_apply4(ev, a, sa, sbv[J][u], bzv[J][u]);
+                buf_store8(rC, u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)}, voff);
+            }
+    }
+}
+
+template <bool BPRE, int WAVES, int PD>
+static hipError_t launch_mx4w(const TiledArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_mx4w_kernel<BPRE, WAVES, PD>), dim3(a.grid), dim3(64 * WAVES), 0, s, a);
+    return hipGetLastError();
+}
+
+#define TG_MX4W(BPRE, WAVES, PD)                                                                  \
+    TiledVariant{W4_BM, W4_BN, 1, WAVES, kMx4, kOutBf16, BPRE, W4_NS * W4_STAGE, W4_NS,           \
+                 &launch_mx4w<BPRE, WAVES, PD>}
+
+// The first variant of each layout is the planner's choice; the rest are
+// alternatives selectable by index (TGEMM_MX4W_VARIANT).
+static const TiledVariant kMx4w[] = {
+    TG_MX4W(true, 8, 6),
+    TG_MX4W(false, 8, 6),
+    TG_MX4W(true, 8, 4),     // 2
+    TG_MX4W(true, 4, 6),     // 3: one wave per SIMD
+    TG_MX4W(false, 4, 6),
+};
+
+const TiledVariant *mx4w_variants(int *count)
+{
+    *count = (int)(sizeof(kMx4w) / sizeof(kMx4w[0]));
+    return kMx4w;
+}
+
+}  // namespace tg

@@ -79,6 +79,11 @@ struct BscaleArgs {
     int32_t kblocks;        // K / 32
     int32_t groups;         // G = ceil(ceil(K / 128) / 4)
     int32_t quads;          // ceil(R / 64)
+    // 0: the layout above.  1: the 32x32x64 MFMA's (MXFP4 tile kernel): word
+    // w of lane l, byte b holds row 64 quad + 32 (w / 2) + l % 32, K block
+    // 16 g + 2 (2 b + w % 2) + l / 32, so one 16-byte load per lane brings
+    // both 32-row halves of a quad for the 8 64-element slices of a group.
+    int32_t form;
 };
 
 struct SkinnyArgs {
@@ -136,6 +141,7 @@ const TiledVariant *tiled_variants(int *count);
 hipError_t launch_split_reduce(const SplitReduceArgs &a, hipStream_t s);
 const TiledVariant *pipe_variants(int *count);
 const TiledVariant *dma_variants(int *count);
+const TiledVariant *mx4w_variants(int *count);   // MXFP4 on the 32x32x64 scaled MFMA
 const SkinnyVariant *skinny_variants(int *count);
 hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
 hipError_t launch_bscale_image(const BscaleArgs &, hipStream_t);

@@ -58,11 +58,13 @@ __global__ __launch_bounds__(256) void bscale_image_kernel(const BscaleArgs p)
         uint32_t word[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int64_t row = quad * 64 + b * 16 + (lane & 15);
+            const int64_t row = p.form ? quad * 64 + (b >> 1) * 32 + (lane & 31) : quad * 64 + b * 16 + (lane & 15);
             uint32_t w = 0;
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) {
-                const int64_t blk = (int64_t)(4 * g + sl) * 4 + (lane >> 4);   // 32-element block along K
+                // 32-element block along K
+                const int64_t blk = p.form ? (int64_t)16 * g + 2 * (2 * sl + (b & 1)) + (lane >> 5)
+                                           : (int64_t)(4 * g + sl) * 4 + (lane >> 4);
                 const uint32_t v = (row < p.rows && blk < p.kblocks) ? p.src[row * p.kblocks + blk] : 127u;
                 w |= v << (8 * sl);
             }
