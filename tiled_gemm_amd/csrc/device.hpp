@@ -44,6 +44,11 @@ __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+
 __device__ inline uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);

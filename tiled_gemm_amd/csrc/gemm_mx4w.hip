@@ -160,7 +160,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
     const auto rSB = make_rsrc(p.sb_img, (uint32_t)((p.N + 63) / 64) * (uint32_t)G * 1024u);
     const uint32_t qb = (uint32_t)((n0 + WN * w) / 64);
     const int ub0 = ((WN * w) >> 5) & 1;                  // row half of the quad of block J = 0
-    u32x4 scA[4], scA_n[4], scB, scB_n;
+    // B: with one 32-column block per wave only the two words of its row half
+    // are loaded (8 bytes).
+    using ScB = typename std::conditional<JB == 1, u32x2, u32x4>::type;
+    u32x4 scA[4], scA_n[4];
+    ScB scB, scB_n;
     auto issue_scales = [&](int g2) {
         const bool in = g2 < G;              // past the last group: out of range
 #pragma unroll
@@ -168,7 +172,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
             scA_n[Q] = buf_load16(
                 rSA, keep_or_oob(in, ((uint32_t)(m0 / 64 + Q) * (uint32_t)G + (uint32_t)g2) * 1024u + (uint32_t)l * 16u),
                 0);
-        scB_n = buf_load16(rSB, keep_or_oob(in, (qb * (uint32_t)G + (uint32_t)g2) * 1024u + (uint32_t)l * 16u), 0);
+        const uint32_t ob = (qb * (uint32_t)G + (uint32_t)g2) * 1024u + (uint32_t)l * 16u;
+        if constexpr (JB == 1)
+            scB_n = buf_load8(rSB, keep_or_oob(in, ob + (uint32_t)ub0 * 8u), 0);
+        else
+            scB_n = buf_load16(rSB, keep_or_oob(in, ob), 0);
         issue_fence();
     };
 
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
             const int i = t & 7, s = t >> 3;
 #pragma unroll
             for (int J = 0; J < JB; ++J)
-                mx4w(acc[i][J], bq[CUR][4 * J + s], fa[t], scB[2 * (ub0 + J) + (s & 1)],
+                mx4w(acc[i][J], bq[CUR][4 * J + s], fa[t], scB[JB == 1 ? (s & 1) : 2 * J + (s & 1)],
                      scA[i >> 1][2 * (i & 1) + (s & 1)], 2 * GP + (s >> 1));
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -337,7 +345,9 @@ static const TiledVariant kMx4w[] = {
     TG_MX4W(true, 8, 6),
     TG_MX4W(false, 8, 6),
     TG_MX4W(true, 8, 4),     // 2
-    TG_MX4W(true, 4, 6),     // 3: one wave per SIMD
+    TG_MX4W(true, 8, 5),
+    TG_MX4W(true, 8, 7),
+    TG_MX4W(true, 4, 6),     // 5: one wave per SIMD
     TG_MX4W(false, 4, 6),
 };
 
