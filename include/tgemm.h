@@ -256,11 +256,11 @@ int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *C,
  * the bytes (ceil(R/64), G, 64, 4, 4), G = ceil(ceil(K/128)/4), row-major:
  * row quad, slice group g, lane l, 16-row block b, slice s holds
  * S[64 quad + 16 b + l % 16][4 (4 g + s) + l / 16] (127 past the rows or K).
- * That is form 0 (gemm_plan_info.scale_form), for the 16x16x128 MFMA.  MXFP4
+ * That is form 0 (gemm_plan_info.scale_form), for the 16x16x128 MFMA.  MX
  * plans on 256 x 256 tiles run the 32x32x64 form of the instruction (twice
- * the e2m1 rate), whose lanes take row l % 32 and K block 2 s' + l / 32 of
- * 64-element slice s'; their image is form 1, with the same size and record
- * order: (quad, g, lane l, word w, byte b) holds
+ * the e2m1 rate, 8 waves), whose lanes take the scale of row l % 32 and K
+ * block 2 s' + l / 32 of 64-element slice s'; their image is form 1, with the
+ * same size and record order: (quad, g, lane l, word w, byte b) holds
  * S[64 quad + 32 (w / 2) + l % 32][16 g + 2 (2 b + w % 2) + l / 32].
  * gemm_preshuffle_bscale writes the plan's form.
  */

@@ -265,11 +265,8 @@ def test_mx_plans(lib, monkeypatch, dtype, bits, layout):
             if M <= 64 and layout == tg.GEMM_LAYOUT_BT_PRESHUFFLED:      # decode: the skinny kernel
                 assert info["kernel"] == 1 and info["tile_n"] == 32
                 assert info["scale_form"] == 0
-            elif bits == 8:
-                assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 256   # 4-wave pipelined
-                assert info["scale_form"] == 0
-            else:                            # MXFP4 tiles: the 32x32x64 kernel, image form 1
-                assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] in (256, 512)
+            else:                            # MX tiles: the 8-wave 32x32x64 kernel, image form 1
+                assert info["kernel"] == 0 and info["tile_m"] == 256 and info["threads"] == 512
                 assert info["scale_form"] == 1
             assert info["elem_bits"] == bits and info["elem_bytes"] == bits // 8
             assert tg.gemm_preshuffled_b_bytes(p.handle) == N * K * bits // 8
@@ -277,10 +274,10 @@ def test_mx_plans(lib, monkeypatch, dtype, bits, layout):
             assert p.bscale_image_bytes(0) == (M + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(1) == (N + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(2) == 0
-    monkeypatch.setenv("TGEMM_MX4W", "0")             # the 16x16x128 kernel reads form 0
+    monkeypatch.setenv("TGEMM_MXW", "0")             # the 16x16x128 kernel reads form 0
     with tg.Plan(300, 272, 1152, dtype, layout) as p:
         assert p.info()["threads"] == 256 and p.info()["scale_form"] == 0
-    monkeypatch.delenv("TGEMM_MX4W")
+    monkeypatch.delenv("TGEMM_MXW")
     with pytest.raises(tg.GemmError, match="2\\^31"):
         tg.Plan(64, 1 << 21, 1 << 16, dtype, layout)    # block-scale image past 32-bit offsets
     with tg.Plan(64, 1 << 20, 1 << 14, dtype, layout) as p:

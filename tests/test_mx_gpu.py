@@ -34,11 +34,15 @@ def say(*a):
 
 
 @pytest.mark.parametrize("R,K", [(200, 1088), (64, 128), (513, 4096)])
-def test_bscale_image_byte_exact(R, K):
+def test_bscale_image_byte_exact(monkeypatch, R, K):
+    # form 0: the 16x16x128 kernels' image (the skinny MX kernels, and the tile
+    # kernel with TGEMM_MXW=0)
     say("case bscale image", R, K)
+    monkeypatch.setenv("TGEMM_MXW", "0")
     rng = np.random.default_rng(R + K)
     S = rng.integers(0, 255, (R, K // 32)).astype(np.uint8)
     with tg.Plan(R, 64, K, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert p.info()["scale_form"] == 0
         n = p.bscale_image_bytes(0)
         src = torch.from_numpy(S).cuda()
         img = torch.full((n,), 0xEE, dtype=torch.uint8, device="cuda")
@@ -52,7 +56,7 @@ def test_bscale_image_byte_exact(R, K):
 
 @pytest.mark.parametrize("R,K", [(200, 1152), (513, 4096)])
 def test_bscale_image_form1_byte_exact(R, K):
-    # MXFP4 on 256 x 256 tiles runs the 32x32x64 kernel, whose plan writes form 1.
+    # MX on 256 x 256 tiles runs the 32x32x64 kernel, whose plan writes form 1.
     say("case bscale image form 1", R, K)
     rng = np.random.default_rng(R * K)
     S = rng.integers(0, 255, (R, K // 32)).astype(np.uint8)

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtgemm.so")
 SOURCES = ["capi.cpp", "gemm_tiled.hip", "gemm_pipe.hip", "gemm_dma.hip", "gemm_skinny.hip", "preshuffle.hip",
-           "splitk.hip", "gemm_mx4w.hip"]
+           "splitk.hip", "gemm_mxw.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -35,12 +35,12 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// The plan's tile kernel is the 32x32x64 MXFP4 one, which reads block-scale
+// The plan's tile kernel is the 32x32x64 MX one, which reads block-scale
 // image form 1.
 bool wide_scales(const gemm_plan *p)
 {
     int n = 0;
-    const tg::TiledVariant *x = tg::mx4w_variants(&n);
+    const tg::TiledVariant *x = tg::mxw_variants(&n);
     return p->info.kernel == 0 && p->tiled && p->tiled >= x && p->tiled < x + n;
 }
 
@@ -133,20 +133,20 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
         // to n-wave variants.
         const char *ew = getenv("TGEMM_PIPE_WAVES");
         const int waves = ew ? atoi(ew) : 0;
-        // MXFP4 runs on the 32x32x64 kernel (twice the e2m1 rate of the
-        // 16x16x128 form) unless TGEMM_MX4W=0; TGEMM_MX4W_VARIANT=<index>
-        // picks one of its sweep variants.
-        const char *e4 = getenv("TGEMM_MX4W");
-        if (elem == tg::kMx4 && !(e4 && e4[0] == '0')) {
+        // MX tiles run on the 32x32x64 kernel (twice the e2m1 rate of the
+        // 16x16x128 form, and 8 waves) unless TGEMM_MXW=0;
+        // TGEMM_MXW_VARIANT=<index> picks one of its sweep variants.
+        const char *e4 = getenv("TGEMM_MXW");
+        if (is_mx(I.dtype) && !(e4 && e4[0] == '0')) {
             int nw = 0;
-            const tg::TiledVariant *x = tg::mx4w_variants(&nw);
-            if (const char *ev = getenv("TGEMM_MX4W_VARIANT")) {
+            const tg::TiledVariant *x = tg::mxw_variants(&nw);
+            if (const char *ev = getenv("TGEMM_MXW_VARIANT")) {
                 const int k = atoi(ev);
-                if (k >= 0 && k < nw && x[k].preshuffled == pre)
+                if (k >= 0 && k < nw && x[k].elem == elem && x[k].preshuffled == pre)
                     return &x[k];
             }
             for (int i = 0; i < nw; ++i)
-                if (x[i].preshuffled == pre && (waves == 0 || x[i].wgm * x[i].wgn == waves))
+                if (x[i].elem == elem && x[i].preshuffled == pre && (waves == 0 || x[i].wgm * x[i].wgn == waves))
                     return &x[i];
         }
         int nb = 0;

@@ -205,6 +205,26 @@ __device__ inline void mfma_mx4w_a(f32x16 &acc, u32x4 x, u32x4 y, uint32_t sx, u
         asm volatile(TG_MX32_ASM(1, 1) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
 }
 #undef TG_MX32_ASM
+// The same for e4m3 operands (8 VGPRs each): lane l feeds row l % 32 with K
+// bytes 16 (l / 32) .. +15 and 32 + 16 (l / 32) .. +15 of the 64-byte slice,
+// while its scale byte covers K block l / 32 (elements 32 (l / 32) .. +31).
+#define TG_MX32F8_ASM(LO, HI)                                                                   \
+    "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #LO "," #LO ",0] "     \
+    "op_sel_hi:[" #HI "," #HI ",0]"
+template <int BYTE>
+__device__ inline void mfma_mx8w_a(f32x16 &acc, i32x8 x, i32x8 y, uint32_t sx, uint32_t sy)
+{
+    static_assert(BYTE >= 0 && BYTE < 4, "scale byte");
+    if constexpr (BYTE == 0)
+        asm volatile(TG_MX32F8_ASM(0, 0) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 1)
+        asm volatile(TG_MX32F8_ASM(1, 0) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else if constexpr (BYTE == 2)
+        asm volatile(TG_MX32F8_ASM(0, 1) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+    else
+        asm volatile(TG_MX32F8_ASM(1, 1) : "+a"(acc) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+}
+#undef TG_MX32F8_ASM
 
 // int8 atom: D += X * Y^T over 64 int8 values per row (16 bytes per lane, the
 // same lane / K slot assignment as the bf16 atom), int32 sums.  The

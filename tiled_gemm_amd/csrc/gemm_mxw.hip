@@ -1,4 +1,4 @@
-// MXFP4 GEMM C = A * B^T on the 32x32x64 form of gfx950's scaled MFMA,
+// MX GEMM C = A * B^T (MXFP4, MXFP8) on the 32x32x64 form of gfx950's scaled MFMA,
 // 256 x 256 tiles (FlyDSL "Kernel Authoring" skill, section 6 "GEMM Pattern
 // (Preshuffle)": B pre-shuffled into operand order, A staged through
 // XOR-swizzled LDS, LDS ping-pong; section 3 "Runtime Loops with
@@ -6,27 +6,31 @@
 // Kernel authoring guide", section 4.3 "ROCm intrinsics", for the f8f6f4
 // scaled MFMA family and its E8M0 block scales).
 //
-// Why a second MXFP4 kernel: e2m1 operands run at twice the e4m3 rate only in
+// Why a second MX kernel: e2m1 operands run at twice the e4m3 rate only in
 // the 32x32x64 shape (the 16x16x128 shape is capped near the e4m3 rate; an
 // independent-accumulator microbenchmark on every CU measured 7.3 against
-// 4.7 PFLOP/s).  Per 64-element K slice a lane feeds one 16-byte operand of
-// row l % 32, elements 32 (l / 32) .. +31, and one scale byte for them.
+// 4.7 PFLOP/s), and its 32 x 32 accumulators let MX run on 8 waves (the
+// 16x16x128 MX kernel spills there).  Per 64-element K slice a lane feeds row
+// l % 32 -- e2m1: one 16-byte chunk, elements 32 (l / 32) .. +31; e4m3: chunks
+// l / 32 and 2 + l / 32 of the slice -- and one scale byte, for K block
+// l / 32 of the slice.
 //
 // Workgroup: WAVES waves side by side along N; wave w owns all 256 rows and
 // the WN = 256 / WAVES columns from WN w (JB = WN / 32 blocks of 32), i.e.
 // 8 x JB accumulators of 32 x 32 in AGPRs.  Main-loop step: 128 bytes of K
-// (256 elements, four 64-element slices).
+// (e2m1: 256 elements, four 64-element slices; e4m3: two slices).
 //
 //   A   global -> LDS by loads that write LDS directly, ring of 4 stages of
 //       32 KiB (rows of 128 bytes, 16-byte chunks XOR-swizzled); a fragment
-//       is one 16-byte LDS read (row 32 i + l % 32, chunk 2 s + l / 32).
+//       is one or two 16-byte LDS reads (row 32 i + l % 32, the chunks above).
 //   B   global -> VGPRs, 4 JB 16-byte loads per lane and step, issued one
 //       step ahead into two register sets renamed by unrolling.  From the
-//       pre-shuffled image, lane l of column block J and slice s reads
-//       16-row block n / 16, k-block 2 kt + s / 2, quarter 2 (s % 2) + l / 32,
-//       row n % 16 (n = WN w + 32 J + l % 32): two 512-byte runs per wave load.
+//       pre-shuffled image, chunk c of the step for column n = WN w + 32 J +
+//       l % 32 is 16-row block n / 16, k-block 2 kt + c / 4, quarter c % 4,
+//       row n % 16: two 512-byte runs per wave load.
 //   Scales from block-scale image form 1 (one record of 1 KiB per 64-row
-//       quad and 512-element group): lane l's 16 bytes hold, in word 2 u + par,
+//       quad and 512-element group, 2 steps of e2m1 or 4 of e4m3): lane l's
+//       16 bytes hold, in word 2 u + par,
 //       byte b, the scale of row 32 u + l % 32 of the quad for K block
 //       2 s' + l / 32 of slice s' = 2 b + par.  One 16-byte load per quad and
 //       group brings a lane every scale it feeds; op_sel picks the byte.
@@ -48,13 +52,12 @@ constexpr int W4_BM = 256;
 constexpr int W4_BN = 256;
 constexpr int W4_NS = 4;                                   // LDS stages of A
 constexpr int W4_STAGE = W4_BM * kTileKBytes;              // 32 KiB
-constexpr int W4_NG = 32;                                  // groups per step: (row block, slice)
 
 template <int N>
 using xc = std::integral_constant<int, N>;
 
 // The scaled MFMA with scale byte `byte` (a constant once the loops unroll).
-__device__ inline void mx4w(f32x16 &acc, u32x4 x, u32x4 y, uint32_t sx, uint32_t sy, int byte)
+__device__ inline void mxw(f32x16 &acc, u32x4 x, u32x4 y, uint32_t sx, uint32_t sy, int byte)
 {
     switch (byte) {
     case 0: mfma_mx4w_a<0>(acc, x, y, sx, sy); break;
@@ -63,19 +66,34 @@ __device__ inline void mx4w(f32x16 &acc, u32x4 x, u32x4 y, uint32_t sx, uint32_t
     default: mfma_mx4w_a<3>(acc, x, y, sx, sy); break;
     }
 }
+__device__ inline void mxw(f32x16 &acc, i32x8 x, i32x8 y, uint32_t sx, uint32_t sy, int byte)
+{
+    switch (byte) {
+    case 0: mfma_mx8w_a<0>(acc, x, y, sx, sy); break;
+    case 1: mfma_mx8w_a<1>(acc, x, y, sx, sy); break;
+    case 2: mfma_mx8w_a<2>(acc, x, y, sx, sy); break;
+    default: mfma_mx8w_a<3>(acc, x, y, sx, sy); break;
+    }
+}
 
 }  // namespace
 
-template <bool BPRE, int WAVES, int PD>
-__global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArgs p)
+template <int ELEM, bool BPRE, int WAVES, int PD>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_mxw_kernel(const TiledArgs p)
 {
+    constexpr bool F8 = ELEM == kMx8;
+    constexpr int SLICES = F8 ? 2 : 4;                     // 64-element K slices per step
+    constexpr int W4_NG = 8 * SLICES;                      // groups per step: (row block, slice)
+    constexpr int SPG = 8 / SLICES;                        // steps per scale group
+    constexpr int BL = F8 ? 2 : 1;                         // chunks per row and slice
     constexpr int THREADS = 64 * WAVES;
     constexpr int WN = W4_BN / WAVES;                      // columns per wave
     constexpr int JB = WN / 32;                            // 32-column blocks per wave
     constexpr int AR = W4_STAGE / (THREADS * kChunkBytes); // A loads per lane and step
-    constexpr int BR = 4 * JB;                             // B loads per lane and step
+    constexpr int BR = JB * SLICES * BL;                   // B loads per lane and step (4 JB)
     constexpr int SL = 5;                                  // scale loads per group
     static_assert(JB >= 1 && WN % 32 == 0, "whole 32-column blocks per wave");
+    static_assert(ELEM == kMx4 || ELEM == kMx8, "MX operands");
     static_assert(PD >= 1 && PD < W4_NG / 2, "prefetch distance");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[W4_NS * W4_STAGE];
 
@@ -109,17 +127,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
         voffA[r] = (uint32_t)row * kb + (uint32_t)c * kChunkBytes;
         tailA |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << r;
     }
-    // ---- B: load b = 4 J + s brings chunk 2 s + g of column WN w + 32 J + r32.
+    // ---- B: load b = (SLICES J + s) BL + h brings chunk c of the step of
+    // column WN w + 32 J + r32: e2m1 c = 2 s + g, e4m3 c = 4 s + 2 h + g.
     uint32_t voffB[BR];
     uint32_t tailB = 0;
 #pragma unroll
     for (int b = 0; b < BR; ++b) {
-        const int J = b >> 2, s = b & 3;
+        const int J = b / (SLICES * BL), s = (b / BL) % SLICES, h = b % BL;
         const int n = WN * w + 32 * J + r32;
-        const int c = 2 * s + g;
+        const int c = F8 ? 4 * s + 2 * h + g : 2 * s + g;
         if constexpr (BPRE)
-            voffB[b] = (uint32_t)(n >> 4) * 16u * kbB + (uint32_t)(s >> 1) * 1024u +
-                       (uint32_t)((2 * (s & 1) + g) * 16 + (n & 15)) * 16u;
+            voffB[b] = (uint32_t)(n >> 4) * 16u * kbB + (uint32_t)(c >> 2) * 1024u +
+                       (uint32_t)((c & 3) * 16 + (n & 15)) * 16u;
         else
             voffB[b] = (uint32_t)n * kbB + (uint32_t)c * kChunkBytes;
         tailB |= ((uint32_t)(c * kChunkBytes) < tail ? 1u : 0u) << b;
@@ -190,11 +209,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
                 acc[i][J][v] = 0.f;
 
     // ---- fragments: group t of a step = (row block t % 8, slice t / 8).
-    u32x4 fa[W4_NG];
+    using FragT = typename std::conditional<F8, i32x8, u32x4>::type;
+    FragT fa[W4_NG];
     auto load_frag = [&](int stage, int t) {
         const int i = t & 7, s = t >> 3;
         const int row = 32 * i + r32;
-        fa[t] = lds_load16(lds + stage * W4_STAGE + row * kTileKBytes + swz_chunk(row, 2 * s + g) * kChunkBytes);
+        const uint8_t *base = lds + stage * W4_STAGE + row * kTileKBytes;
+        if constexpr (F8)
+            fa[t] = join32(lds_load16(base + swz_chunk(row, 4 * s + g) * kChunkBytes),
+                           lds_load16(base + swz_chunk(row, 4 * s + 2 + g) * kChunkBytes));
+        else
+            fa[t] = lds_load16(base + swz_chunk(row, 2 * s + g) * kChunkBytes);
     };
 
     // Load issue order per step k: the next group's scales at the start of
@@ -204,8 +229,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
     // barrier(k), A(k+1) has two B steps, one A step and one group of
     // scales behind it.
     constexpr int kVmStart = AR;
-    constexpr int kVmBar = 2 * BR + AR + SL;
-    static_assert(kVmBar < 64, "vmcnt is 6 bits");
+    constexpr int kVmBar0 = 2 * BR + AR;
+    static_assert(kVmBar0 + SL < 64, "vmcnt is 6 bits");
     auto wait_vm = [&](auto n_c) {
         constexpr int n = decltype(n_c)::value;
         __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | (n & 0xF) | ((n >> 4) << 14));
@@ -219,6 +244,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
     auto step = [&](int kt, auto cur_c, auto gp_c, auto mask_c) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int GP = decltype(gp_c)::value;
+        // scale loads behind A(k+1): one group's when step k or k-1 starts a group
+        constexpr int kVmBar = kVmBar0 + SL * ((GP == 0) + ((GP - 1 + SPG) % SPG == 0));
         const int st = kt % W4_NS;
         wait_vm(xc<kVmStart>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -227,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
             for (int Q = 0; Q < 4; ++Q)
                 scA[Q] = scA_n[Q];
             scB = scB_n;
-            issue_scales(kt / 2 + 1);
+            issue_scales(kt / SPG + 1);
         }
 #pragma unroll
         for (int t = 0; t < W4_NG; ++t) {
@@ -250,10 +277,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
             else
                 load_frag((kt + 1) % W4_NS, t + PD - W4_NG);
             const int i = t & 7, s = t >> 3;
+            const int sg = SLICES * GP + s;                  // slice of the scale group
 #pragma unroll
-            for (int J = 0; J < JB; ++J)
-                mx4w(acc[i][J], bq[CUR][4 * J + s], fa[t], scB[JB == 1 ? (s & 1) : 2 * J + (s & 1)],
-                     scA[i >> 1][2 * (i & 1) + (s & 1)], 2 * GP + (s >> 1));
+            for (int J = 0; J < JB; ++J) {
+                const int b0 = (SLICES * J + s) * BL;
+                const uint32_t sx = scB[JB == 1 ? (sg & 1) : 2 * J + (sg & 1)];
+                const uint32_t sy = scA[i >> 1][2 * (i & 1) + (sg & 1)];
+                if constexpr (F8)
+                    mxw(acc[i][J], join32(bq[CUR][b0], bq[CUR][b0 + 1]), fa[t], sx, sy, sg >> 1);
+                else
+                    mxw(acc[i][J], bq[CUR][b0], fa[t], sx, sy, sg >> 1);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -278,19 +312,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
 #pragma unroll
     for (int t = 0; t < PD; ++t)
         load_frag(0, t);
-    // Steps run in pairs (one scale group); a step past nk is a phantom on
-    // zeros.  A pair whose loads (B up to kt + 2, A up to kt + NS) all cover
-    // whole, in-range tiles runs without per-lane masks.
+    // Steps run in scale groups (2 or 4 steps); a step past nk is a phantom
+    // on zeros.  A group whose loads (B up to kt + SPG, A up to kt + SPG +
+    // NS - 2) all cover whole, in-range tiles runs without per-lane masks.
     int kt = 0;
     const int nfull = tail == (uint32_t)kTileKBytes ? nk : nk - 1;
-    for (; kt + W4_NS < nfull; kt += 2) {
-        step(kt, xc<0>{}, xc<0>{}, unmasked{});
-        step(kt + 1, xc<1>{}, xc<1>{}, unmasked{});
-    }
-    for (; kt < nk; kt += 2) {
-        step(kt, xc<0>{}, xc<0>{}, masked{});
-        step(kt + 1, xc<1>{}, xc<1>{}, masked{});
-    }
+    auto group = [&](int k0, auto mask_c) {
+        step(k0, xc<0>{}, xc<0>{}, mask_c);
+        step(k0 + 1, xc<1>{}, xc<1>{}, mask_c);
+        if constexpr (SPG == 4) {
+            step(k0 + 2, xc<0>{}, xc<2>{}, mask_c);
+            step(k0 + 3, xc<1>{}, xc<3>{}, mask_c);
+        }
+    };
+    for (; kt + SPG + W4_NS - 2 < nfull; kt += SPG)
+        group(kt, unmasked{});
+    for (; kt < nk; kt += SPG)
+        group(kt, masked{});
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     mfma_drain_acc(acc);
 
@@ -328,33 +366,35 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_mx4w_kernel(const TiledArg
     }
 }
 
-template <bool BPRE, int WAVES, int PD>
-static hipError_t launch_mx4w(const TiledArgs &a, hipStream_t s)
+template <int ELEM, bool BPRE, int WAVES, int PD>
+static hipError_t launch_mxw(const TiledArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_mx4w_kernel<BPRE, WAVES, PD>), dim3(a.grid), dim3(64 * WAVES), 0, s, a);
+    hipLaunchKernelGGL((gemm_mxw_kernel<ELEM, BPRE, WAVES, PD>), dim3(a.grid), dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();
 }
 
-#define TG_MX4W(BPRE, WAVES, PD)                                                                  \
-    TiledVariant{W4_BM, W4_BN, 1, WAVES, kMx4, kOutBf16, BPRE, W4_NS * W4_STAGE, W4_NS,           \
-                 &launch_mx4w<BPRE, WAVES, PD>}
+#define TG_MXW(ELEM, BPRE, WAVES, PD)                                                            \
+    TiledVariant{W4_BM, W4_BN, 1, WAVES, ELEM, kOutBf16, BPRE, W4_NS * W4_STAGE, W4_NS,           \
+                 &launch_mxw<ELEM, BPRE, WAVES, PD>}
 
 // The first variant of each layout is the planner's choice; the rest are
-// alternatives selectable by index (TGEMM_MX4W_VARIANT).
-static const TiledVariant kMx4w[] = {
-    TG_MX4W(true, 8, 6),
-    TG_MX4W(false, 8, 6),
-    TG_MX4W(true, 8, 4),     // 2
-    TG_MX4W(true, 8, 5),
-    TG_MX4W(true, 8, 7),
-    TG_MX4W(true, 4, 6),     // 5: one wave per SIMD
-    TG_MX4W(false, 4, 6),
+// alternatives selectable by index (TGEMM_MXW_VARIANT).
+static const TiledVariant kMxw[] = {
+    TG_MXW(kMx4, true, 8, 6),
+    TG_MXW(kMx4, false, 8, 6),
+    TG_MXW(kMx8, true, 8, 2),     // 2 (e4m3 fragments are 8 VGPRs: deeper prefetch spills)
+    TG_MXW(kMx8, false, 8, 2),
+    TG_MXW(kMx4, true, 8, 4),     // 4
+    TG_MXW(kMx4, true, 8, 5),
+    TG_MXW(kMx4, true, 8, 7),
+    TG_MXW(kMx4, true, 4, 6),     // 7: one wave per SIMD
+    TG_MXW(kMx4, false, 4, 6),
 };
 
-const TiledVariant *mx4w_variants(int *count)
+const TiledVariant *mxw_variants(int *count)
 {
-    *count = (int)(sizeof(kMx4w) / sizeof(kMx4w[0]));
-    return kMx4w;
+    *count = (int)(sizeof(kMxw) / sizeof(kMxw[0]));
+    return kMxw;
 }
 
 }  // namespace tg

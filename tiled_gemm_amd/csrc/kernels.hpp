@@ -141,7 +141,7 @@ const TiledVariant *tiled_variants(int *count);
 hipError_t launch_split_reduce(const SplitReduceArgs &a, hipStream_t s);
 const TiledVariant *pipe_variants(int *count);
 const TiledVariant *dma_variants(int *count);
-const TiledVariant *mx4w_variants(int *count);   // MXFP4 on the 32x32x64 scaled MFMA
+const TiledVariant *mxw_variants(int *count);   // MX on the 32x32x64 scaled MFMA
 const SkinnyVariant *skinny_variants(int *count);
 hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
 hipError_t launch_bscale_image(const BscaleArgs &, hipStream_t);
