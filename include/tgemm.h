@@ -82,9 +82,9 @@ typedef enum {
 typedef enum {
     GEMM_LAYOUT_BT = 0,               /* B is N x K row-major                        */
     GEMM_LAYOUT_BT_PRESHUFFLED = 1,   /* B is the image written by gemm_preshuffle_b */
-    GEMM_LAYOUT_BN = 2,               /* B is K x N row-major: C = A * B (bf16, e4m3) */
-    GEMM_LAYOUT_AT = 3,               /* A is K x M row-major, B N x K (bf16 only)   */
-    GEMM_LAYOUT_AT_BN = 4             /* A is K x M, B K x N row-major (bf16 only)   */
+    GEMM_LAYOUT_BN = 2,               /* B is K x N row-major: C = A * B (bf16, e4m3, int8) */
+    GEMM_LAYOUT_AT = 3,               /* A is K x M row-major, B N x K (bf16, e4m3, int8)   */
+    GEMM_LAYOUT_AT_BN = 4             /* A is K x M, B K x N row-major (bf16, e4m3, int8)   */
 } gemm_layout;
 
 typedef struct gemm_plan gemm_plan;   /* opaque, immutable after creation */
@@ -104,6 +104,43 @@ typedef struct gemm_plan gemm_plan;   /* opaque, immutable after creation */
  * caller frees with gemm_plan_destroy.
  */
 gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout);
+
+/*
+ * Kernel choice for gemm_plan_create_opt.  GEMM_KERNEL_AUTO is the planner's
+ * own pick by shape, dtype and layout (what gemm_plan_create does); the others
+ * force one kernel family for every shape, so that each family the planner
+ * may pick can be checked and timed on any shape.  Every choice computes the
+ * same C within the same bound; only speed differs.
+ */
+typedef enum {
+    GEMM_KERNEL_AUTO = 0,         /* the planner's table                                      */
+    GEMM_KERNEL_GENERIC_128 = 1,  /* generic tiled kernel, 128 x 128 tiles (bf16, e4m3)       */
+    GEMM_KERNEL_GENERIC_256 = 2,  /* generic tiled kernel, 256 x 256 tiles (bf16, e4m3)       */
+    GEMM_KERNEL_TILE256 = 3,      /* the planner's 256 x 256 kernel at any size (no skinny
+                                     kernel, no 128 x 128 tiles)                              */
+    GEMM_KERNEL_PIPE = 4,         /* 256 x 256, B straight to registers, 8 waves (bf16 and
+                                     e4m3 with B N x K or pre-shuffled; integer operands)     */
+    GEMM_KERNEL_PIPE4 = 5         /* the same with 4 waves and AGPR accumulators; for MX plans
+                                     the 16x16x128 form of the scaled MFMA (block-scale image
+                                     form 0)                                                   */
+} gemm_kernel_choice;
+
+typedef struct {
+    int32_t kernel;               /* gemm_kernel_choice                                       */
+    int32_t splits;               /* gemm_run_ws K slices: 0 the planner's choice, 1 never
+                                     split, 2..64 that many (plans whose kernel can split)    */
+} gemm_plan_options;
+
+/*
+ * gemm_plan_create_opt -- gemm_plan_create with an explicit kernel choice and
+ * split count.  opt == NULL (or all fields 0) is exactly gemm_plan_create.
+ * Errors as gemm_plan_create, plus GEMM_ERR_INVALID_ARG for an unknown choice
+ * or a split count outside 0..64, and GEMM_ERR_UNSUPPORTED when the chosen
+ * family has no kernel for the dtype and layout.  The library reads no
+ * environment variables: a plan depends on these arguments only.
+ */
+gemm_plan *gemm_plan_create_opt(int64_t M, int64_t N, int64_t K, int dtype, int layout,
+                                const gemm_plan_options *opt);
 
 /* gemm_plan_destroy -- free a plan (NULL is ignored). */
 void gemm_plan_destroy(gemm_plan *plan);

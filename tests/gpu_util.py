@@ -20,6 +20,16 @@ RHO = {"bf16": 2.0 ** -8, "e4m3": 2.0 ** -3, "mxfp8": 2.0 ** -8, "mxfp4": 2.0 **
        "w4a8": 2.0 ** -8}
 ABS_COEF = 4e-6
 
+# Kernel choice and split count for the plans run_gemm creates (see
+# gemm_plan_create_opt); tests set them through the ``plan_opts`` fixture,
+# which restores the planner's own choice afterwards.
+PLAN_OPTS = {"kernel": 0, "splits": 0}
+
+# Short names of the kernel families (gemm_kernel_choice): "generic128" /
+# "generic256" the generic tiled kernel, "tile256" the planner's 256 x 256
+# kernel at any size, "pipe" the 8-wave software-pipelined kernel with B in
+# registers, "pipe4" its 4-wave AGPR form (MX: the 16x16x128 kernel).
+
 DTYPE_CODE = {("bf16", "f32"): tg.GEMM_BF16_OUT_F32, ("bf16", "bf16"): tg.GEMM_BF16_OUT_BF16,
               ("e4m3", "bf16"): tg.GEMM_E4M3_OUT_BF16, ("mxfp8", "bf16"): tg.GEMM_MXFP8_OUT_BF16,
               ("mxfp4", "bf16"): tg.GEMM_MXFP4_OUT_BF16, ("i8", "bf16"): tg.GEMM_I8_OUT_BF16,
@@ -53,7 +63,7 @@ def run_gemm(A_bits, B_bits, M, N, K, dtype="bf16", out="bf16", layout="bt",
     lay = tg.LAYOUTS[layout]
     own = plan is None
     if own:
-        plan = tg.Plan(M, N, K, code, lay)
+        plan = tg.Plan(M, N, K, code, lay, **PLAN_OPTS)
     s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
     ob = 4 if out == "f32" else 2
     A = to_dev(A_bits) if A_bits.size else torch.empty(16, dtype=torch.uint8, device="cuda")
@@ -163,3 +173,16 @@ def sample_entries(M: int, N: int, n_random: int, seed: int):
     cols = [np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1, np.int64),
             rng.integers(0, N, n_random)]
     return np.concatenate(rows), np.concatenate(cols)
+
+
+def force(kernel=None, splits=0):
+    """Set the kernel choice (a name of tg.KERNELS, None = the planner's) and
+    split count of the plans created by run_gemm and plan(); the plan_opts
+    fixture restores the defaults after each test."""
+    PLAN_OPTS["kernel"] = tg.KERNELS[kernel or "auto"]
+    PLAN_OPTS["splits"] = int(splits)
+
+
+def plan(M, N, K, dtype_code, layout_code):
+    """A tg.Plan with the current PLAN_OPTS (kernel choice, split count)."""
+    return tg.Plan(M, N, K, dtype_code, layout_code, **PLAN_OPTS)

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import workloads as W
+import gpu_util
 from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
@@ -29,15 +30,9 @@ def say(*a):
 
 
 def set_tile(monkeypatch, tile):
-    # "256x256": the planner's 256 x 256 kernel (both operands staged in LDS);
-    # "256x256g": the generic tiled kernel.
-    monkeypatch.delenv("TGEMM_TILE", raising=False)
-    monkeypatch.delenv("TGEMM_DMA", raising=False)
-    if tile and tile.endswith("g"):
-        monkeypatch.setenv("TGEMM_DMA", "0")
-        tile = tile[:-1]
-    if tile:
-        monkeypatch.setenv("TGEMM_TILE", tile)
+    # "tile256": the planner's 256 x 256 kernel (both operands staged in LDS);
+    # "generic256" / "generic128": the generic tiled kernel.
+    gpu_util.force(tile)
 
 
 def int_kn(M, N, K, seed):
@@ -58,7 +53,7 @@ def _exact(oracle_mod, bits, out, C):
         int(bad.sum()), np.argwhere(bad)[0], decode(bits)[tuple(np.argwhere(bad)[0])], C[tuple(np.argwhere(bad)[0])])
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x256g", "128x128"])
+@pytest.mark.parametrize("tile", ["tile256", "generic256", "generic128"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(300, 272, 1056), (256, 512, 1024), (1, 16, 32), (77, 48, 96)])
 def test_bn_bit_exact(oracle_mod, monkeypatch, tile, out, M, N, K):
@@ -71,7 +66,7 @@ def test_bn_bit_exact(oracle_mod, monkeypatch, tile, out, M, N, K):
     _exact(oracle_mod, bits, out, C)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x256g", "128x128"])
+@pytest.mark.parametrize("tile", ["tile256", "generic256", "generic128"])
 def test_bn_random_within_bound(oracle_mod, monkeypatch, tile):
     M, N, K = 520, 784, 1504
     set_tile(monkeypatch, tile)

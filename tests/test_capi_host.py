@@ -186,9 +186,46 @@ def test_plan_choices(lib, monkeypatch):
     c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
     assert c["lds_stages"] == 4                      # fp8: B in registers
-    monkeypatch.setenv("TGEMM_DMA", "0")
-    c = info(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT)
+    with tg.Plan(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT, kernel=tg.GEMM_KERNEL_PIPE) as p:
+        c = p.info()
     assert (c["threads"], c["lds_stages"]) == (512, 4)
+    # every forced family disables the skinny kernel and the 128 x 128 default
+    for kc, tile, threads in ((tg.GEMM_KERNEL_GENERIC_128, 128, 256), (tg.GEMM_KERNEL_GENERIC_256, 256, 256),
+                              (tg.GEMM_KERNEL_TILE256, 256, 512), (tg.GEMM_KERNEL_PIPE, 256, 512),
+                              (tg.GEMM_KERNEL_PIPE4, 256, 256)):
+        with tg.Plan(32, 1024, 1024, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED, kernel=kc) as p:
+            c = p.info()
+        assert (c["kernel"], c["tile_m"], c["threads"]) == (0, tile, threads), kc
+
+
+def test_plan_options_are_checked(lib):
+    opt = tg.gemm_plan_options(99, 0)
+    assert not lib.gemm_plan_create_opt(256, 256, 256, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT, ctypes.byref(opt))
+    assert "kernel choice" in tg.gemm_last_error()
+    opt = tg.gemm_plan_options(0, 65)
+    assert not lib.gemm_plan_create_opt(256, 256, 256, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT, ctypes.byref(opt))
+    # NULL options: exactly gemm_plan_create
+    h = lib.gemm_plan_create_opt(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT, None)
+    assert h
+    a = tg.gemm_plan_query(h)
+    lib.gemm_plan_destroy(h)
+    with tg.Plan(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+        assert p.info() == a
+    # a family without a kernel for the dtype / layout is refused
+    for dt, lay, kc in ((tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT, tg.GEMM_KERNEL_PIPE),
+                        (tg.GEMM_I8_OUT_BF16, tg.GEMM_LAYOUT_BT, tg.GEMM_KERNEL_GENERIC_128),
+                        (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BN, tg.GEMM_KERNEL_PIPE),
+                        (tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_AT, tg.GEMM_KERNEL_GENERIC_256)):
+        with pytest.raises(tg.GemmError, match="kernel choice"):
+            tg.Plan(512, 512, 1024, dt, lay, kernel=kc)
+
+
+def test_library_reads_no_environment(lib):
+    # The planner's choices depend on the arguments alone: the library's
+    # imports hold no getenv.
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", tg.LIB_PATH], capture_output=True, text=True).stdout
+    assert "getenv" not in out
 
 
 @pytest.mark.parametrize("args,code", [
@@ -274,10 +311,9 @@ def test_mx_plans(lib, monkeypatch, dtype, bits, layout):
             assert p.bscale_image_bytes(0) == (M + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(1) == (N + 63) // 64 * groups * 1024
             assert p.bscale_image_bytes(2) == 0
-    monkeypatch.setenv("TGEMM_MXW", "0")             # the 16x16x128 kernel reads form 0
-    with tg.Plan(300, 272, 1152, dtype, layout) as p:
+    # the 4-wave 16x16x128 kernel reads form 0
+    with tg.Plan(300, 272, 1152, dtype, layout, kernel=tg.GEMM_KERNEL_PIPE4) as p:
         assert p.info()["threads"] == 256 and p.info()["scale_form"] == 0
-    monkeypatch.delenv("TGEMM_MXW")
     with pytest.raises(tg.GemmError, match="2\\^31"):
         tg.Plan(64, 1 << 21, 1 << 16, dtype, layout)    # block-scale image past 32-bit offsets
     with tg.Plan(64, 1 << 20, 1 << 14, dtype, layout) as p:
@@ -308,10 +344,8 @@ def test_int_plans(lib, monkeypatch, dtype, b_bits, layout):
             assert tuple(map(tuple, tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B))) == ((N, kb), (kb, 1))
             assert tuple(map(tuple, tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B_SHUF)))[0] == (N // 16, kb // 64, 4, 16, 16)
             assert p.bscale_image_bytes(0) == 0
-    monkeypatch.setenv("TGEMM_PIPE_WAVES", "4")
-    with tg.Plan(512, 512, 1024, dtype, layout) as p:
+    with tg.Plan(512, 512, 1024, dtype, layout, kernel=tg.GEMM_KERNEL_PIPE4) as p:
         assert p.info()["threads"] == 256
-    monkeypatch.delenv("TGEMM_PIPE_WAVES")
     with pytest.raises(tg.GemmError):
         tg.Plan(64, 64, 96, dtype, layout)                    # K % 64
     if b_bits == 4:
@@ -346,10 +380,8 @@ def test_bn_layout_plans(lib, monkeypatch):
                 assert tg.gemm_preshuffled_b_bytes(p.handle) == 0
                 assert tg.gemm_plan_layout(p.handle, tg.GEMM_VIEW_B) == ((K, 2 * N), (2 * N, 1))
                 assert lib.gemm_preshuffle_b(p.handle, 0x100000, 0x200000, None) == tg.GEMM_ERR_INVALID_ARG
-        monkeypatch.setenv("TGEMM_DMA", "0")
-        with tg.Plan(4096, 4096, 4096, dtype, tg.GEMM_LAYOUT_BN) as p:
+        with tg.Plan(4096, 4096, 4096, dtype, tg.GEMM_LAYOUT_BN, kernel=tg.GEMM_KERNEL_GENERIC_256) as p:
             assert p.info()["threads"] == 256                # the generic tiled kernel
-        monkeypatch.delenv("TGEMM_DMA")
     # fp8 e4m3 and int8 with B stored K x N: the LDS-staged kernel on 256 x 256 tiles at every size
     for dtype in (tg.GEMM_E4M3_OUT_BF16, tg.GEMM_I8_OUT_BF16):
         for M, N, K in [(4096, 4096, 4096), (300, 272, 1088), (1, 16, 64)]:
@@ -423,10 +455,10 @@ def test_mx_entry_point_guards(lib):
 def test_split_k_plans(lib, monkeypatch):
     """Split K (gemm_run_ws): slices while 256 x 256 tiles x slices <= 256 and
     each slice keeps >= 8 K steps; every slice non-empty; workspace bytes."""
-    monkeypatch.delenv("TGEMM_SPLIT", raising=False)
+    forced = {"splits": 0, "kernel": tg.GEMM_KERNEL_AUTO}
 
     def plan(M, N, K, dt=tg.GEMM_BF16_OUT_BF16, lay=tg.GEMM_LAYOUT_BT_PRESHUFFLED):
-        with tg.Plan(M, N, K, dt, lay) as p:
+        with tg.Plan(M, N, K, dt, lay, **forced) as p:
             return p.info(), p.workspace_bytes()
     for M, want in ((65, 8), (256, 8), (257, 4), (512, 4), (768, 2), (1024, 2), (1025, 1), (8192, 1)):
         info, ws = plan(M, 8192, 8192)
@@ -448,14 +480,14 @@ def test_split_k_plans(lib, monkeypatch):
     assert plan(256, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16)[0]["ws_splits"] == 1
     assert plan(256, 8192, 8192, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BN)[0]["ws_splits"] == 1
     # a forced count, uneven slices; an impossible one is refused (no split)
-    monkeypatch.setenv("TGEMM_SPLIT", "3")
+    forced["splits"] = 3
     assert plan(136, 528, 4160)[0]["ws_splits"] == 3
     assert plan(136, 528, 4160, tg.GEMM_E4M3_OUT_BF16)[0]["ws_splits"] == 3   # forced: fp8 too
-    monkeypatch.setenv("TGEMM_SPLIT", "64")
+    forced["splits"] = 64
     assert plan(136, 528, 4160)[0]["ws_splits"] == 1                # 65 steps: slices would be empty
     # the generic tiled kernel does not read the split fields: never split on it
-    monkeypatch.setenv("TGEMM_SPLIT", "4")
-    monkeypatch.setenv("TGEMM_PIPE", "0")
+    forced["splits"] = 4
+    forced["kernel"] = tg.GEMM_KERNEL_GENERIC_256
     assert plan(256, 8192, 8192)[0]["ws_splits"] == 1
 
 

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import workloads as W
+import gpu_util
 from gpu_util import assert_epilogue_within_bound, decode, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
@@ -21,8 +22,8 @@ pytestmark = pytest.mark.gpu
 # B stored N x K: both operands through LDS; fp8: pipelined 8-wave),
 # "256x256p" pipelined 8-wave with B in registers, "256x256q" pipelined
 # 4-wave, "256x256g" generic, "128x128" generic, None with M <= 64 skinny.
-PATHS = [("256x256", "bt", None), ("256x256p", "bt", None), ("256x256q", "bt_preshuffled", None), ("256x256g", "bt", None),
-         ("128x128", "bt_preshuffled", None), (None, "bt", 33), (None, "bt_preshuffled", 33)]
+PATHS = [("tile256", "bt", None), ("pipe", "bt", None), ("pipe4", "bt_preshuffled", None), ("generic256", "bt", None),
+         ("generic128", "bt_preshuffled", None), (None, "bt", 33), (None, "bt_preshuffled", 33)]
 DTYPES = [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16")]
 
 
@@ -37,21 +38,8 @@ def say(*a):
     print(*a, flush=True)
 
 
-def set_path(monkeypatch, tile):
-    for k in ("TGEMM_PIPE", "TGEMM_TILE", "TGEMM_PIPE_WAVES", "TGEMM_DMA"):
-        monkeypatch.delenv(k, raising=False)
-    if tile is None:
-        return
-    if tile.endswith("p"):
-        monkeypatch.setenv("TGEMM_DMA", "0")
-        tile = tile[:-1]
-    if tile.endswith("g"):
-        monkeypatch.setenv("TGEMM_PIPE", "0")
-        tile = tile[:-1]
-    if tile.endswith("q"):
-        monkeypatch.setenv("TGEMM_PIPE_WAVES", "4")
-        tile = tile[:-1]
-    monkeypatch.setenv("TGEMM_TILE", tile)
+def set_path(monkeypatch, kernel):
+    gpu_util.force(kernel)
 
 
 def epi_case(name, M, N, rng):

@@ -18,23 +18,24 @@ from gpu_util import assert_within_bound, decode, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
 
-# (dtype, out, layout, tile) -- tile None = the planner's own choice; "256x256"
-# is the planner's 256 x 256 kernel (bf16 with B stored N x K: both operands
-# through LDS; otherwise the software-pipelined kernel), "256x256p" the
-# software-pipelined kernel with B in registers, "256x256g" the generic tiled
-# kernel, "256x256q" the 4-wave pipelined kernel.
+# (dtype, out, layout, kernel) -- kernel: a gemm_kernel_choice name (None = the
+# planner's own choice): "tile256" the planner's 256 x 256 kernel (bf16 with B
+# stored N x K: both operands through LDS; otherwise the software-pipelined
+# kernel), "pipe" the software-pipelined kernel with B in registers,
+# "generic128" / "generic256" the generic tiled kernel, "pipe4" the 4-wave
+# pipelined kernel.
 PATHS = [
-    ("bf16", "f32", "bt", "128x128"), ("bf16", "f32", "bt", "256x256"), ("bf16", "f32", "bt", "256x256g"),
-    ("bf16", "bf16", "bt", "128x128"), ("bf16", "bf16", "bt", "256x256"), ("bf16", "bf16", "bt", "256x256g"),
-    ("bf16", "bf16", "bt_preshuffled", "128x128"), ("bf16", "bf16", "bt_preshuffled", "256x256"),
-    ("bf16", "bf16", "bt_preshuffled", "256x256g"), ("bf16", "f32", "bt_preshuffled", "256x256"),
-    ("e4m3", "bf16", "bt", "128x128"), ("e4m3", "bf16", "bt", "256x256"), ("e4m3", "bf16", "bt", "256x256g"),
-    ("e4m3", "bf16", "bt_preshuffled", "128x128"), ("e4m3", "bf16", "bt_preshuffled", "256x256"),
-    ("e4m3", "bf16", "bt_preshuffled", "256x256g"),
-    ("bf16", "f32", "bt", "256x256q"), ("bf16", "bf16", "bt", "256x256q"),
-    ("bf16", "bf16", "bt_preshuffled", "256x256q"), ("bf16", "f32", "bt_preshuffled", "256x256q"),
-    ("e4m3", "bf16", "bt", "256x256q"), ("e4m3", "bf16", "bt_preshuffled", "256x256q"),
-    ("bf16", "f32", "bt", "256x256p"), ("bf16", "bf16", "bt", "256x256p"),
+    ("bf16", "f32", "bt", "generic128"), ("bf16", "f32", "bt", "tile256"), ("bf16", "f32", "bt", "generic256"),
+    ("bf16", "bf16", "bt", "generic128"), ("bf16", "bf16", "bt", "tile256"), ("bf16", "bf16", "bt", "generic256"),
+    ("bf16", "bf16", "bt_preshuffled", "generic128"), ("bf16", "bf16", "bt_preshuffled", "tile256"),
+    ("bf16", "bf16", "bt_preshuffled", "generic256"), ("bf16", "f32", "bt_preshuffled", "tile256"),
+    ("e4m3", "bf16", "bt", "generic128"), ("e4m3", "bf16", "bt", "tile256"), ("e4m3", "bf16", "bt", "generic256"),
+    ("e4m3", "bf16", "bt_preshuffled", "generic128"), ("e4m3", "bf16", "bt_preshuffled", "tile256"),
+    ("e4m3", "bf16", "bt_preshuffled", "generic256"),
+    ("bf16", "f32", "bt", "pipe4"), ("bf16", "bf16", "bt", "pipe4"),
+    ("bf16", "bf16", "bt_preshuffled", "pipe4"), ("bf16", "f32", "bt_preshuffled", "pipe4"),
+    ("e4m3", "bf16", "bt", "pipe4"), ("e4m3", "bf16", "bt_preshuffled", "pipe4"),
+    ("bf16", "f32", "bt", "pipe"), ("bf16", "bf16", "bt", "pipe"),
 ]
 
 
@@ -51,25 +52,9 @@ def _gpu():
 
 
 @pytest.fixture
-def tile_env(monkeypatch):
-    def set_tile(t):
-        monkeypatch.delenv("TGEMM_PIPE", raising=False)
-        monkeypatch.delenv("TGEMM_PIPE_WAVES", raising=False)
-        monkeypatch.delenv("TGEMM_DMA", raising=False)
-        if t and t.endswith("p"):
-            monkeypatch.setenv("TGEMM_DMA", "0")
-            t = t[:-1]
-        if t and t.endswith("q"):
-            monkeypatch.setenv("TGEMM_PIPE_WAVES", "4")
-            t = t[:-1]
-        if t and t.endswith("g"):
-            monkeypatch.setenv("TGEMM_PIPE", "0")
-            t = t[:-1]
-        if t:
-            monkeypatch.setenv("TGEMM_TILE", t)
-        else:
-            monkeypatch.delenv("TGEMM_TILE", raising=False)
-    return set_tile
+def tile_env(plan_opts):
+    """Kernel choice for the plans run_gemm creates (None: the planner's)."""
+    return lambda kernel: plan_opts(kernel=kernel)
 
 
 def exact_check(oracle_mod, inp, M, N, K, dtype, out, layout, scale=(1.0, 1.0)):
@@ -175,11 +160,11 @@ def test_random_within_bound(oracle_mod, tile_env, dtype, out, layout, tile):
 
 # ------------------------------------------------------------------ full-size workloads, sampled
 
-@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_4096", "256x256p"), ("bf16_8192_preshuffled", None),
+@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_4096", "pipe"), ("bf16_8192_preshuffled", None),
                                        ("bf16_skinny_32x8192x8192", None),
                                        ("bf16_skinny_32x8192x8192_preshuffled", None), ("e4m3_8192", None),
-                                       ("bf16_8192_preshuffled", "256x256q"), ("e4m3_8192", "256x256q"),
-                                       ("bf16_4096", "256x256q")])
+                                       ("bf16_8192_preshuffled", "pipe4"), ("e4m3_8192", "pipe4"),
+                                       ("bf16_4096", "pipe4")])
 def test_full_size_sampled(oracle_mod, tile_env, name, tile):
     tile_env(tile)
     w = W.WORKLOADS[name]

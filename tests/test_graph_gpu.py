@@ -24,11 +24,9 @@ def say(*a):
 
 
 @pytest.fixture(autouse=True)
-def _gpu(monkeypatch):
+def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    for k in ("TGEMM_SPLIT", "TGEMM_TILE", "TGEMM_PIPE", "TGEMM_DMA", "TGEMM_PIPE_WAVES"):
-        monkeypatch.delenv(k, raising=False)
     yield
 
 

@@ -16,6 +16,7 @@ import torch
 
 import tiled_gemm_amd as tg
 import workloads as W
+import gpu_util
 from gpu_util import assert_epilogue_within_bound, decode, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
@@ -36,9 +37,8 @@ def say(*a):
 
 
 def set_waves(monkeypatch, waves):
-    monkeypatch.delenv("TGEMM_PIPE_WAVES", raising=False)
-    if waves:
-        monkeypatch.setenv("TGEMM_PIPE_WAVES", waves)
+    # None: the planner's 8-wave kernel; "4": the 4-wave AGPR form.
+    gpu_util.force("pipe4" if waves == "4" else None)
 
 
 def _k_for(fmt, ragged):

@@ -14,6 +14,7 @@ import torch
 
 import tiled_gemm_amd as tg
 import workloads as W
+import gpu_util
 from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
 from oracle import layout as OL
 
@@ -35,13 +36,13 @@ def say(*a):
 
 @pytest.mark.parametrize("R,K", [(200, 1088), (64, 128), (513, 4096)])
 def test_bscale_image_byte_exact(monkeypatch, R, K):
-    # form 0: the 16x16x128 kernels' image (the skinny MX kernels, and the tile
-    # kernel with TGEMM_MXW=0)
+    # form 0: the 16x16x128 kernels' image (the skinny MX kernels, and the
+    # 4-wave tile kernel)
     say("case bscale image", R, K)
-    monkeypatch.setenv("TGEMM_MXW", "0")
+    gpu_util.force("pipe4")
     rng = np.random.default_rng(R + K)
     S = rng.integers(0, 255, (R, K // 32)).astype(np.uint8)
-    with tg.Plan(R, 64, K, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
+    with gpu_util.plan(R, 64, K, tg.GEMM_MXFP8_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
         assert p.info()["scale_form"] == 0
         n = p.bscale_image_bytes(0)
         src = torch.from_numpy(S).cuda()

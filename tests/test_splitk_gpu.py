@@ -15,6 +15,7 @@ import torch
 
 import tiled_gemm_amd as tg
 import workloads as W
+import gpu_util
 from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
@@ -29,17 +30,14 @@ def say(*a):
 
 
 @pytest.fixture(autouse=True)
-def _gpu(monkeypatch):
+def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    for k in ("TGEMM_SPLIT", "TGEMM_TILE", "TGEMM_PIPE", "TGEMM_DMA", "TGEMM_PIPE_WAVES", "TGEMM_PIPE_VARIANT",
-              "TGEMM_DMA_VARIANT"):
-        monkeypatch.delenv(k, raising=False)
     yield
 
 
 def splits_of(M, N, K, dtype, out, layout):
-    with tg.Plan(M, N, K, CODES[(dtype, out)], tg.LAYOUTS[layout]) as p:
+    with gpu_util.plan(M, N, K, CODES[(dtype, out)], tg.LAYOUTS[layout]) as p:
         return p.info()["ws_splits"]
 
 
@@ -73,7 +71,7 @@ def test_split_fp8_exact(oracle_mod, monkeypatch, layout, M):
     # e4m3 integers in [-4, 4], per-tensor scales 0.5 and 0.25 (applied by the
     # reduction); K = 4160 bytes: 33 steps, the last one half full.  At these
     # sizes the planner keeps fp8 unsplit, so the split is forced.
-    monkeypatch.setenv("TGEMM_SPLIT", "4")
+    gpu_util.force(splits=4)
     N, K = 784, 4160
     s = splits_of(M, N, K, "e4m3", "bf16", layout)
     say("case split fp8 exact", layout, M, "splits", s)
@@ -83,7 +81,7 @@ def test_split_fp8_exact(oracle_mod, monkeypatch, layout, M):
 
 
 def test_split_fp8_random_within_bound(oracle_mod, monkeypatch):
-    monkeypatch.setenv("TGEMM_SPLIT", "3")
+    gpu_util.force(splits=3)
     M, N, K = 200, 784, 4160
     inp = W.make_inputs(W.WORKLOADS["e4m3_8192"], M=M, N=N, K=K, seed=4444)
     bits = run_gemm(inp.A, inp.B, M, N, K, "e4m3", "bf16", "bt_preshuffled", scale=(inp.scale_a, inp.scale_b),
@@ -102,9 +100,9 @@ def test_split_int_exact(oracle_mod, monkeypatch, fmt, layout, M):
     # power-of-two dequantisation scales in the reduction's epilogue.  K =
     # 2048 keeps every sum of |a b| below 2^24 (16 steps: two slices, forced,
     # since the planner keeps the partials within B's bytes).
-    monkeypatch.setenv("TGEMM_SPLIT", "2")
+    gpu_util.force(splits=2)
     N, K = 784, 2048
-    with tg.Plan(M, N, K, tg.GEMM_I8_OUT_BF16 if fmt == "i8" else tg.GEMM_W4A8_OUT_BF16, tg.LAYOUTS[layout]) as p:
+    with gpu_util.plan(M, N, K, tg.GEMM_I8_OUT_BF16 if fmt == "i8" else tg.GEMM_W4A8_OUT_BF16, tg.LAYOUTS[layout]) as p:
         s = p.info()["ws_splits"]
     say("case split int exact", fmt, layout, M, "splits", s)
     assert s > 1
@@ -122,7 +120,7 @@ def test_split_int_exact(oracle_mod, monkeypatch, fmt, layout, M):
 @pytest.mark.parametrize("splits", [2, 3, 5, 8])
 def test_split_forced_counts(oracle_mod, monkeypatch, splits):
     # uneven slices (65 steps over 3 or 5 slices), every slice non-empty
-    monkeypatch.setenv("TGEMM_SPLIT", str(splits))
+    gpu_util.force(splits=splits)
     M, N, K = 136, 528, 4160
     assert splits_of(M, N, K, "bf16", "bf16", "bt_preshuffled") == splits
     say("case split forced", splits)

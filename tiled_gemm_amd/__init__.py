@@ -40,11 +40,17 @@ GEMM_EPI_NONE, GEMM_EPI_BIAS, GEMM_EPI_BIAS_RELU, GEMM_EPI_BIAS_SILU, GEMM_EPI_B
 EPILOGUES = {"none": GEMM_EPI_NONE, "bias": GEMM_EPI_BIAS, "bias_relu": GEMM_EPI_BIAS_RELU,
              "bias_silu": GEMM_EPI_BIAS_SILU, "bias_gelu": GEMM_EPI_BIAS_GELU}
 
+# gemm_kernel_choice (gemm_plan_create_opt)
+GEMM_KERNEL_AUTO, GEMM_KERNEL_GENERIC_128, GEMM_KERNEL_GENERIC_256, GEMM_KERNEL_TILE256, GEMM_KERNEL_PIPE, \
+    GEMM_KERNEL_PIPE4 = range(6)
+KERNELS = {"auto": GEMM_KERNEL_AUTO, "generic128": GEMM_KERNEL_GENERIC_128, "generic256": GEMM_KERNEL_GENERIC_256,
+           "tile256": GEMM_KERNEL_TILE256, "pipe": GEMM_KERNEL_PIPE, "pipe4": GEMM_KERNEL_PIPE4}
+
 GEMM_MAX_RANK = 8
 GEMM_VIEW_A, GEMM_VIEW_B, GEMM_VIEW_B_SHUF, GEMM_VIEW_B_SRC, GEMM_VIEW_C, GEMM_VIEW_LDS_A, GEMM_VIEW_TILE = range(7)
 
 EXPORTS = (
-    "gemm_plan_create", "gemm_plan_destroy", "gemm_preshuffled_b_bytes", "gemm_preshuffle_b",
+    "gemm_plan_create", "gemm_plan_create_opt", "gemm_plan_destroy", "gemm_preshuffled_b_bytes", "gemm_preshuffle_b",
     "gemm_run", "gemm_run_ex", "gemm_bscale_image_bytes", "gemm_preshuffle_bscale", "gemm_run_mx",
     "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
     "gemm_layout_idx2crd", "gemm_lds_swizzle", "gemm_tile_of_workgroup", "gemm_workspace_bytes",
@@ -62,6 +68,10 @@ class gemm_epilogue_args(ctypes.Structure):
     _fields_ = [("scale_a", ctypes.c_void_p), ("scale_b", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("scale_a_per_row", ctypes.c_int32), ("scale_b_per_col", ctypes.c_int32),
                 ("epilogue", ctypes.c_int32)]
+
+
+class gemm_plan_options(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("splits", ctypes.c_int32)]
 
 
 class gemm_plan_info(ctypes.Structure):
@@ -92,6 +102,7 @@ def load() -> ctypes.CDLL:
     p32 = ctypes.POINTER(ctypes.c_int32)
     sig = {
         "gemm_plan_create": (vp, [i64, i64, i64, c_int, c_int]),
+        "gemm_plan_create_opt": (vp, [i64, i64, i64, c_int, c_int, ctypes.POINTER(gemm_plan_options)]),
         "gemm_plan_destroy": (None, [vp]),
         "gemm_preshuffled_b_bytes": (ctypes.c_size_t, [vp]),
         "gemm_preshuffle_b": (c_int, [vp, vp, vp, vp]),
@@ -139,6 +150,15 @@ def gemm_plan_create(M: int, N: int, K: int, dtype: int, layout: int) -> int:
     h = load().gemm_plan_create(M, N, K, dtype, layout)
     if not h:
         raise GemmError(-1, "gemm_plan_create", gemm_last_error())
+    return h
+
+
+def gemm_plan_create_opt(M: int, N: int, K: int, dtype: int, layout: int, kernel: int = GEMM_KERNEL_AUTO,
+                         splits: int = 0) -> int:
+    opt = gemm_plan_options(kernel, splits)
+    h = load().gemm_plan_create_opt(M, N, K, dtype, layout, ctypes.byref(opt))
+    if not h:
+        raise GemmError(-1, "gemm_plan_create_opt", gemm_last_error())
     return h
 
 
@@ -249,11 +269,17 @@ LAYOUTS = {"bt": GEMM_LAYOUT_BT, "bt_preshuffled": GEMM_LAYOUT_BT_PRESHUFFLED, "
 
 
 class Plan:
-    """Owns one plan handle; ``with Plan(...) as p:`` destroys it on exit."""
+    """Owns one plan handle; ``with Plan(...) as p:`` destroys it on exit.
+    ``kernel`` (a gemm_kernel_choice) and ``splits`` go to
+    gemm_plan_create_opt; the defaults are gemm_plan_create."""
 
-    def __init__(self, M: int, N: int, K: int, dtype: int, layout: int):
+    def __init__(self, M: int, N: int, K: int, dtype: int, layout: int, kernel: int = GEMM_KERNEL_AUTO,
+                 splits: int = 0):
         self.handle = 0                      # set before create, which may raise
-        self.handle = gemm_plan_create(M, N, K, dtype, layout)
+        if kernel == GEMM_KERNEL_AUTO and splits == 0:
+            self.handle = gemm_plan_create(M, N, K, dtype, layout)
+        else:
+            self.handle = gemm_plan_create_opt(M, N, K, dtype, layout, kernel, splits)
 
     def close(self):
         h, self.handle = self.handle, 0

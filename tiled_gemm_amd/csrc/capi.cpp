@@ -101,10 +101,43 @@ int elem_of(int dtype)
 int64_t scale_groups(int64_t K) { return ((K + 127) / 128 + 3) / 4; }
 int out_of(int dtype) { return dtype == GEMM_BF16_OUT_F32 ? tg::kOutF32 : tg::kOutBf16; }
 
-// Static tile table: the first entry whose predicate holds.  An optional
-// TGEMM_TILE=<bm>x<bn> in the environment forces a tiled variant (sweeps).
-// force256: 256 x 256 tiles with fp32 output (the split-K partial tiles).
-const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = false)
+// Sweep builds (-DTGEMM_SWEEP) also compile the alternative tile
+// configurations of every kernel family and let TGEMM_VARIANT=<family>:<index>
+// pick one of them by its index in the family's table (family: pipe, dma,
+// mxw or skinny).  A default build has neither the alternatives nor this
+// hook: its plans depend on the arguments of gemm_plan_create[_opt] only.
+#ifdef TGEMM_SWEEP
+template <typename V, typename Pred>
+const V *sweep_pick(const char *family, const V *v, int n, Pred ok)
+{
+    const char *e = getenv("TGEMM_VARIANT");
+    const size_t len = strlen(family);
+    if (!e || strncmp(e, family, len) != 0 || e[len] != ':')
+        return nullptr;
+    const int k = atoi(e + len + 1);
+    return k >= 0 && k < n && ok(v[k]) ? &v[k] : nullptr;
+}
+#define TG_SWEEP_PICK(FAMILY, V, N, PRED)                        \
+    if (const auto *sv_ = sweep_pick(FAMILY, V, N, PRED))      \
+        return sv_;
+#else
+#define TG_SWEEP_PICK(FAMILY, V, N, PRED)
+#endif
+
+template <typename V, typename Pred>
+const V *first_of(const V *v, int n, Pred ok)
+{
+    for (int i = 0; i < n; ++i)
+        if (ok(v[i]))
+            return &v[i];
+    return nullptr;
+}
+
+// Static tile table: the first entry of the chosen kernel family whose
+// predicate holds.  `kc` is the caller's gemm_kernel_choice (GEMM_KERNEL_AUTO:
+// the planner's own pick by shape).  force256: 256 x 256 tiles with fp32
+// output (the split-K partial tiles).
+const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, int kc, bool force256 = false)
 {
     int n = 0;
     const tg::TiledVariant *v = tg::tiled_variants(&n);
@@ -112,134 +145,102 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, bool force256 = fals
     const bool bkn = I.layout == GEMM_LAYOUT_BN || I.layout == GEMM_LAYOUT_AT_BN;
     const bool akm = I.layout == GEMM_LAYOUT_AT || I.layout == GEMM_LAYOUT_AT_BN;
     const int elem = elem_of(I.dtype), out = force256 ? tg::kOutF32 : out_of(I.dtype);
+    const bool any256 = kc == GEMM_KERNEL_AUTO || kc == GEMM_KERNEL_TILE256;
+    int nd = 0, nb = 0;
+    const tg::TiledVariant *d = tg::dma_variants(&nd);
+    const tg::TiledVariant *b = tg::pipe_variants(&nb);
     // A stored K x M, and 8-bit B stored K x N: only the LDS-staged 256 x 256
     // kernel reads them.
     if (akm || (bkn && (elem == tg::kFp8 || elem == tg::kI8))) {
-        int nd = 0;
-        const tg::TiledVariant *d = tg::dma_variants(&nd);
-        if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
-            const int k = atoi(e);
-            if (k >= 0 && k < nd && d[k].akm == akm && d[k].elem == elem && d[k].out == out && d[k].bkn == bkn)
-                return &d[k];
-        }
-        for (int i = 0; i < nd; ++i)
-            if (d[i].akm == akm && d[i].elem == elem && d[i].out == out && d[i].bkn == bkn)
-                return &d[i];
-        return nullptr;
+        if (!any256)
+            return nullptr;
+        auto ok = [&](const tg::TiledVariant &x) {
+            return x.akm == akm && x.elem == elem && x.out == out && x.bkn == bkn;
+        };
+        TG_SWEEP_PICK("dma", d, nd, ok)
+        return first_of(d, nd, ok);
     }
     if (is_mx(I.dtype) || is_int(I.dtype)) {
-        // MX and integer operands: only the pipelined 256 x 256 kernel (any
-        // M, N: tails are masked).  TGEMM_PIPE_WAVES=<n> restricts the choice
-        // to n-wave variants.
-        const char *ew = getenv("TGEMM_PIPE_WAVES");
-        const int waves = ew ? atoi(ew) : 0;
-        // MX tiles run on the 32x32x64 kernel (twice the e2m1 rate of the
-        // 16x16x128 form, and 8 waves) unless TGEMM_MXW=0;
-        // TGEMM_MXW_VARIANT=<index> picks one of its sweep variants.
-        const char *e4 = getenv("TGEMM_MXW");
-        if (is_mx(I.dtype) && !(e4 && e4[0] == '0')) {
+        // MX and integer operands: 256 x 256 tiles at any M, N (tails are
+        // masked).  MX tiles run on the 32x32x64 kernel (twice the e2m1 rate
+        // of the 16x16x128 form, and 8 waves); GEMM_KERNEL_PIPE4 picks the
+        // 16x16x128 form on the 4-wave pipelined kernel.  Integer tiles run on
+        // the pipelined kernel, 8 waves, or 4 with GEMM_KERNEL_PIPE4.
+        if (is_mx(I.dtype) && any256) {
             int nw = 0;
             const tg::TiledVariant *x = tg::mxw_variants(&nw);
-            if (const char *ev = getenv("TGEMM_MXW_VARIANT")) {
-                const int k = atoi(ev);
-                if (k >= 0 && k < nw && x[k].elem == elem && x[k].preshuffled == pre)
-                    return &x[k];
-            }
-            for (int i = 0; i < nw; ++i)
-                if (x[i].elem == elem && x[i].preshuffled == pre && (waves == 0 || x[i].wgm * x[i].wgn == waves))
-                    return &x[i];
+            auto ok = [&](const tg::TiledVariant &y) { return y.elem == elem && y.preshuffled == pre; };
+            TG_SWEEP_PICK("mxw", x, nw, ok)
+            return first_of(x, nw, ok);
         }
-        int nb = 0;
-        const tg::TiledVariant *b = tg::pipe_variants(&nb);
-        for (int i = 0; i < nb; ++i)
-            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre &&
-                (waves == 0 || b[i].wgm * b[i].wgn == waves))
-                return &b[i];
-        return nullptr;
+        const int waves = kc == GEMM_KERNEL_PIPE4 ? 4 : 8;
+        if (!(any256 || kc == GEMM_KERNEL_PIPE || kc == GEMM_KERNEL_PIPE4) || (is_mx(I.dtype) && waves != 4))
+            return nullptr;
+        auto ok = [&](const tg::TiledVariant &y) {
+            return y.elem == elem && y.out == out && y.preshuffled == pre && y.wgm * y.wgn == waves;
+        };
+        TG_SWEEP_PICK("pipe", b, nb, ok)
+        return first_of(b, nb, ok);
     }
-    int want_bm = 0, want_bn = 0;
-    if (force256)
-        want_bm = want_bn = 256;
-    else if (const char *e = getenv("TGEMM_TILE"))
-        if (sscanf(e, "%dx%d", &want_bm, &want_bn) != 2)
-            want_bm = want_bn = 0;
-    if (!want_bm) {
+    int tile = 0;
+    if (force256 || kc == GEMM_KERNEL_TILE256 || kc == GEMM_KERNEL_PIPE || kc == GEMM_KERNEL_PIPE4 ||
+        kc == GEMM_KERNEL_GENERIC_256)
+        tile = 256;
+    else if (kc == GEMM_KERNEL_GENERIC_128)
+        tile = 128;
+    else {
         const int64_t big = ((I.M + 255) / 256) * ((I.N + 255) / 256);
-        want_bm = want_bn = big >= 128 ? 256 : 128;
+        tile = big >= 128 ? 256 : 128;
     }
-    // 256 x 256 tiles.  bf16 with B stored N x K or K x N: both operands
-    // staged through LDS by the loads' own LDS writes (gemm_dma.hip: whole
-    // 128-byte lines of B, where the register-staged kernel's MFMA lane order
-    // can only load half lines; K x N through the transpose read).
-    // TGEMM_DMA=0, or a forced pipelined variant or wave count, selects the
-    // other kernels; TGEMM_DMA_VARIANT=<index> picks a sweep variant.
-    const char *pp = getenv("TGEMM_PIPE");
-    if (want_bm == 256 && want_bn == 256 && !(pp && pp[0] == '0')) {
-        int nd = 0;
-        const tg::TiledVariant *d = tg::dma_variants(&nd);
-        if (const char *e = getenv("TGEMM_DMA_VARIANT")) {
-            const int k = atoi(e);
-            if (k >= 0 && k < nd && d[k].elem == elem && d[k].out == out && d[k].preshuffled == pre &&
-                d[k].bkn == bkn && !d[k].akm)
-                return &d[k];
-        }
-        const char *dm = getenv("TGEMM_DMA");
-        if (elem == tg::kBf16 && !pre && !(dm && dm[0] == '0') && !getenv("TGEMM_PIPE_VARIANT") &&
-            !getenv("TGEMM_PIPE_WAVES")) {
-            for (int i = 0; i < nd; ++i)
-                if (d[i].elem == elem && d[i].out == out && !d[i].preshuffled && d[i].bkn == bkn && !d[i].akm)
-                    return &d[i];
+    if (tile == 256 && any256) {
+        // bf16 with B stored N x K or K x N: both operands staged through LDS
+        // by the loads' own LDS writes (gemm_dma.hip: whole 128-byte lines of
+        // B, where the register-staged kernel's MFMA lane order can only load
+        // half lines; K x N through the transpose read).
+        if (elem == tg::kBf16 && !pre) {
+            auto ok = [&](const tg::TiledVariant &x) {
+                return x.elem == elem && x.out == out && !x.preshuffled && x.bkn == bkn && !x.akm;
+            };
+            TG_SWEEP_PICK("dma", d, nd, ok)
+            return first_of(d, nd, ok);
         }
     }
     // Otherwise 256 x 256 tiles run the software-pipelined kernel (B N x K or
-    // pre-shuffled), unless TGEMM_PIPE=0 asks for the generic one.
-    // TGEMM_PIPE_VARIANT=<index> picks a sweep variant of the same element
-    // type, output and layout.
-    if (want_bm == 256 && want_bn == 256 && !bkn && !(pp && pp[0] == '0')) {
-        int nb = 0;
-        const tg::TiledVariant *b = tg::pipe_variants(&nb);
-        if (const char *e = getenv("TGEMM_PIPE_VARIANT")) {
-            const int k = atoi(e);
-            if (k >= 0 && k < nb && b[k].elem == elem && b[k].out == out && b[k].preshuffled == pre)
-                return &b[k];
-        }
-        // TGEMM_PIPE_WAVES=<n> restricts the choice to n-wave variants.
-        const char *ew = getenv("TGEMM_PIPE_WAVES");
-        const int waves = ew ? atoi(ew) : 0;
-        for (int i = 0; i < nb; ++i)
-            if (b[i].elem == elem && b[i].out == out && b[i].preshuffled == pre &&
-                (waves == 0 || b[i].wgm * b[i].wgn == waves))
-                return &b[i];
+    // pre-shuffled, B straight to registers), 8 waves, or 4 waves with AGPR
+    // accumulators for GEMM_KERNEL_PIPE4.
+    if (tile == 256 && !bkn && kc != GEMM_KERNEL_GENERIC_256) {
+        const int waves = kc == GEMM_KERNEL_PIPE4 ? 4 : 8;
+        auto ok = [&](const tg::TiledVariant &y) {
+            return y.elem == elem && y.out == out && y.preshuffled == pre && y.wgm * y.wgn == waves;
+        };
+        TG_SWEEP_PICK("pipe", b, nb, ok)
+        return first_of(b, nb, ok);
     }
-    for (int i = 0; i < n; ++i)
-        if (v[i].bm == want_bm && v[i].bn == want_bn && v[i].elem == elem && v[i].out == out &&
-            v[i].preshuffled == pre && v[i].bkn == bkn)
-            return &v[i];
-    return nullptr;
+    if (kc == GEMM_KERNEL_PIPE || kc == GEMM_KERNEL_PIPE4)
+        return nullptr;
+    return first_of(v, n, [&](const tg::TiledVariant &x) {
+        return x.bm == tile && x.bn == tile && x.elem == elem && x.out == out && x.preshuffled == pre &&
+               x.bkn == bkn;
+    });
 }
 
-const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
+const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I, int kc)
 {
     // Skinny kernels: bf16, fp8 and int8 with B N x K or pre-shuffled; W4A8
-    // and the MX formats with B pre-shuffled.
+    // and the MX formats with B pre-shuffled.  Only the planner's own choice
+    // (GEMM_KERNEL_AUTO) takes them.
     const bool pre = I.layout == GEMM_LAYOUT_BT_PRESHUFFLED;
-    if ((I.layout != GEMM_LAYOUT_BT && !pre) || I.M < 1 || I.M > 64 || getenv("TGEMM_TILE") ||
+    if ((I.layout != GEMM_LAYOUT_BT && !pre) || I.M < 1 || I.M > 64 || kc != GEMM_KERNEL_AUTO ||
         ((I.dtype == GEMM_W4A8_OUT_BF16 || is_mx(I.dtype)) && !pre))
         return nullptr;
     const int mb = I.M <= 16 ? 1 : (I.M <= 32 ? 2 : 4);
     int n = 0;
     const tg::SkinnyVariant *v = tg::skinny_variants(&n);
-    if (const char *e = getenv("TGEMM_SKINNY_VARIANT")) {
-        const int k = atoi(e);
-        if (k >= 0 && k < n && v[k].mblocks == mb && v[k].elem == elem_of(I.dtype) && v[k].out == out_of(I.dtype) &&
-            v[k].preshuffled == pre)
-            return &v[k];
-    }
-    for (int i = 0; i < n; ++i)
-        if (v[i].mblocks == mb && v[i].elem == elem_of(I.dtype) && v[i].out == out_of(I.dtype) &&
-            v[i].preshuffled == pre)
-            return &v[i];
-    return nullptr;
+    auto ok = [&](const tg::SkinnyVariant &x) {
+        return x.mblocks == mb && x.elem == elem_of(I.dtype) && x.out == out_of(I.dtype) && x.preshuffled == pre;
+    };
+    TG_SWEEP_PICK("skinny", v, n, ok)
+    return first_of(v, n, ok);
 }
 
 // Split K for the workspace entry point.  A problem whose 256 x 256 tiles
@@ -248,14 +249,16 @@ const tg::SkinnyVariant *pick_skinny(const gemm_plan_info &I)
 // s slices: tiles * s workgroups each write an fp32 partial tile, and a
 // reduction kernel sums the slices in order and applies the epilogue.  s is
 // the largest power of two with tiles * s <= 256, at least 8 K steps (1 KiB
-// of K) per slice and partials no larger than B; TGEMM_SPLIT=<s> forces it
-// (sweeps; 1 disables).
-void plan_split(gemm_plan *p)
+// of K) per slice and partials no larger than B; `forced` (the caller's
+// gemm_plan_options.splits) overrides it, 1 disabling the split.
+void plan_split(gemm_plan *p, int kc, int forced)
 {
     const gemm_plan_info &I = p->info;
     p->splits = 1;
     p->split_steps = p->k_tiles;
     const int elem = elem_of(I.dtype);
+    if (kc == GEMM_KERNEL_GENERIC_128 || kc == GEMM_KERNEL_GENERIC_256)   // the generic kernel does not split
+        return;
     if (I.kernel != 0 || I.M == 0 || I.N == 0 || I.K == 0 || is_mx(I.dtype) ||
         (I.layout != GEMM_LAYOUT_BT && I.layout != GEMM_LAYOUT_BT_PRESHUFFLED) ||
         I.N * 4 * 256 >= (int64_t(1) << 31))
@@ -263,9 +266,8 @@ void plan_split(gemm_plan *p)
     const int64_t tm = (I.M + 255) / 256, tn = (I.N + 255) / 256;
     const int64_t tiles = tm * tn;
     int s = 1;
-    const char *e = getenv("TGEMM_SPLIT");
-    if (e) {
-        s = atoi(e);
+    if (forced > 0) {
+        s = forced;
     } else if (elem == tg::kFp8 && I.tile_m != 256) {
         // fp8 B is half the bytes, so the fp32 partials weigh twice as much:
         // measured, splitting beats the 128 x 128 tiles' plan only where that
@@ -284,7 +286,7 @@ void plan_split(gemm_plan *p)
     const int per = (p->k_tiles + s - 1) / s;
     if ((int64_t)(s - 1) * per >= p->k_tiles)           // every slice non-empty
         return;
-    const tg::TiledVariant *v = pick_tiled(I, true);
+    const tg::TiledVariant *v = pick_tiled(I, kc == GEMM_KERNEL_AUTO ? GEMM_KERNEL_TILE256 : kc, true);
     // Only the pipelined and the LDS-staged kernels read the split fields.
     int np = 0, nd = 0;
     const tg::TiledVariant *pv = tg::pipe_variants(&np), *dv = tg::dma_variants(&nd);
@@ -380,8 +382,19 @@ extern "C" {
 
 const char *gemm_last_error(void) { return g_last_error.c_str(); }
 
-gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout)
+gemm_plan *gemm_plan_create_opt(int64_t M, int64_t N, int64_t K, int dtype, int layout,
+                                const gemm_plan_options *opt)
 {
+    const int kc = opt ? opt->kernel : GEMM_KERNEL_AUTO;
+    const int forced_splits = opt ? opt->splits : 0;
+    if (kc < GEMM_KERNEL_AUTO || kc > GEMM_KERNEL_PIPE4) {
+        fail(GEMM_ERR_INVALID_ARG, "unknown kernel choice %d", kc);
+        return nullptr;
+    }
+    if (forced_splits < 0 || forced_splits > 64) {
+        fail(GEMM_ERR_INVALID_ARG, "splits=%d outside 0..64", forced_splits);
+        return nullptr;
+    }
     if (dtype < GEMM_BF16_OUT_F32 || dtype > GEMM_W4A8_OUT_BF16) {
         fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
         return nullptr;
@@ -491,7 +504,7 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
     I.tile_k_bytes = tg::kTileKBytes;
     I.split_k = 1;
 
-    if ((p->skinny = pick_skinny(I)) != nullptr) {
+    if ((p->skinny = pick_skinny(I, kc)) != nullptr) {
         I.kernel = 1;
         I.tile_m = p->skinny->mblocks * 16;
         I.tile_n = tg::kSkinnyTileN;
@@ -503,7 +516,7 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         I.group_m = 1;
         I.split_k = p->skinny->waves;
         I.grid = I.tiles_n;
-    } else if ((p->tiled = pick_tiled(I)) != nullptr) {
+    } else if ((p->tiled = pick_tiled(I, kc)) != nullptr) {
         I.kernel = 0;
         I.tile_m = p->tiled->bm;
         I.tile_n = p->tiled->bn;
@@ -524,7 +537,7 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         I.grid = (int32_t)grid;
     } else {
         delete p;
-        fail(GEMM_ERR_UNSUPPORTED, "no kernel variant for this dtype/layout/tile");
+        fail(GEMM_ERR_UNSUPPORTED, "no kernel for this dtype/layout%s", kc ? " and kernel choice" : "");
         return nullptr;
     }
     if (I.lds_bytes > kLdsLimit) {
@@ -532,12 +545,17 @@ gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layo
         fail(GEMM_ERR_UNSUPPORTED, "tile needs %d bytes of LDS (> 160 KiB)", I.lds_bytes);
         return nullptr;
     }
-    plan_split(p);
+    plan_split(p, kc, forced_splits);
     I.ws_splits = p->splits;
     I.ws_grid = p->splits > 1 ? p->split_grid : I.grid;
     I.scale_form = wide_scales(p) ? 1 : 0;
     ok();
     return p;
+}
+
+gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, int dtype, int layout)
+{
+    return gemm_plan_create_opt(M, N, K, dtype, layout, nullptr);
 }
 
 void gemm_plan_destroy(gemm_plan *plan) { delete plan; }

@@ -445,38 +445,41 @@ static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
                  &launch_dma<ELEM, kOutBf16, false, 1, 8, 2, BKN, true>, BKN, true}
 
 static const TiledVariant kDma[] = {
-    TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // 0
-    TG_DMA(kBf16, kOutBf16, false, 2, 4, 4),   // 1
-    TG_DMA(kBf16, kOutF32, false, 2, 4, 4),    // 2
-    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // 3
-    TG_DMA(kFp8, kOutBf16, false, 1, 8, 2),    // 4
-    TG_DMA(kFp8, kOutBf16, true, 1, 8, 3),     // 5
-    TG_DMA(kBf16, kOutBf16, true, 2, 4, 6),    // 6
-    TG_DMA_KN(kOutBf16, 2, 4, 4),              // 7: B stored K x N
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // B N x K
+    TG_DMA(kBf16, kOutF32, false, 2, 4, 4),
+    TG_DMA_KN(kOutBf16, 2, 4, 4),              // B stored K x N
     TG_DMA_KN(kOutF32, 2, 4, 4),
-    TG_DMA_KN(kOutBf16, 2, 4, 6),
     // A stored K x M: prefetch distance 2 (a K x M fragment is two transpose
     // reads and their addresses; at 4 the kernel spilled 19-38 VGPRs and ran
     // 13-17% slower)
-    TG_DMA_L(kOutBf16, 2, 4, 2, false, true),  // 10: A stored K x M, B N x K
+    TG_DMA_L(kOutBf16, 2, 4, 2, false, true),  // A stored K x M, B N x K
     TG_DMA_L(kOutF32, 2, 4, 2, false, true),
-    TG_DMA_L(kOutBf16, 2, 4, 2, true, true),   // 12: A stored K x M, B K x N
+    TG_DMA_L(kOutBf16, 2, 4, 2, true, true),   // A stored K x M, B K x N
     TG_DMA_L(kOutF32, 2, 4, 2, true, true),
-    TG_DMA_KN8(1, 8, 3),                       // 14: fp8, B stored K x N
-    TG_DMA_KN8(1, 8, 2),
-    TG_DMA_KN8E(kI8, 1, 8, 3),                 // 16: int8, B stored K x N
-    // sweep: other prefetch distances for the transposed layouts
-    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 17: A K x M
-    TG_DMA_L(kOutBf16, 2, 4, 3, false, true),
-    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 19: A K x M, B K x N
-    TG_DMA_L(kOutBf16, 2, 4, 3, true, true),
-    TG_DMA_KN(kOutBf16, 2, 4, 3),              // 21: B K x N
-    TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 22: B N x K
+    TG_DMA_KN8(1, 8, 3),                       // fp8, B stored K x N
+    TG_DMA_KN8E(kI8, 1, 8, 3),                 // int8, B stored K x N
     // 8-bit A stored K x M (8-bit transpose reads on both operands)
-    TG_DMA_AT8(kFp8, false),                   // 23: fp8, A K x M, B N x K
-    TG_DMA_AT8(kFp8, true),                    //     fp8, A K x M, B K x N
-    TG_DMA_AT8(kI8, false),                    // 25: int8, A K x M, B N x K
-    TG_DMA_AT8(kI8, true),                     //     int8, A K x M, B K x N
+    TG_DMA_AT8(kFp8, false),                   // fp8, A K x M, B N x K
+    TG_DMA_AT8(kFp8, true),                    // fp8, A K x M, B K x N
+    TG_DMA_AT8(kI8, false),                    // int8, A K x M, B N x K
+    TG_DMA_AT8(kI8, true),                     // int8, A K x M, B K x N
+#ifdef TGEMM_SWEEP
+    // alternatives (sweep builds only): other prefetch distances, and fp8 and
+    // pre-shuffled B through LDS
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 4),   // 14
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // 15
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 2),
+    TG_DMA(kFp8, kOutBf16, true, 1, 8, 3),
+    TG_DMA(kBf16, kOutBf16, true, 2, 4, 6),    // 18
+    TG_DMA_KN(kOutBf16, 2, 4, 6),
+    TG_DMA_KN8(1, 8, 2),                       // 20
+    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 21: A K x M
+    TG_DMA_L(kOutBf16, 2, 4, 3, false, true),
+    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 23: A K x M, B K x N
+    TG_DMA_L(kOutBf16, 2, 4, 3, true, true),
+    TG_DMA_KN(kOutBf16, 2, 4, 3),              // 25: B K x N
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 26: B N x K
+#endif
 };
 
 const TiledVariant *dma_variants(int *count)

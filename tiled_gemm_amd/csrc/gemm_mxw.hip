@@ -378,17 +378,20 @@ static hipError_t launch_mxw(const TiledArgs &a, hipStream_t s)
                  &launch_mxw<ELEM, BPRE, WAVES, PD>}
 
 // The first variant of each layout is the planner's choice; the rest are
-// alternatives selectable by index (TGEMM_MXW_VARIANT).
+// alternatives compiled into sweep builds only.
 static const TiledVariant kMxw[] = {
     TG_MXW(kMx4, true, 8, 6),
     TG_MXW(kMx4, false, 8, 6),
     TG_MXW(kMx8, true, 8, 2),     // 2 (e4m3 fragments are 8 VGPRs: deeper prefetch spills)
     TG_MXW(kMx8, false, 8, 2),
+#ifdef TGEMM_SWEEP
+    // alternatives (sweep builds only): prefetch distances, one wave per SIMD
     TG_MXW(kMx4, true, 8, 4),     // 4
     TG_MXW(kMx4, true, 8, 5),
     TG_MXW(kMx4, true, 8, 7),
     TG_MXW(kMx4, true, 4, 6),     // 7: one wave per SIMD
     TG_MXW(kMx4, false, 4, 6),
+#endif
 };
 
 const TiledVariant *mxw_variants(int *count)

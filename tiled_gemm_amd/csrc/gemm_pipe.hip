@@ -522,8 +522,8 @@ static hipError_t launch_pipe(const TiledArgs &a, hipStream_t s)
                  &launch_pipe<ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA, (WGM * WGN == 4), SPREAD>}
 #define TG_PIPE(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA) TG_PIPE_S(ELEM, OUT, BPRE, WGM, WGN, NS, PD, ADMA, false)
 
-// The first variant of each (elem, out, layout) is the planner's choice; the
-// rest are alternatives selectable by index with TGEMM_PIPE_VARIANT (sweeps).
+// The first 8-wave and the first 4-wave variant of each (elem, out, layout)
+// are the ones a plan can get; sweep builds add alternatives.
 static const TiledVariant kPipe[] = {
     TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 6, true, true),
     TG_PIPE_S(kBf16, kOutF32, true, 1, 8, 4, 6, true, true),
@@ -552,21 +552,23 @@ static const TiledVariant kPipe[] = {
     TG_PIPE_S(kI8, kOutBf16, false, 1, 4, 4, 12, true, true),
     TG_PIPE_S(kW4A8, kOutBf16, true, 1, 4, 4, 12, true, true),
     TG_PIPE_S(kW4A8, kOutBf16, false, 1, 4, 4, 12, true, true),
-    // sweep alternatives
-    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),           // 24: loads in bursts
-    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 5, true, true),   // 25
-    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 7, true, true),   // 26
-    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 5, 6, true, true),   // 27
-    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 28
-    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 29
-    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 30: loads in bursts
     // fp8 and integer operands with fp32 output: the split-K partial tiles
-    TG_PIPE_S(kFp8, kOutF32, false, 1, 8, 4, 3, true, true),    // 31
+    TG_PIPE_S(kFp8, kOutF32, false, 1, 8, 4, 3, true, true),    // 24
     TG_PIPE_S(kFp8, kOutF32, true, 1, 8, 4, 3, true, true),
-    TG_PIPE_S(kI8, kOutF32, true, 1, 8, 4, 6, true, true),      // 33
+    TG_PIPE_S(kI8, kOutF32, true, 1, 8, 4, 6, true, true),      // 26
     TG_PIPE_S(kI8, kOutF32, false, 1, 8, 4, 6, true, true),
     TG_PIPE_S(kW4A8, kOutF32, true, 1, 8, 4, 6, true, true),
     TG_PIPE_S(kW4A8, kOutF32, false, 1, 8, 4, 6, true, true),
+#ifdef TGEMM_SWEEP
+    // alternatives (sweep builds only)
+    TG_PIPE(kBf16, kOutBf16, true, 1, 8, 4, 4, true),           // 30: loads in bursts
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 5, true, true),   // 31
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 4, 7, true, true),   // 32
+    TG_PIPE_S(kBf16, kOutBf16, true, 1, 8, 5, 6, true, true),   // 33
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 2, true, true),   // 34
+    TG_PIPE_S(kFp8, kOutBf16, false, 1, 8, 4, 4, true, true),   // 35
+    TG_PIPE(kFp8, kOutBf16, false, 1, 8, 4, 3, true),           // 36: loads in bursts
+#endif
 };
 
 const TiledVariant *pipe_variants(int *count)

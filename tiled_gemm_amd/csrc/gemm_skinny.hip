@@ -487,41 +487,43 @@ static hipError_t launch_skinny_pre(const SkinnyArgs &a, int grid, hipStream_t s
 #define TG_SKINNY_PRE(MB, ELEM, OUT, WAVES, DEPTH) TG_SKINNY_PRE_L(MB, ELEM, OUT, WAVES, DEPTH, false)
 
 // The first variant of each (rows, elem, out, B layout) is the planner's choice; the
-// rest are alternatives selectable by index with TGEMM_SKINNY_VARIANT.
+// rest are alternatives compiled into sweep builds only.
 static const SkinnyVariant kSkinny[] = {
     TG_SKINNY(1, kBf16, kOutBf16, 8, 3, true), TG_SKINNY(2, kBf16, kOutBf16, 8, 2, true),
     TG_SKINNY(4, kBf16, kOutBf16, 4, 3, true), TG_SKINNY(1, kBf16, kOutF32, 8, 3, true),
     TG_SKINNY(2, kBf16, kOutF32, 8, 2, true),  TG_SKINNY(4, kBf16, kOutF32, 4, 3, true),
     TG_SKINNY(1, kFp8, kOutBf16, 8, 3, true),  TG_SKINNY(2, kFp8, kOutBf16, 8, 2, true),
     TG_SKINNY(4, kFp8, kOutBf16, 4, 3, true),
-    // alternatives for the 32-row bf16 shape
-    TG_SKINNY(2, kBf16, kOutBf16, 8, 2, false), TG_SKINNY(2, kBf16, kOutBf16, 4, 4, true),
-    TG_SKINNY(2, kBf16, kOutBf16, 2, 8, true),
     // B pre-shuffled (register-staged B, steps in runs, no rotation)
-    TG_SKINNY_PRE(1, kBf16, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kBf16, kOutBf16, 12, 2),     // 12
+    TG_SKINNY_PRE(1, kBf16, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kBf16, kOutBf16, 12, 2),     // 9
     TG_SKINNY_PRE(4, kBf16, kOutBf16, 8, 2),  TG_SKINNY_PRE(1, kBf16, kOutF32, 12, 2),
     TG_SKINNY_PRE(2, kBf16, kOutF32, 12, 2),  TG_SKINNY_PRE(4, kBf16, kOutF32, 8, 2),
-    TG_SKINNY_PRE(1, kFp8, kOutBf16, 12, 2),  TG_SKINNY_PRE(2, kFp8, kOutBf16, 12, 2),      // 18
+    TG_SKINNY_PRE(1, kFp8, kOutBf16, 12, 2),  TG_SKINNY_PRE(2, kFp8, kOutBf16, 12, 2),      // 15
     TG_SKINNY_PRE(4, kFp8, kOutBf16, 8, 2),
-    // alternatives for the 32-row bf16 shape: (waves, stages, B via LDS, order)
-    TG_SKINNY_PRE_O(2, kBf16, kOutBf16, 8, 4, false, 0), TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 4),   // 21
-    TG_SKINNY_PRE(2, kBf16, kOutBf16, 16, 2), TG_SKINNY_PRE(2, kBf16, kOutBf16, 12, 3),
-    TG_SKINNY_PRE_L(2, kBf16, kOutBf16, 8, 2, true), TG_SKINNY_PRE_O(2, kBf16, kOutBf16, 12, 2, false, 3), // 25
-    TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 3), TG_SKINNY_PRE(2, kBf16, kOutBf16, 10, 2),
-    // alternative for the 64-row shape
-    TG_SKINNY_PRE(4, kBf16, kOutBf16, 4, 4),                                                    // 29
     // integer operands: int8 with B N x K or pre-shuffled, W4A8 pre-shuffled
-    TG_SKINNY(1, kI8, kOutBf16, 8, 3, true), TG_SKINNY(2, kI8, kOutBf16, 8, 2, true),          // 30
+    TG_SKINNY(1, kI8, kOutBf16, 8, 3, true), TG_SKINNY(2, kI8, kOutBf16, 8, 2, true),          // 18
     TG_SKINNY(4, kI8, kOutBf16, 4, 3, true),
-    TG_SKINNY_PRE(1, kI8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kI8, kOutBf16, 12, 2),             // 33
+    TG_SKINNY_PRE(1, kI8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kI8, kOutBf16, 12, 2),             // 21
     TG_SKINNY_PRE(4, kI8, kOutBf16, 8, 2),
-    TG_SKINNY_PRE(1, kW4A8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kW4A8, kOutBf16, 12, 2),         // 36
+    TG_SKINNY_PRE(1, kW4A8, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kW4A8, kOutBf16, 12, 2),         // 24
     TG_SKINNY_PRE(4, kW4A8, kOutBf16, 8, 2),
     // MX block-scaled operands, B pre-shuffled
-    TG_SKINNY_PRE(1, kMx8, kOutBf16, 8, 4), TG_SKINNY_PRE(2, kMx8, kOutBf16, 8, 4),           // 39
+    TG_SKINNY_PRE(1, kMx8, kOutBf16, 8, 4), TG_SKINNY_PRE(2, kMx8, kOutBf16, 8, 4),           // 27
     TG_SKINNY_PRE(4, kMx8, kOutBf16, 4, 4),
-    TG_SKINNY_PRE(1, kMx4, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kMx4, kOutBf16, 12, 2),         // 42
+    TG_SKINNY_PRE(1, kMx4, kOutBf16, 12, 2), TG_SKINNY_PRE(2, kMx4, kOutBf16, 12, 2),         // 30
     TG_SKINNY_PRE(4, kMx4, kOutBf16, 8, 2),
+#ifdef TGEMM_SWEEP
+    // alternatives (sweep builds only) for the 32-row bf16 shape: B N x K
+    TG_SKINNY(2, kBf16, kOutBf16, 8, 2, false), TG_SKINNY(2, kBf16, kOutBf16, 4, 4, true),     // 33
+    TG_SKINNY(2, kBf16, kOutBf16, 2, 8, true),
+    // B pre-shuffled: (waves, stages, B via LDS, order)
+    TG_SKINNY_PRE_O(2, kBf16, kOutBf16, 8, 4, false, 0), TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 4),   // 36
+    TG_SKINNY_PRE(2, kBf16, kOutBf16, 16, 2), TG_SKINNY_PRE(2, kBf16, kOutBf16, 12, 3),
+    TG_SKINNY_PRE_L(2, kBf16, kOutBf16, 8, 2, true), TG_SKINNY_PRE_O(2, kBf16, kOutBf16, 12, 2, false, 3), // 40
+    TG_SKINNY_PRE(2, kBf16, kOutBf16, 8, 3), TG_SKINNY_PRE(2, kBf16, kOutBf16, 10, 2),
+    // the 64-row shape
+    TG_SKINNY_PRE(4, kBf16, kOutBf16, 4, 4),                                                    // 44
+#endif
 };
 
 const SkinnyVariant *skinny_variants(int *count)
