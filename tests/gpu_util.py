@@ -165,14 +165,20 @@ def assert_epilogue_within_bound(Y, Y_ref, S_z, Z_abs, bias_abs, dtype, kind, wh
     return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
 
 
-def sample_entries(M: int, N: int, n_random: int, seed: int):
-    """Rows 0 and M-1 in full, columns 0 and N-1 in full, and random entries."""
+def block_entries(M: int, N: int, seed: int, block: int = 16):
+    """Entries of C to check at full size: one in every block x block tile,
+    at a seeded random position inside the tile (so each of the 256 positions
+    of a 16 x 16 MFMA output fragment is hit about M * N / 65536 times, and
+    every tile of every workgroup, wave and MFMA is visited), plus rows 0 and
+    M - 1 and columns 0 and N - 1 in full."""
     rng = np.random.default_rng(seed)
-    rows = [np.zeros(N, np.int64), np.full(N, M - 1, np.int64), np.arange(M), np.arange(M),
-            rng.integers(0, M, n_random)]
-    cols = [np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1, np.int64),
-            rng.integers(0, N, n_random)]
-    return np.concatenate(rows), np.concatenate(cols)
+    bm, bn = -(-M // block), -(-N // block)
+    slot = rng.integers(0, block * block, size=(bm, bn))
+    r = np.minimum(np.arange(bm)[:, None] * block + slot // block, M - 1).reshape(-1)
+    c = np.minimum(np.arange(bn)[None, :] * block + slot % block, N - 1).reshape(-1)
+    rows = [np.zeros(N, np.int64), np.full(N, M - 1, np.int64), np.arange(M), np.arange(M), r]
+    cols = [np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1, np.int64), c]
+    return np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64)
 
 
 def force(kernel=None, splits=0):

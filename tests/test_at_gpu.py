@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
+from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, block_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,7 @@ def test_at_full_size_sampled(oracle_mod, name):
     say("case at full-size", w.name)
     inp = W.make_inputs(w)
     bits = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout)
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    rows, cols = block_entries(w.M, w.N, seed=w.seed)
     C, S = oracle_mod.gemm_at_entries(inp.A, inp.B, rows, cols, b_kn=w.layout == "at_bn")
     r = assert_within_bound(decode(bits[rows, cols]), C, S, "bf16", w.name)
     say("  worst err/bound", r)
@@ -145,7 +145,7 @@ def test_at_fp8_random_4096_sampled(oracle_mod, layout):
     A_km = np.ascontiguousarray(inp.A.T)
     B = np.ascontiguousarray(inp.B.T) if layout == "at_bn" else inp.B
     bits = run_gemm(A_km, B, M, N, K, "e4m3", "bf16", layout, scale=(inp.scale_a, inp.scale_b))
-    rows, cols = sample_entries(M, N, 8192, seed=72)
+    rows, cols = block_entries(M, N, seed=72)
     sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
     C, S = oracle_mod.gemm_at_entries(A_km, B, rows, cols, dtype="e4m3", sigma=sigma, b_kn=layout == "at_bn")
     r = assert_within_bound(decode(bits[rows, cols]), C, S, "e4m3", "at fp8 %s 4096^3" % layout)

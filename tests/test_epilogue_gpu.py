@@ -14,7 +14,7 @@ import torch
 
 import workloads as W
 import gpu_util
-from gpu_util import assert_epilogue_within_bound, decode, run_gemm, sample_entries
+from gpu_util import assert_epilogue_within_bound, decode, run_gemm, block_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,7 @@ def test_epilogue_full_size_sampled(oracle_mod, monkeypatch, name, kind):
     sb = rng.uniform(0.5, 2.0, w.N) * inp.scale_b
     e = dict(scale_a=sa, scale_b=sb, bias=rng.normal(0.0, 1.0, w.N), kind=kind)
     bits = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, epi=e)
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    rows, cols = block_entries(w.M, w.N, seed=w.seed)
     acc, S = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype)
     want = oracle_mod.epilogue_entries(acc, sa[rows], sb[cols], e["bias"][cols], kind)
     scale = np.abs(sa[rows] * sb[cols])

@@ -7,6 +7,7 @@ launch configuration the benchmark times and are checked on sampled entries.
 """
 import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import torch
 
 import tiled_gemm_amd as tg
 import workloads as W
-from gpu_util import assert_within_bound, decode, run_gemm, sample_entries
+from gpu_util import assert_within_bound, decode, run_gemm, block_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -158,14 +159,33 @@ def test_random_within_bound(oracle_mod, tile_env, dtype, out, layout, tile):
     say("  worst err/bound", r)
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled
+# ------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_4096", "pipe"), ("bf16_8192_preshuffled", None),
+# Workloads whose whole C the oracle computes within seconds on the host: the
+# 4096^3 GEMM (1.4e11 multiply-adds) and the decode shapes.  The 8192^3 ones
+# are checked on one entry of every 16 x 16 block of C plus the border rows
+# and columns (gpu_util.block_entries).
+FULL_C = ("bf16_4096", "bf16_skinny_32x8192x8192", "bf16_skinny_32x8192x8192_preshuffled")
+_full_ref = {}
+
+
+def _oracle_full(oracle_mod, name, inp):
+    if name not in _full_ref:
+        w = W.WORKLOADS[name]
+        t0 = time.perf_counter()
+        sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+        _full_ref[name] = oracle_mod.gemm_bt(inp.A, inp.B, dtype=w.dtype, sigma=sigma)
+        say("  oracle: whole C of %s in %.1f s on %d threads" % (name, time.perf_counter() - t0,
+                                                                 oracle_mod.threads()))
+    return _full_ref[name]
+
+
+@pytest.mark.parametrize("name,tile", [("bf16_4096", None), ("bf16_4096", "pipe"), ("bf16_4096", "pipe4"),
+                                       ("bf16_8192_preshuffled", None), ("bf16_8192_preshuffled", "pipe4"),
                                        ("bf16_skinny_32x8192x8192", None),
                                        ("bf16_skinny_32x8192x8192_preshuffled", None), ("e4m3_8192", None),
-                                       ("bf16_8192_preshuffled", "pipe4"), ("e4m3_8192", "pipe4"),
-                                       ("bf16_4096", "pipe4")])
-def test_full_size_sampled(oracle_mod, tile_env, name, tile):
+                                       ("e4m3_8192", "pipe4"), ("e4m3_8192_preshuffled", None)])
+def test_full_size(oracle_mod, tile_env, name, tile):
     tile_env(tile)
     w = W.WORKLOADS[name]
     say("case full-size", name, tile)
@@ -173,13 +193,21 @@ def test_full_size_sampled(oracle_mod, tile_env, name, tile):
     C_bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout,
                             scale=(inp.scale_a, inp.scale_b), return_plan_info=True)
     say("  plan", info)
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    C = decode(C_bits)
+    assert np.all(np.isfinite(C))
+    if name in FULL_C:
+        C_ref, S = _oracle_full(oracle_mod, name, inp)
+        r = assert_within_bound(C, C_ref, S, w.dtype, name)
+        say("  whole C (%d entries): worst err/bound %.3g" % (C.size, r))
+        return
+    rows, cols = block_entries(w.M, w.N, seed=w.seed)
     sigma = oracle_mod.sigma_of(inp.scale_a, inp.scale_b)
+    t0 = time.perf_counter()
     c_ref, s = oracle_mod.gemm_bt_entries(inp.A, inp.B, rows, cols, dtype=w.dtype, sigma=sigma)
-    r = assert_within_bound(decode(C_bits[rows, cols]), c_ref, s, w.dtype, name)
-    say("  worst err/bound", r)
-    # property at any size: no NaN/Inf anywhere in C
-    assert np.all(np.isfinite(decode(C_bits)))
+    say("  oracle: %d entries (one per 16 x 16 block + border rows / columns) in %.1f s" % (
+        len(rows), time.perf_counter() - t0))
+    r = assert_within_bound(C[rows, cols], c_ref, s, w.dtype, name)
+    say("  worst err/bound %.3g" % r)
 
 
 # ------------------------------------------------------------------ preshuffle kernel
@@ -222,22 +250,57 @@ def test_m_zero_is_noop():
         assert torch.all(C == 7)
 
 
-def test_repeat_runs_bitwise_stable(tile_env):
+# The kernels whose correctness rests on hand-counted vmcnt immediates and one
+# barrier per step, at 4096^3 in the planner's own configuration: 20 runs of
+# each must give the same C bit for bit (a race would show as a run that
+# differs).  (workload, expected kernel threads)
+REPEAT = [("bf16_8192_preshuffled", 512), ("e4m3_8192_preshuffled", 512), ("e4m3_8192", 512),
+          ("bf16_4096", 512), ("mxfp4_8192", 512), ("mxfp8_8192", 512)]
+
+
+@pytest.mark.parametrize("name,threads", REPEAT)
+def test_repeat_runs_bitwise_stable(tile_env, name, threads):
     tile_env(None)
-    M = N = K = 2048
-    say("case repeat", M, N, K)
-    w = W.WORKLOADS["bf16_4096"]
+    M = N = K = 4096
+    w = W.WORKLOADS[name]
+    say("case repeat x20", name, M, N, K)
     inp = W.make_inputs(w, M=M, N=N, K=K, seed=3)
-    with tg.Plan(M, N, K, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT) as p:
-        A, B = torch.from_numpy(inp.A.view(np.int16)).cuda(), torch.from_numpy(inp.B.view(np.int16)).cuda()
+    code = {"bf16": tg.GEMM_BF16_OUT_BF16, "e4m3": tg.GEMM_E4M3_OUT_BF16, "mxfp4": tg.GEMM_MXFP4_OUT_BF16,
+            "mxfp8": tg.GEMM_MXFP8_OUT_BF16}[w.dtype]
+    s = torch.cuda.current_stream().cuda_stream
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16) if x.dtype == np.uint16
+                                     else np.ascontiguousarray(x)).cuda()
+    with tg.Plan(M, N, K, code, tg.LAYOUTS[w.layout]) as p:
+        info = p.info()
+        assert info["tile_m"] == 256 and info["threads"] == threads, info
+        A, B = dev(inp.A), dev(inp.B)
+        if w.layout == "bt_preshuffled":
+            Bs = torch.empty(tg.gemm_preshuffled_b_bytes(p.handle), dtype=torch.uint8, device="cuda")
+            p.preshuffle_b(B.data_ptr(), Bs.data_ptr(), s)
+            B = Bs
+        sc = torch.tensor([inp.scale_a, inp.scale_b], dtype=torch.float32, device="cuda")
+        imgs = []
+        if w.dtype.startswith("mx"):
+            for operand, blocks in ((0, inp.sa_blocks), (1, inp.sb_blocks)):
+                src = torch.from_numpy(np.ascontiguousarray(blocks)).cuda()
+                img = torch.empty(p.bscale_image_bytes(operand), dtype=torch.uint8, device="cuda")
+                p.preshuffle_bscale(operand, src.data_ptr(), img.data_ptr(), s)
+                imgs.append(img)
+
+        def run(C):
+            if imgs:
+                p.run_mx(A.data_ptr(), imgs[0].data_ptr(), B.data_ptr(), imgs[1].data_ptr(), C.data_ptr(), stream=s)
+            else:
+                p.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), sc.data_ptr(), s)
         C0 = torch.empty(M * N, dtype=torch.int16, device="cuda")
         C1 = torch.empty_like(C0)
-        s = torch.cuda.current_stream().cuda_stream
-        p.run(A.data_ptr(), B.data_ptr(), C0.data_ptr(), None, s)
-        for _ in range(20):
-            p.run(A.data_ptr(), B.data_ptr(), C1.data_ptr(), None, s)
+        run(C0)
+        for i in range(20):
+            C1.fill_(0x5A5A)
+            run(C1)
             torch.cuda.synchronize()
-            assert torch.equal(C0, C1)
+            assert torch.equal(C0, C1), "run %d differs from the first in %d entries" % (
+                i + 1, int((C0 != C1).sum()))
 
 
 def test_side_stream_and_scale_pointer(oracle_mod, tile_env):

@@ -17,7 +17,7 @@ import torch
 import tiled_gemm_amd as tg
 import workloads as W
 import gpu_util
-from gpu_util import assert_epilogue_within_bound, decode, run_gemm, sample_entries
+from gpu_util import assert_epilogue_within_bound, decode, run_gemm, block_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -210,7 +210,7 @@ def test_int_full_size_sampled(oracle_mod, monkeypatch, name):
     inp = W.make_inputs(w)
     e = dict(scale_a=inp.sa_rows.astype(np.float64), scale_b=inp.sb_cols.astype(np.float64), kind="none")
     bits = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, epi=e)
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    rows, cols = block_entries(w.M, w.N, seed=w.seed)
     acc, S = oracle_mod.gemm_bt_int_entries(inp.A, inp.B, w.K, rows, cols, w.dtype)
     want = oracle_mod.epilogue_entries(acc, e["scale_a"][rows], e["scale_b"][cols], None, "none")
     scale = np.abs(e["scale_a"][rows] * e["scale_b"][cols])

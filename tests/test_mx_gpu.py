@@ -15,7 +15,7 @@ import torch
 import tiled_gemm_amd as tg
 import workloads as W
 import gpu_util
-from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
+from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, block_entries
 from oracle import layout as OL
 
 pytestmark = pytest.mark.gpu
@@ -183,7 +183,7 @@ def test_mx_full_size_sampled(oracle_mod, name, kind):
                  bias=rng.normal(0.0, 1.0, w.N), kind=kind)
     bits = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, sa_blocks=inp.sa_blocks,
                     sb_blocks=inp.sb_blocks, epi=e)
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    rows, cols = block_entries(w.M, w.N, seed=w.seed)
     acc, S = oracle_mod.gemm_bt_mx_entries(inp.A, inp.sa_blocks, inp.B, inp.sb_blocks, w.K, rows, cols, w.dtype)
     got = decode(bits[rows, cols])
     if e is None:

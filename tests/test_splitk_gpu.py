@@ -16,7 +16,7 @@ import torch
 import tiled_gemm_amd as tg
 import workloads as W
 import gpu_util
-from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, sample_entries
+from gpu_util import assert_epilogue_within_bound, assert_within_bound, decode, run_gemm, block_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -201,7 +201,7 @@ def test_split_full_size_sampled(oracle_mod, name):
     w = W.WORKLOADS[name]
     say("case split full-size", name)
     inp = W.make_inputs(w)
-    rows, cols = sample_entries(w.M, w.N, 8192, seed=w.seed)
+    rows, cols = block_entries(w.M, w.N, seed=w.seed)
     if w.dtype in ("i8", "w4a8"):
         e = dict(scale_a=inp.sa_rows.astype(np.float64), scale_b=inp.sb_cols.astype(np.float64), kind="none")
         bits, info = run_gemm(inp.A, inp.B, w.M, w.N, w.K, w.dtype, w.out, w.layout, epi=e, workspace=True,

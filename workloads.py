@@ -116,6 +116,9 @@ WORKLOADS = {
     "e4m3_8192": Workload("e4m3_8192", 8192, 8192, 8192, "e4m3", "bf16", "bt",
                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1005,
                           "per-tensor scales amax/448"),
+    "e4m3_8192_preshuffled": Workload("e4m3_8192_preshuffled", 8192, 8192, 8192, "e4m3", "bf16", "bt_preshuffled",
+                                      ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1005,
+                                      "the same inputs as e4m3_8192, B pre-shuffled"),
     "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "mxfp8", "bf16", "bt_preshuffled",
                            ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1006,
                            "MX block scales, e4m3 elements"),
