@@ -273,6 +273,26 @@ int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *C,
                 hipStream_t stream);
 
 /*
+ * gemm_run_ws_noalloc -- gemm_run_ws on the library's own static workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * library holds one GEMM_STATIC_WORKSPACE_BYTES array per GPU it runs on,
+ * from first use until the process ends; this call allocates nothing and
+ * calls no allocating routine.
+ *   A, B, C, epi, stream  as for gemm_run_ex.
+ * A plan that does not split runs exactly as gemm_run_ex.  A plan whose
+ * partials (gemm_workspace_bytes) exceed GEMM_STATIC_WORKSPACE_BYTES is
+ * refused with GEMM_ERR_UNSUPPORTED (gemm_run_ws takes any workspace).
+ * Every call on one GPU shares that GPU's array, whose contents are whatever
+ * the last call left (every element a split reads is written first by the
+ * same call, so nothing needs clearing): calls that overlap in time on one
+ * GPU race -- issue them on one stream.  Errors as gemm_run_ws.
+ */
+#define GEMM_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int gemm_run_ws_noalloc(const gemm_plan *plan, const void *A, const void *B, void *C,
+                        const gemm_epilogue_args *epi, hipStream_t stream);
+
+/*
  * MX block-scaled operands (GEMM_MXFP8_OUT_BF16, GEMM_MXFP4_OUT_BF16).  The
  * pages' gfx950 scaled MFMA (FlyDSL "Kernel authoring guide", section 4.3
  * "ROCm intrinsics", MFMA instructions: mfma_scale_f32_16x16x128_f8f6f4)

@@ -54,8 +54,10 @@ EXPORTS = (
     "gemm_run", "gemm_run_ex", "gemm_bscale_image_bytes", "gemm_preshuffle_bscale", "gemm_run_mx",
     "gemm_last_error", "gemm_plan_query", "gemm_plan_layout", "gemm_layout_crd2idx",
     "gemm_layout_idx2crd", "gemm_lds_swizzle", "gemm_tile_of_workgroup", "gemm_workspace_bytes",
-    "gemm_run_ws",
+    "gemm_run_ws", "gemm_run_ws_noalloc",
 )
+
+GEMM_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
 class GemmError(RuntimeError):
@@ -113,6 +115,7 @@ def load() -> ctypes.CDLL:
         "gemm_run_mx": (c_int, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp]),
         "gemm_workspace_bytes": (ctypes.c_size_t, [vp]),
         "gemm_run_ws": (c_int, [vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp, ctypes.c_size_t, vp]),
+        "gemm_run_ws_noalloc": (c_int, [vp, vp, vp, vp, ctypes.POINTER(gemm_epilogue_args), vp]),
         "gemm_last_error": (ctypes.c_char_p, []),
         "gemm_plan_query": (c_int, [vp, ctypes.POINTER(gemm_plan_info)]),
         "gemm_plan_layout": (c_int, [vp, c_int, p32, p64, p64]),
@@ -198,6 +201,14 @@ def gemm_run_ws(plan: int, A: int, B: int, C: int, workspace: int | None, worksp
                              int(scale_b_per_col), epilogue)
     _check(load().gemm_run_ws(plan, A, B, C, ctypes.byref(epi), workspace or None, workspace_bytes, stream),
            "gemm_run_ws")
+
+
+def gemm_run_ws_noalloc(plan: int, A: int, B: int, C: int, scale_a: int | None = None,
+                        scale_a_per_row: bool = False, scale_b: int | None = None, scale_b_per_col: bool = False,
+                        bias: int | None = None, epilogue: int = GEMM_EPI_NONE, stream: int = 0) -> None:
+    epi = gemm_epilogue_args(scale_a or None, scale_b or None, bias or None, int(scale_a_per_row),
+                             int(scale_b_per_col), epilogue)
+    _check(load().gemm_run_ws_noalloc(plan, A, B, C, ctypes.byref(epi), stream), "gemm_run_ws_noalloc")
 
 
 def gemm_bscale_image_bytes(plan: int, operand: int) -> int:
@@ -325,3 +336,7 @@ class Plan:
                **epi) -> None:
         """gemm_run_ws; keyword arguments as for the module-level gemm_run_ex."""
         gemm_run_ws(self.handle, A, B, C, workspace, workspace_bytes, stream=stream, **epi)
+
+    def run_ws_noalloc(self, A: int, B: int, C: int, stream: int = 0, **epi) -> None:
+        """gemm_run_ws_noalloc; keyword arguments as for the module-level gemm_run_ex."""
+        gemm_run_ws_noalloc(self.handle, A, B, C, stream=stream, **epi)

@@ -918,6 +918,40 @@ int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *C, co
     return run_split(plan, A, B, C, workspace, e, stream);
 }
 
+int gemm_run_ws_noalloc(const gemm_plan *plan, const void *A, const void *B, void *C,
+                        const gemm_epilogue_args *epi, hipStream_t stream)
+{
+    static_assert(GEMM_STATIC_WORKSPACE_BYTES == tg::kStaticWorkspaceBytes, "header and library agree");
+    if (int rc = reject_mx(plan))
+        return rc;
+    tg::EpiArgs e;
+    if (int rc = epi_from(epi, &e))
+        return rc;
+    const size_t need = workspace_bytes(plan);
+    if (need == 0)
+        return run_impl(plan, A, B, C, e, stream);
+    if (need > tg::kStaticWorkspaceBytes)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "the plan's split-K partials need %zu bytes, more than the %zu-byte static workspace "
+                    "(gemm_run_ws takes a workspace of any size)",
+                    need, tg::kStaticWorkspaceBytes);
+    const gemm_plan_info &I = plan->info;
+    if (!A || !B || !C)
+        return fail(GEMM_ERR_INVALID_ARG, "NULL A, B or C");
+    if (misaligned(A) || misaligned(B) || misaligned(C))
+        return fail(GEMM_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
+    const size_t cbytes = (size_t)I.M * I.N * I.out_bytes;
+    if (overlap(C, cbytes, A, (size_t)I.M * plan->kbytes) || overlap(C, cbytes, B, (size_t)I.N * plan->kbytes_b))
+        return fail(GEMM_ERR_INVALID_ARG, "C overlaps A or B");
+    if (int rc = check_device())
+        return rc;
+    void *ws = nullptr;
+    const hipError_t he = tg::static_workspace(&ws);
+    if (he != hipSuccess || !ws)
+        return fail(GEMM_ERR_HIP, "static workspace address: %s", hipGetErrorString(he));
+    return run_split(plan, A, B, C, ws, e, stream);
+}
+
 size_t gemm_bscale_image_bytes(const gemm_plan *plan, int operand)
 {
     if (!plan || !is_mx(plan->info.dtype) || (operand != 0 && operand != 1))

@@ -146,4 +146,10 @@ const SkinnyVariant *skinny_variants(int *count);
 hipError_t launch_preshuffle(const PreshuffleArgs &, hipStream_t);
 hipError_t launch_bscale_image(const BscaleArgs &, hipStream_t);
 
+// The library's static split-K workspace (gemm_run_ws_noalloc): its device
+// address on the current device (looked up on the first call per device).
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_workspace(void **ptr);
+
 }  // namespace tg

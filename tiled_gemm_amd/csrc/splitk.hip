@@ -14,6 +14,8 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+#include <mutex>
+
 namespace tg {
 
 constexpr int kReduceThreads = 256;
@@ -67,6 +69,39 @@ hipError_t launch_split_reduce(const SplitReduceArgs &a, hipStream_t s)
     else
         hipLaunchKernelGGL(split_reduce_kernel<kOutBf16>, dim3((unsigned)blocks), dim3(kReduceThreads), 0, s, a);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The library's own split-K workspace, for callers that cannot allocate
+// (gemm_run_ws_noalloc): one statically sized device array, held on every
+// GPU the library runs on until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory; its device address is
+// looked up once per device with hipGetSymbolAddress (with that device
+// current) and only that address is ever handed to kernels.  Every call on
+// one GPU shares the array, so calls that overlap in time on one GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace tg
