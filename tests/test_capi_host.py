@@ -185,7 +185,9 @@ def test_plan_choices(lib, monkeypatch):
     assert info(32, 8192, 8192, tg.GEMM_MXFP4_OUT_BF16, tg.GEMM_LAYOUT_BT)["kernel"] == 0
     c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT)
     assert c["elem_bytes"] == 1 and c["tile_k_bytes"] % 64 == 0
-    assert c["lds_stages"] == 4                      # fp8: B in registers
+    assert c["lds_stages"] == 2                      # fp8, B N x K: both operands through LDS
+    c = info(8192, 8192, 8192, tg.GEMM_E4M3_OUT_BF16, tg.GEMM_LAYOUT_BT_PRESHUFFLED)
+    assert c["lds_stages"] == 4                      # fp8, B pre-shuffled: B in registers
     with tg.Plan(4096, 4096, 4096, tg.GEMM_BF16_OUT_BF16, tg.GEMM_LAYOUT_BT, kernel=tg.GEMM_KERNEL_PIPE) as p:
         c = p.info()
     assert (c["threads"], c["lds_stages"]) == (512, 4)

@@ -193,17 +193,16 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, int kc, bool force25
         tile = big >= 128 ? 256 : 128;
     }
     if (tile == 256 && any256) {
-        // bf16 with B stored N x K or K x N: both operands staged through LDS
-        // by the loads' own LDS writes (gemm_dma.hip: whole 128-byte lines of
-        // B, where the register-staged kernel's MFMA lane order can only load
-        // half lines; K x N through the transpose read).
-        if (elem == tg::kBf16 && !pre) {
-            auto ok = [&](const tg::TiledVariant &x) {
-                return x.elem == elem && x.out == out && !x.preshuffled && x.bkn == bkn && !x.akm;
-            };
-            TG_SWEEP_PICK("dma", d, nd, ok)
+        // bf16 and fp8 with B stored N x K (bf16 also K x N): both operands
+        // staged through LDS by the loads' own LDS writes (gemm_dma.hip: whole
+        // 128-byte lines of B, where the register-staged kernel's MFMA lane
+        // order can only load half lines; K x N through the transpose read).
+        auto ok = [&](const tg::TiledVariant &x) {
+            return x.elem == elem && x.out == out && x.preshuffled == pre && x.bkn == bkn && !x.akm;
+        };
+        TG_SWEEP_PICK("dma", d, nd, ok)
+        if ((elem == tg::kBf16 || elem == tg::kFp8) && !pre)
             return first_of(d, nd, ok);
-        }
     }
     // Otherwise 256 x 256 tiles run the software-pipelined kernel (B N x K or
     // pre-shuffled, B straight to registers), 8 waves, or 4 waves with AGPR

@@ -447,6 +447,8 @@ static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // B N x K
     TG_DMA(kBf16, kOutF32, false, 2, 4, 4),
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // fp8, B N x K
+    TG_DMA(kFp8, kOutF32, false, 1, 8, 3),
     TG_DMA_KN(kOutBf16, 2, 4, 4),              // B stored K x N
     TG_DMA_KN(kOutF32, 2, 4, 4),
     // A stored K x M: prefetch distance 2 (a K x M fragment is two transpose
@@ -464,21 +466,20 @@ static const TiledVariant kDma[] = {
     TG_DMA_AT8(kI8, false),                    // int8, A K x M, B N x K
     TG_DMA_AT8(kI8, true),                     // int8, A K x M, B K x N
 #ifdef TGEMM_SWEEP
-    // alternatives (sweep builds only): other prefetch distances, and fp8 and
+    // alternatives (sweep builds only): other prefetch distances, and
     // pre-shuffled B through LDS
-    TG_DMA(kBf16, kOutBf16, false, 2, 4, 4),   // 14
-    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // 15
-    TG_DMA(kFp8, kOutBf16, false, 1, 8, 2),
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 4),   // 16
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 2),    // 17
     TG_DMA(kFp8, kOutBf16, true, 1, 8, 3),
-    TG_DMA(kBf16, kOutBf16, true, 2, 4, 6),    // 18
+    TG_DMA(kBf16, kOutBf16, true, 2, 4, 6),    // 19
     TG_DMA_KN(kOutBf16, 2, 4, 6),
-    TG_DMA_KN8(1, 8, 2),                       // 20
-    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 21: A K x M
+    TG_DMA_KN8(1, 8, 2),                       // 21
+    TG_DMA_L(kOutBf16, 2, 4, 4, false, true),  // 22: A K x M
     TG_DMA_L(kOutBf16, 2, 4, 3, false, true),
-    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 23: A K x M, B K x N
+    TG_DMA_L(kOutBf16, 2, 4, 4, true, true),   // 24: A K x M, B K x N
     TG_DMA_L(kOutBf16, 2, 4, 3, true, true),
-    TG_DMA_KN(kOutBf16, 2, 4, 3),              // 25: B K x N
-    TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 26: B N x K
+    TG_DMA_KN(kOutBf16, 2, 4, 3),              // 26: B K x N
+    TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 27: B N x K
 #endif
 };
 
