@@ -132,10 +132,15 @@ __device__ inline f32x4 mfma_fp8(u32x4 x_lo, u32x4 x_hi, u32x4 y_lo, u32x4 y_hi,
 // The same two atoms with the accumulator pinned to AGPRs (inline assembly,
 // "+a"), for kernels whose accumulators fill the AGPR file (256 per lane): the
 // compiler then keeps every accumulator in place across the main loop instead
-// of copying between register files.  It does not know these are MFMAs, so
-// code that reads the accumulators with other instructions must first call
-// mfma_drain(); dependent MFMAs on one accumulator must be far apart (the
-// kernels using these issue at least 32 other MFMAs in between).
+// of copying between register files.  It does not know these are MFMAs and
+// inserts none of the wait states around them, so the kernels using them keep
+// two rules: (1) an MFMA that depends on an earlier one reads that MFMA's
+// result only as its accumulator, with SrcC and vDst the very same registers
+// (the case the matrix unit resolves by itself; the 8-wave 32x32x64 MX kernel
+// updates an accumulator every 8 MFMAs, the others every 32 or more); (2) no
+// other instruction reads or writes an accumulator until mfma_drain_acc() has
+// waited out more cycles than any of these MFMAs takes to finish (its passes
+// plus two) and pinned the reads behind that wait.
 // v_mfma_f32_16x16x128_f8f6f4 with its default format fields is e4m3 x e4m3,
 // the unscaled form of mfma_fp8x8 above.
 __device__ inline void mfma_bf16_a(f32x4 &acc, u32x4 x, u32x4 y)
