@@ -278,8 +278,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         return lds + s * DM_STAGE + DM_A + row * kTileKBytes + swz_chunk(row, h * 4 + q) * kChunkBytes;
     };
     using FragT = typename std::conditional<F8, i32x8, u32x4>::type;
+    // 8-bit operands on a 2 x 4 grid: two sets of the four 8-register B
+    // fragments would not fit beside 128 accumulators in 256 registers, so
+    // there is one set, and the last group of a step reloads fragment j from
+    // the next stage right after its last MFMA (SB).
+    constexpr bool SB = F8 && FN > 2;
     FragT fa[NG];
-    FragT fb[2][FN];        // bf16: [half][block]; fp8: [step parity][block]
+    FragT fb[SB ? 1 : 2][FN];   // bf16: [half][block]; fp8: [step parity][block]
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -289,16 +294,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
 
     // Reads for group t of the step held in stage s: the half's B fragments
     // first when t opens a half, then t's A fragment.
+    auto b8_frag = [&](int s, int j) -> i32x8 {
+        if constexpr (BKN)
+            return bkn8_frag(s, j);
+        else
+            return join32(lds_load16(b_addr(s, 0, j)), lds_load16(b_addr(s, 1, j)));
+    };
     auto load_group = [&](int s, int t) {
         if constexpr (F8) {
-            if (t == 0) {
+            if (t == 0 && !SB) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    if constexpr (BKN)
-                        fb[s][j] = bkn8_frag(s, j);
-                    else
-                        fb[s][j] = join32(lds_load16(b_addr(s, 0, j)), lds_load16(b_addr(s, 1, j)));
-                }
+                for (int j = 0; j < FN; ++j)
+                    fb[SB ? 0 : s][j] = b8_frag(s, j);
             }
             if constexpr (AKM)
                 fa[t] = akm8_frag(s, t);
@@ -349,13 +356,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
             const int i = g % FM, h = g / FM;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
+                constexpr int SF = SB ? 0 : S;
                 if constexpr (I8) {
-                    acc[i][j] = mfma_i8(lo16(fb[S][j]), lo16(fa[g]), acc[i][j]);
-                    acc[i][j] = mfma_i8(hi16(fb[S][j]), hi16(fa[g]), acc[i][j]);
+                    acc[i][j] = mfma_i8(lo16(fb[SF][j]), lo16(fa[g]), acc[i][j]);
+                    acc[i][j] = mfma_i8(hi16(fb[SF][j]), hi16(fa[g]), acc[i][j]);
                 } else if constexpr (F8) {
-                    acc[i][j] = mfma_fp8x8(fb[S][j], fa[g], acc[i][j]);
+                    acc[i][j] = mfma_fp8x8(fb[SF][j], fa[g], acc[i][j]);
                 } else {
                     acc[i][j] = mfma_bf16(fb[h][j], fa[g], acc[i][j]);
+                }
+                // The barrier of this step (PD groups back) has made the next
+                // stage visible.
+                if constexpr (SB) {
+                    if (g == NG - 1) {
+                        // in this order: the reload may take the registers
+                        // the MFMA above has just read
+                        __builtin_amdgcn_sched_barrier(0);
+                        fb[0][j] = b8_frag(S ^ 1, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -371,6 +390,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
         issue_one(1, dic<1>{}, idx, std::true_type{});
     __builtin_amdgcn_s_waitcnt(0);
     barrier();
+    if constexpr (SB) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[0][j] = b8_frag(0, j);
+    }
 #pragma unroll
     for (int t = 0; t < PD; ++t)
         load_group(0, t);
@@ -447,8 +471,8 @@ static hipError_t launch_dma(const TiledArgs &a, hipStream_t s)
 static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 6),   // B N x K
     TG_DMA(kBf16, kOutF32, false, 2, 4, 4),
-    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // fp8, B N x K
-    TG_DMA(kFp8, kOutF32, false, 1, 8, 3),
+    TG_DMA(kFp8, kOutBf16, false, 2, 4, 2),    // fp8, B N x K
+    TG_DMA(kFp8, kOutF32, false, 2, 4, 2),
     TG_DMA_KN(kOutBf16, 2, 4, 4),              // B stored K x N
     TG_DMA_KN(kOutF32, 2, 4, 4),
     // A stored K x M: prefetch distance 2 (a K x M fragment is two transpose
@@ -480,6 +504,9 @@ static const TiledVariant kDma[] = {
     TG_DMA_L(kOutBf16, 2, 4, 3, true, true),
     TG_DMA_KN(kOutBf16, 2, 4, 3),              // 26: B K x N
     TG_DMA(kBf16, kOutBf16, false, 2, 4, 5),   // 27: B N x K
+    TG_DMA(kFp8, kOutBf16, false, 1, 8, 3),    // 28: fp8 1 x 8
+    TG_DMA(kFp8, kOutBf16, false, 2, 4, 3),
+    TG_DMA(kFp8, kOutBf16, true, 2, 4, 3),     // 30: fp8 2 x 4, B pre-shuffled
 #endif
 };
 
