@@ -212,7 +212,8 @@ def test_full_size(oracle_mod, tile_env, name, tile):
 
 # ------------------------------------------------------------------ preshuffle kernel
 
-@pytest.mark.parametrize("dtype,N,K", [("bf16", 48, 96), ("bf16", 256, 1056), ("e4m3", 64, 320), ("bf16", 8192, 8192)])
+@pytest.mark.parametrize("dtype,N,K", [("bf16", 48, 96), ("bf16", 256, 1056), ("e4m3", 64, 320), ("e4m3", 528, 8256),
+                                       ("bf16", 8192, 8192)])
 def test_preshuffle_byte_exact(dtype, N, K):
     from oracle import layout as OL
     say("case preshuffle", dtype, N, K)

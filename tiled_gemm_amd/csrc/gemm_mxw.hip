@@ -6,11 +6,14 @@
 // Kernel authoring guide", section 4.3 "ROCm intrinsics", for the f8f6f4
 // scaled MFMA family and its E8M0 block scales).
 //
-// Why a second MX kernel: e2m1 operands run at twice the e4m3 rate only in
-// the 32x32x64 shape (the 16x16x128 shape is capped near the e4m3 rate; an
-// independent-accumulator microbenchmark on every CU measured 7.3 against
-// 4.7 PFLOP/s), and its 32 x 32 accumulators let MX run on 8 waves (the
-// 16x16x128 MX kernel spills there).  Per 64-element K slice a lane feeds row
+// Why a second MX kernel: a lane's 16-byte e2m1 operand feeds a 32x32x64
+// MFMA (131072 flops) where the 16x16x128 shape does half that, so the A
+// fragment reads from LDS per flop halve; the matrix unit alone runs either
+// shape at over 92% of the e2m1 peak (8 waves per CU, independent
+// accumulators), but one 16-byte LDS read per 32x32x64 MFMA interleaved with
+// them already caps it near 64% (one read per two MFMAs: 80-84%).  The
+// 32 x 32 accumulators also let MX run on 8 waves (the 16x16x128 MX kernel
+// spills there).  Per 64-element K slice a lane feeds row
 // l % 32 -- e2m1: one 16-byte chunk, elements 32 (l / 32) .. +31; e4m3: chunks
 // l / 32 and 2 + l / 32 of the slice -- and one scale byte, for K block
 // l / 32 of the slice.
