@@ -15,7 +15,8 @@
 //
 // Workgroup: WGM x WGN waves over a 256 x 256 output tile (2 x 4: each wave
 // 128 rows x 64 columns, 128 fp32 accumulators per lane).  Main-loop step:
-// 128 bytes of K (two 16x16x32 bf16 MFMAs per 16 x 16 block).
+// 128 bytes of K (two 16x16x32 bf16 MFMAs per 16 x 16 block, or one fp8
+// 16x16x128).
 //
 //   LDS     two stages of 64 KiB: A (256 rows x 128 B, chunk-swizzled) and B
 //           (pre-shuffled: 32 operand blocks of 1 KiB; plain: 256 rows x
@@ -84,7 +85,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     constexpr int NG = F8 ? FM : 2 * FM;                   // groups per step: half h = g / FM (bf16)
     static_assert(WAVES == 8, "two waves per SIMD: 128 accumulators per lane in VGPRs");
     // bf16: next-step B fragments of half 0 reuse the dead registers of
-    // half 0; fp8: B fragments are double-buffered by step parity.
+    // half 0; fp8: B fragments are double-buffered by step parity on the 1 x 8
+    // grid, single-buffered (SB, below) on the 2 x 4 grid.
     static_assert(PD >= 1 && (F8 ? PD < FM : PD <= FM), "prefetch distance");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[DM_LDS];
 
