@@ -304,10 +304,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma_kernel(const Tiled
     };
     auto load_group = [&](int s, int t) {
         if constexpr (F8) {
-            if (t == 0 && !SB) {
+            if constexpr (!SB) {
+                if (t == 0) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    fb[SB ? 0 : s][j] = b8_frag(s, j);
+                    for (int j = 0; j < FN; ++j)
+                        fb[s][j] = b8_frag(s, j);
+                }
             }
             if constexpr (AKM)
                 fa[t] = akm8_frag(s, t);
