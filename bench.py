@@ -54,7 +54,7 @@ CONFIGS = {"c1": "bf16_int_256", "c2": "bf16_4096", "c3": HEADLINE, "c4": "bf16_
 ALSO = ["bf16_int_256", "bf16_4096", "bf16_4096_bn", "bf16_4096_at", "bf16_4096_at_bn", "bf16_skinny_32x8192x8192",
         "bf16_skinny_32x8192x8192_preshuffled", "bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192",
         "e4m3_1024x8192x8192", "e4m3_8192", "e4m3_8192_preshuffled", "e4m3_8192_bn", "mxfp8_8192", "mxfp4_8192",
-        "mxfp4_32x8192x8192", "i8_8192", "w4a8_8192", "w4a8_32x8192x8192", "w4a8_256x8192x8192"]
+        "mxfp4_32x8192x8192", "i8_8192", "i8_8192_bt", "w4a8_8192", "w4a8_32x8192x8192", "w4a8_256x8192x8192"]
 # Workloads with fewer 256 x 256 tiles than CUs: timed through gemm_run_ws
 # (split K with a workspace), plain gemm_run reported beside.
 SPLIT_K_WORKLOADS = ("bf16_256x8192x8192_preshuffled", "bf16_1024x8192x8192", "e4m3_1024x8192x8192",

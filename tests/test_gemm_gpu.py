@@ -256,7 +256,7 @@ def test_m_zero_is_noop():
 # each must give the same C bit for bit (a race would show as a run that
 # differs).  (workload, expected kernel threads)
 REPEAT = [("bf16_8192_preshuffled", 512), ("e4m3_8192_preshuffled", 512), ("e4m3_8192", 512),
-          ("bf16_4096", 512), ("mxfp4_8192", 512), ("mxfp8_8192", 512)]
+          ("bf16_4096", 512), ("mxfp4_8192", 512), ("mxfp8_8192", 512), ("i8_8192_bt", 512)]
 
 
 @pytest.mark.parametrize("name,threads", REPEAT)
@@ -267,7 +267,7 @@ def test_repeat_runs_bitwise_stable(tile_env, name, threads):
     say("case repeat x20", name, M, N, K)
     inp = W.make_inputs(w, M=M, N=N, K=K, seed=3)
     code = {"bf16": tg.GEMM_BF16_OUT_BF16, "e4m3": tg.GEMM_E4M3_OUT_BF16, "mxfp4": tg.GEMM_MXFP4_OUT_BF16,
-            "mxfp8": tg.GEMM_MXFP8_OUT_BF16}[w.dtype]
+            "mxfp8": tg.GEMM_MXFP8_OUT_BF16, "i8": tg.GEMM_I8_OUT_BF16}[w.dtype]
     s = torch.cuda.current_stream().cuda_stream
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16) if x.dtype == np.uint16
                                      else np.ascontiguousarray(x)).cuda()

@@ -202,7 +202,7 @@ def test_int_quantised_within_bound(oracle_mod, monkeypatch, fmt, kind, waves):
     say("  worst err/bound", r)
 
 
-@pytest.mark.parametrize("name", ["i8_8192", "w4a8_8192", "w4a8_32x8192x8192"])
+@pytest.mark.parametrize("name", ["i8_8192", "i8_8192_bt", "w4a8_8192", "w4a8_32x8192x8192"])
 def test_int_full_size_sampled(oracle_mod, monkeypatch, name):
     set_waves(monkeypatch, None)
     w = W.WORKLOADS[name]

@@ -173,6 +173,17 @@ const tg::TiledVariant *pick_tiled(const gemm_plan_info &I, int kc, bool force25
             TG_SWEEP_PICK("mxw", x, nw, ok)
             return first_of(x, nw, ok);
         }
+        // int8 with B stored N x K: the LDS-staged kernel, whose loads cover
+        // whole 128-byte lines of B (as for fp8); the split-K partial tiles
+        // (fp32 out) stay on the pipelined kernel.
+        if (elem == tg::kI8 && !pre && any256 && out == tg::kOutBf16) {
+            auto ok = [&](const tg::TiledVariant &x) {
+                return x.elem == elem && x.out == out && !x.preshuffled && !x.bkn && !x.akm;
+            };
+            TG_SWEEP_PICK("dma", d, nd, ok)
+            if (const tg::TiledVariant *x = first_of(d, nd, ok))
+                return x;
+        }
         const int waves = kc == GEMM_KERNEL_PIPE4 ? 4 : 8;
         if (!(any256 || kc == GEMM_KERNEL_PIPE || kc == GEMM_KERNEL_PIPE4) || (is_mx(I.dtype) && waves != 4))
             return nullptr;

@@ -477,6 +477,7 @@ static const TiledVariant kDma[] = {
     TG_DMA(kBf16, kOutF32, false, 2, 4, 4),
     TG_DMA(kFp8, kOutBf16, false, 2, 4, 2),    // fp8, B N x K
     TG_DMA(kFp8, kOutF32, false, 2, 4, 2),
+    TG_DMA(kI8, kOutBf16, false, 2, 4, 2),     // int8, B N x K
     TG_DMA_KN(kOutBf16, 2, 4, 4),              // B stored K x N
     TG_DMA_KN(kOutF32, 2, 4, 4),
     // A stored K x M: prefetch distance 2 (a K x M fragment is two transpose

@@ -143,6 +143,9 @@ WORKLOADS = {
     "i8_8192": Workload("i8_8192", 8192, 8192, 8192, "i8", "bf16", "bt_preshuffled",
                         ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1008,
                         "per-row / per-channel absmax scales"),
+    "i8_8192_bt": Workload("i8_8192_bt", 8192, 8192, 8192, "i8", "bf16", "bt",
+                           ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1021,
+                           "per-row / per-channel absmax scales, B N x K"),
     "w4a8_32x8192x8192": Workload("w4a8_32x8192x8192", 32, 8192, 8192, "w4a8", "bf16", "bt_preshuffled",
                                   ("normal", 0.0, 1.0), ("normal", 0.0, 1.0), 1017,
                                   "decode with an int4 weight: int8 A, packed int4 B"),
